@@ -1,0 +1,35 @@
+"""Bandwidth figures of an AllReduce, in the convention of the NCCL course
+pages: algBW = M / t and busBW = algBW * 2(N-1)/N with GB = 1e9, where M is
+the message size of one rank.  Each rank sends 2(N-1) chunks of M/N
+[NCCL 专家课程 12, "为什么是 2(N-1) 次发送"].
+
+The algorithmic HBM bytes of one ring AllReduce on a single device that hosts
+all N ranks count, per loop of N chunks of M/N each, the reads and writes
+every primitive must make (f = FIFO bytes per payload byte: Simple 1, LL 2,
+LL128 16/15):
+
+    send 1+f, recvReduceSend 1+2f, recvReduceCopySend 2+2f,
+    recvCopySend 1+2f, recv 1+f
+
+Summed over the N ranks: B = [4 + 4f + 2(N-2)(2f+1)] * M.
+"""
+from fractions import Fraction
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published peak (8 TB/s)
+
+FIFO_FACTOR = {"SIMPLE": Fraction(1), "LL": Fraction(2), "LL128": Fraction(16, 15)}
+
+
+def algbw_gbps(message_bytes: float, seconds: float) -> float:
+    return message_bytes / seconds / 1e9
+
+
+def busbw_gbps(message_bytes: float, seconds: float, nranks: int) -> float:
+    return algbw_gbps(message_bytes, seconds) * 2.0 * (nranks - 1) / nranks
+
+
+def algorithmic_bytes(message_bytes: int, nranks: int, proto: str) -> float:
+    """HBM bytes the ring schedule must move for one collective, all ranks."""
+    f = FIFO_FACTOR[proto]
+    per_m = 4 + 4 * f + 2 * (nranks - 2) * (2 * f + 1)
+    return float(per_m * message_bytes)
