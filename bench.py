@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the ring AllReduce hot path on one MI355X.
+
+One step = one AllReduce of the whole workload (every virtual rank's buffer)
+through the C ABI, i.e. one launch of the ring kernel; inputs are resident in
+HBM before the timed region starts.  Default workload: 4 virtual ranks on
+ring 0-2-3-1, 12 channels, Simple protocol with a 4 MiB FIFO and 4-step
+chunks, fp32 sum, 64 MiB per rank.
+
+Reported: algBW = M/t and busBW = algBW * 2(N-1)/N (GB = 1e9) as in the NCCL
+course pages, the ring's algorithmic HBM bytes over the kernel's duration as a
+fraction of MI355X peak HBM bandwidth, and the CPU oracle timed on this host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# Tuned launch shape per workload (performance only; no result bit depends on it).
+TUNING = {"simple_64m": dict(lanes=4, waves=8)}
+KERNEL_SRC = os.path.join(ROOT, "ring_all_reduce_channelmask_amd", "csrc", "ring_kernel.hip")
+
+
+def kernel_fingerprint() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def measured_traffic(key, lanes, waves, alg_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none for this kernel source and launch shape."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_fingerprint() or t.get("lanes") != lanes or \
+            t.get("waves") != waves:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, xs, budget_s=12.0, max_runs=5):
+    """The oracle simulator, as it stands, on the same workload."""
+    import oracle
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < max_runs and (time.perf_counter() - t_all) < budget_s:
+        t0 = time.perf_counter()
+        rc, _, _, _ = oracle.allreduce(xs, list(w.ring_order), w.mask, w.proto, w.buff_size,
+                                       w.chunk_steps, w.dtype)
+        times.append(time.perf_counter() - t0)
+        assert rc == oracle.OK
+    return statistics.median(times), len(times)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="simple_64m")
+    ap.add_argument("--lanes", type=int, default=None)
+    ap.add_argument("--waves", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the N virtual ranks all live on a single MI355X "
+              "and no multi-GPU path exists; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ring_all_reduce_channelmask_amd as rar
+    from ring_all_reduce_channelmask_amd import metrics, workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    tune = dict(TUNING.get(args.workload, {}))
+    if args.lanes is not None:
+        tune["lanes"] = args.lanes
+    if args.waves is not None:
+        tune["waves"] = args.waves
+    torch.cuda.set_device(0)
+    xs = workloads.inputs_for(w)
+    N = w.nranks
+
+    def dev(a):
+        if w.dtype == "bfloat16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    sends = [[dev(x[r]) for r in range(N)] for x in xs]
+    recvs = [[torch.empty_like(t) for t in s] for s in sends]
+    comm = rar.Comm(N, list(w.ring_order), w.mask, proto=w.proto, buff_size=w.buff_size,
+                    chunk_steps=w.chunk_steps if w.proto == "SIMPLE" else 0, **tune)
+    shape = comm.shape()
+
+    def step():
+        if len(xs) == 1:
+            comm.allreduce(sends[0], recvs[0])
+        else:
+            with comm.group():
+                for s, r in zip(sends, recvs):
+                    comm.allreduce(s, r)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()  # the stream every launch goes to
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if comm.async_error() != 0:
+        raise RuntimeError("the wait watchdog fired during the timed region")
+    per = [a.elapsed_time(b) * 1e-3 for a, b in ev]            # seconds, one launch each
+    span = ev[0][0].elapsed_time(ev[-1][1]) * 1e-3
+    t_step = span / args.steps
+    t_kernel = statistics.mean(per)
+    # the N receive buffers must agree (a property of the method, not an oracle)
+    for s in recvs:
+        ref = s[0]
+        for t in s[1:]:
+            if not torch.equal(t.view(torch.int16 if w.dtype == "bfloat16" else t.dtype), ref.view(
+                    torch.int16 if w.dtype == "bfloat16" else ref.dtype)):
+                raise RuntimeError("ranks disagree")
+    M = w.message_bytes
+    algbw = metrics.algbw_gbps(M, t_step)
+    busbw = metrics.busbw_gbps(M, t_step, N)
+    alg_bytes = metrics.algorithmic_bytes(M, N, w.proto)
+    achieved = alg_bytes / t_kernel / 1e9
+    traffic = measured_traffic(args.workload, shape["lanes"], shape["waves"], alg_bytes)
+    out = {
+        "metric": "algBW/busBW GB/s, N-virtual-rank ring AllReduce, 1 MI355X; % HBM peak",
+        "value": round(busbw, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"float32": "f32", "bfloat16": "bf16", "int32": "int32"}[w.dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.key}: {w.note}",
+            "nranks": N, "ring_order": list(w.ring_order), "channel_mask": hex(w.mask),
+            "proto": w.proto, "buff_size": w.buff_size, "chunk_steps": w.chunk_steps,
+            "elems_per_rank": sum(w.counts), "collectives_per_step": len(w.counts),
+            "lanes_per_channel": shape["lanes"], "waves_per_lane": shape["waves"],
+            "grid": shape["grid"], "parallelism": f"{N} virtual ranks on 1 GPU",
+        },
+        "algbw_GBps": round(algbw, 3),
+        "busbw_GBps": round(busbw, 3),
+        "aggregate_GBps": round(N * M / t_step / 1e9, 3),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": metrics.HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / metrics.HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": alg_bytes,
+            "kernel_ms": round(t_kernel * 1e3, 4),
+        },
+        "kernel_sha": kernel_fingerprint(),
+    }
+    if not args.no_cpu_baseline:
+        t_cpu, runs = cpu_baseline(w, xs)
+        model, ncpu = cpu_info()
+        out["cpu_baseline"] = {
+            "value": round(metrics.busbw_gbps(M, t_cpu, N), 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole {w.key} collective ({N} ranks x {M >> 20} MiB) in the "
+                      f"single-threaded C++ state-machine oracle, median of {runs} runs, "
+                      f"{t_cpu:.3f} s each; host {model}, {ncpu} CPUs visible",
+        }
+    print(json.dumps(out), flush=True)
+    comm.close()
+
+
+if __name__ == "__main__":
+    main()

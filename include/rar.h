@@ -1,0 +1,187 @@
+/*
+ * rar.h -- C ABI of the MI355X ring AllReduce library (librar.so).
+ *
+ * One GPU hosts N virtual ranks.  Every rank owns a send and a receive buffer
+ * in device memory; neighbouring ranks on the ring exchange data through FIFOs
+ * of NCCL_STEPS (8) slots that the library owns.  One call launches one HIP
+ * kernel that runs every (rank, channel) of the collective.
+ *
+ * Sources for the semantics (two public course pages on NCCL):
+ *   [C12] "NCCL 专家课程 12：Ring AllReduce 逐步推导、真实 Ring 与 Channel 并行"
+ *         (ring AllReduce step by step, real rings and channel parallelism)
+ *   [C23] "NCCL 专家课程 23：Device Kernel、Primitives、Step/Credit 与 LL Flag"
+ *         (device kernel, primitives, step/credit and the LL flag)
+ *
+ * General rules
+ *   - All entry points are plain C; nothing throws across the boundary.
+ *   - Device pointers are HIP device addresses (hipMalloc or a framework
+ *     allocator on the same device).  Host arrays of pointers are read during
+ *     the call and not kept.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Calls are stream ordered and asynchronous: the caller must keep every
+ *     buffer alive and unmodified until the stream has passed the call
+ *     [C23 "排障树": reusing a buffer before the stream completes corrupts it].
+ *   - Calls on one communicator must be issued in order on one stream.
+ *   - On any error nothing is launched; rar_get_last_error() gives detail.
+ */
+#ifndef RAR_H
+#define RAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RAR_SUCCESS = 0,
+  RAR_INVALID_ARGUMENT = 1, /* a precondition below is violated            */
+  RAR_UNSUPPORTED = 2,      /* valid request this build or device cannot run */
+  RAR_HIP_ERROR = 3,        /* the HIP runtime reported an error            */
+  RAR_INTERNAL_ERROR = 4,   /* a library invariant failed                   */
+  RAR_ABORTED = 5           /* a previous launch hit the wait watchdog; the
+                               communicator is poisoned and must be destroyed */
+} rar_result_t;
+
+/* Protocols [C23 "Simple 的 Credit 与 Step", "LL：Data 与 Flag 同 Line",
+ * "LL128：15/16 Payload"]. */
+typedef enum { RAR_PROTO_LL = 0, RAR_PROTO_LL128 = 1, RAR_PROTO_SIMPLE = 2 } rar_proto_t;
+
+/* Element types.  bfloat16 partial sums are rounded to bfloat16 (nearest,
+ * ties to even) after every ring hop; int32 wraps modulo 2^32. */
+typedef enum { RAR_INT32 = 0, RAR_FLOAT32 = 1, RAR_BFLOAT16 = 2 } rar_dtype_t;
+
+typedef enum { RAR_SUM = 0 } rar_redop_t;
+
+typedef struct rar_comm* rar_comm_t;
+
+/* Performance knobs; none of them changes any result bit. */
+typedef struct {
+  int lanes_per_channel; /* workgroups that split each channel's slices; each
+                            lane owns its own head/tail counters. 0 = auto   */
+  int waves_per_lane;    /* 64-thread waves per workgroup (1..8). 0 = auto   */
+  int spin_timeout_us;   /* watchdog for every device-side wait, in
+                            microseconds. 0 = 10 s                        */
+  int debug_flags;       /* test hooks, 0 in normal use.  Bit 0: receivers
+                            never publish head credit (the pages' "drop recv
+                            head" fault), so senders stall after exactly
+                            NCCL_STEPS slots and the watchdog ends the launch
+                            with RAR_ABORTED [C23 "状态机故障注入"]        */
+} rar_tuning_t;
+
+#define RAR_DEBUG_DROP_RECV_HEAD 1
+
+/* Create a communicator: the ring, the active channels, the protocol and the
+ * FIFOs for every (rank, channel).  Allocates N * popcount(mask) * buffSize
+ * bytes of FIFO plus counters on the current HIP device and zeroes them.
+ *
+ *   nranks       2..64 virtual ranks
+ *   ring_order   [nranks] user ranks listed along `next`; must be a
+ *                permutation (any rotation names the same ring).  The ring
+ *                index of a rank is its distance from rank 0 [C12 "ring index
+ *                如何计算"; "Graph 如何变成完整 ring"].
+ *   channel_mask active channels; bit c set = channel c runs.  Channels may be
+ *                sparse; the n-th set bit is the n-th workgroup set
+ *                [C23 "Kernel 如何把 Block 映射到 Channel"].  Must be nonzero.
+ *   proto        RAR_PROTO_*.
+ *   buff_size    FIFO bytes per (rank, channel); 0 = protocol default
+ *                (Simple 4 MiB, LL 512 KiB, LL128 4915200).  Must be a
+ *                multiple of 512 (Simple), 256 (LL) or 2048 (LL128), at most
+ *                2 GiB.
+ *   chunk_steps  Simple: FIFO steps per chunk, 2 or 4 (0 = 4).  A chunk of 8
+ *                steps fills all slots and deadlocks the ring.  Ignored by LL
+ *                and LL128, whose chunk is one step.
+ *   tuning       NULL for defaults.
+ * Errors: RAR_INVALID_ARGUMENT for any violation above or a NULL pointer;
+ * RAR_UNSUPPORTED if the device cannot keep every workgroup resident;
+ * RAR_HIP_ERROR if allocation fails. */
+rar_result_t rar_comm_create(rar_comm_t* comm, int nranks, const int* ring_order,
+                             uint64_t channel_mask, rar_proto_t proto, size_t buff_size,
+                             int chunk_steps, const rar_tuning_t* tuning);
+
+/* AllReduce of `count` elements over all virtual ranks [C12; C23 "Ring
+ * AllReduce 到 Primitive"]: afterwards every recvbufs[r][i] holds the sum over
+ * ranks of sendbufs[r][i], folded in ring order (the rank after the chunk's
+ * owner starts, the owner adds last), identical on every rank.
+ *   sendbufs, recvbufs  host arrays of `nranks` device pointers, each 16-byte
+ *                       aligned.  recvbufs[r] == sendbufs[r] runs in place;
+ *                       other overlap is not allowed.
+ *   count               elements per rank; 0 launches nothing, leaves the
+ *                       FIFO steps untouched and does not look at the pointers.
+ * Inside rar_group_start/rar_group_end the call is queued instead of launched.
+ * Errors: RAR_INVALID_ARGUMENT (NULL or misaligned pointer, bad enum),
+ * RAR_UNSUPPORTED (op other than sum), RAR_ABORTED (poisoned communicator),
+ * RAR_HIP_ERROR (launch failed). */
+rar_result_t rar_allreduce(rar_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                           size_t count, rar_dtype_t dtype, rar_redop_t op, void* stream);
+
+/* Fused works [C23 "RunWorkBatch 与 Fused Work"]: AllReduces queued between
+ * start and end run as one launch; their elements are laid end to end and cut
+ * into one contiguous range per channel, each channel executing its pieces in
+ * call order from work batches staged in LDS.  All queued calls must share
+ * one dtype.  The pointer arrays are copied when queued.  Errors as above;
+ * rar_group_end with nothing queued is a no-op. */
+rar_result_t rar_group_start(rar_comm_t comm);
+rar_result_t rar_group_end(rar_comm_t comm, void* stream);
+
+/* Destroy after the stream has passed the last call.  NULL is a no-op. */
+rar_result_t rar_comm_destroy(rar_comm_t comm);
+
+/* One-shot form of the pages' problem statement: creates (and caches, keyed
+ * by every argument that shapes the FIFOs) a communicator on first use, then
+ * runs rar_allreduce.  The mask is the nchannels lowest bits.  Errors as for
+ * rar_comm_create and rar_allreduce. */
+rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                            size_t count, rar_dtype_t dtype, rar_redop_t op,
+                            const int* ring_order, rar_proto_t proto, int nchannels,
+                            size_t buff_size, int chunk_steps, void* stream);
+
+/* Watchdog status: RAR_ABORTED if a launch on this communicator timed out in
+ * a wait, else RAR_SUCCESS.  Does not synchronize; reflects launches the
+ * device has finished. */
+rar_result_t rar_comm_get_async_error(rar_comm_t comm);
+
+/* Hang triage [C23 "排障树"]: synchronizes the device, then writes for every
+ * connector lane (receiving rank r, dense channel n, lane p) two values at
+ * out[((r*C+n)*P+p)*2]: tail (producer step; for LL/LL128 only updated at the
+ * end of a launch) and head (consumer step).  `cap` is the number of int64
+ * slots available; *written receives the number used. */
+rar_result_t rar_comm_query_state(rar_comm_t comm, int64_t* out, size_t cap, size_t* written);
+
+/* Geometry of a communicator: active channels C, lanes per channel P, waves
+ * per lane W, workgroups in the grid G (including idle padding). */
+rar_result_t rar_comm_shape(rar_comm_t comm, int* nchannels, int* lanes, int* waves, int* grid);
+
+/* ---- host planner, exposed for testing (no device needed) ------------------ */
+
+/* Ring index, prev and next of every user rank, as rar_comm_create computes
+ * them.  Errors: RAR_INVALID_ARGUMENT if ring_order is not a permutation. */
+rar_result_t rar_ring_info(int nranks, const int* ring_order, int* index, int* prev, int* next);
+
+typedef struct {
+  int32_t channel;    /* dense channel index n                        */
+  int32_t channel_id; /* n-th set bit of the mask                     */
+  int32_t work;       /* position of the collective in the launch     */
+  int32_t pad;
+  int64_t grid_offset;   /* first element of the piece in that collective */
+  int64_t channel_count; /* elements of the piece                         */
+  int64_t chunk_count;   /* protocol maximum chunk, in elements           */
+} rar_piece_t;
+
+/* The channel split of a launch of `nworks` collectives of `counts[i]`
+ * elements.  Writes at most `cap` pieces, returns the total in *npieces and
+ * the protocol's chunk maximum (elements) in *chunk_max. */
+rar_result_t rar_plan_pieces(int nranks, uint64_t channel_mask, rar_proto_t proto,
+                             size_t buff_size, int chunk_steps, rar_dtype_t dtype, int nworks,
+                             const size_t* counts, rar_piece_t* pieces, int cap, int* npieces,
+                             int64_t* chunk_max);
+
+const char* rar_get_error_string(rar_result_t r);
+/* Detail of the last failing call on this thread (empty if none). */
+const char* rar_get_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RAR_H */

@@ -110,7 +110,8 @@ bool valid_params(int nranks, uint64_t mask, int proto, size_t buff_size, int ch
   if (proto == ORC_PROTO_SIMPLE) {
     if (chunk_steps != 2 && chunk_steps != 4 && chunk_steps != 8) return false;
     if (slots % (chunk_steps / 2) != 0) return false;
-    if (buff_size == 0 || buff_size % ((size_t)slots * 16) != 0) return false;
+    // a slice is rounded up to 16 elements; 64-byte steps keep it inside its slots
+    if (buff_size == 0 || buff_size % ((size_t)slots * 64) != 0) return false;
   } else if (proto == ORC_PROTO_LL) {
     if (buff_size == 0 || buff_size % ((size_t)slots * 32) != 0) return false;
   } else if (proto == ORC_PROTO_LL128) {

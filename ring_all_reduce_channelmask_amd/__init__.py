@@ -1,1 +1,159 @@
-"""Ring AllReduce on one MI355X hosting N virtual ranks (HIP, gfx950)."""
+"""Ring AllReduce on one MI355X hosting N virtual ranks (HIP, gfx950).
+
+Thin Python binding of librar.so: every byte the collective moves is moved by
+the HIP kernel; this module only marshals pointers, sizes and the stream.
+torch supplies device memory (tensors) and streams.
+
+    comm = Comm(4, [0, 2, 3, 1], mask=0xFFF, proto="SIMPLE")
+    comm.allreduce(sends, recvs)          # lists of N CUDA tensors
+    with comm.group():                    # fused works, one launch
+        for s, r in pairs:
+            comm.allreduce(s, r)
+"""
+import contextlib
+import ctypes
+
+from . import _lib
+from ._lib import RarError  # noqa: F401
+
+__all__ = ["Comm", "ring_allreduce", "ring_info", "plan_pieces", "RarError"]
+
+
+def _dtype_name(t):
+    import torch
+    m = {torch.float32: "float32", torch.bfloat16: "bfloat16", torch.int32: "int32"}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def _check_tensors(sends, recvs, nranks):
+    if len(sends) != nranks or len(recvs) != nranks:
+        raise ValueError(f"need {nranks} send and {nranks} recv tensors")
+    n = sends[0].numel()
+    dt = sends[0].dtype
+    for t in list(sends) + list(recvs):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+        if t.numel() != n or t.dtype != dt:
+            raise ValueError("all tensors need the same size and dtype")
+    return n, _dtype_name(sends[0])
+
+
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Comm:
+    """A communicator: N virtual ranks on the current device, one ring, a
+    channel mask and a protocol; owns the FIFOs between ring neighbours."""
+
+    def __init__(self, nranks, ring_order, mask, proto="SIMPLE", buff_size=0, chunk_steps=0,
+                 lanes=0, waves=0, timeout_us=0, debug_flags=0):
+        lib = _lib.load()
+        if len(ring_order) != nranks:
+            raise ValueError("ring_order must list every rank once")
+        self.nranks = nranks
+        self.ring_order = list(ring_order)
+        self.mask = mask
+        self.proto = proto
+        order = (ctypes.c_int * nranks)(*self.ring_order)
+        tune = _lib.Tuning(lanes, waves, timeout_us, debug_flags)
+        h = ctypes.c_void_p()
+        _lib.check(lib.rar_comm_create(ctypes.byref(h), nranks, order, mask, _lib.PROTO[proto],
+                                       buff_size, chunk_steps, ctypes.byref(tune)))
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def allreduce(self, sends, recvs=None, stream=None):
+        """Sum over ranks; ``recvs=None`` runs in place."""
+        recvs = sends if recvs is None else recvs
+        n, dt = _check_tensors(sends, recvs, self.nranks)
+        lib = _lib.load()
+        _lib.check(lib.rar_allreduce(self._h, _ptr_array(sends), _ptr_array(recvs), n,
+                                     _lib.DTYPE[dt], _lib.SUM, _stream_handle(stream)))
+
+    @contextlib.contextmanager
+    def group(self, stream=None):
+        lib = _lib.load()
+        _lib.check(lib.rar_group_start(self._h))
+        try:
+            yield self
+        finally:
+            _lib.check(lib.rar_group_end(self._h, _stream_handle(stream)))
+
+    def async_error(self):
+        return _lib.load().rar_comm_get_async_error(self._h)
+
+    def shape(self):
+        c, p, w, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        _lib.check(_lib.load().rar_comm_shape(self._h, ctypes.byref(c), ctypes.byref(p),
+                                              ctypes.byref(w), ctypes.byref(g)))
+        return dict(channels=c.value, lanes=p.value, waves=w.value, grid=g.value)
+
+    def query_state(self):
+        s = self.shape()
+        cap = self.nranks * s["channels"] * s["lanes"] * 2
+        out = (ctypes.c_int64 * cap)()
+        written = ctypes.c_size_t()
+        _lib.check(_lib.load().rar_comm_query_state(self._h, out, cap, ctypes.byref(written)))
+        return list(out[:written.value])
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.load().rar_comm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def ring_allreduce(sends, recvs, ring_order, proto="SIMPLE", nchannels=1, buff_size=0,
+                   chunk_steps=0, stream=None):
+    """The pages' problem statement as one call (communicator cached inside)."""
+    nranks = len(sends)
+    n, dt = _check_tensors(sends, recvs, nranks)
+    lib = _lib.load()
+    order = (ctypes.c_int * nranks)(*ring_order)
+    _lib.check(lib.ring_allreduce(_ptr_array(sends), _ptr_array(recvs), nranks, n,
+                                  _lib.DTYPE[dt], _lib.SUM, order, _lib.PROTO[proto], nchannels,
+                                  buff_size, chunk_steps, _stream_handle(stream)))
+
+
+def ring_info(ring_order):
+    """(index, prev, next) per user rank, as the library computes them."""
+    n = len(ring_order)
+    idx, prv, nxt = (ctypes.c_int * n)(), (ctypes.c_int * n)(), (ctypes.c_int * n)()
+    _lib.check(_lib.load().rar_ring_info(n, (ctypes.c_int * n)(*ring_order), idx, prv, nxt))
+    return list(idx), list(prv), list(nxt)
+
+
+def plan_pieces(nranks, mask, proto, buff_size, chunk_steps, dtype, counts):
+    """The library's channel split: (pieces as dicts, chunk maximum)."""
+    counts = list(counts)
+    cap = 64 * (len(counts) + 1)
+    arr = (_lib.Piece * cap)()
+    npieces, cmax = ctypes.c_int(), ctypes.c_int64()
+    carr = (ctypes.c_size_t * len(counts))(*counts)
+    _lib.check(_lib.load().rar_plan_pieces(nranks, mask, _lib.PROTO[proto], buff_size,
+                                           chunk_steps, _lib.DTYPE[dtype], len(counts), carr,
+                                           arr, cap, ctypes.byref(npieces), ctypes.byref(cmax)))
+    assert npieces.value <= cap
+    return ([dict(channel=p.channel, channel_id=p.channel_id, work=p.work,
+                  grid_offset=p.grid_offset, channel_count=p.channel_count,
+                  chunk_count=p.chunk_count) for p in arr[:npieces.value]], cmax.value)

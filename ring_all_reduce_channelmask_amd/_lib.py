@@ -1,0 +1,88 @@
+"""ctypes declarations for librar.so (the C ABI in include/rar.h).
+
+Argument marshalling only.  torch is imported first so that the process has
+one HIP runtime (torch's), which librar.so then shares.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "librar.so")
+
+SUCCESS, INVALID_ARGUMENT, UNSUPPORTED, HIP_ERROR, INTERNAL_ERROR, ABORTED = range(6)
+PROTO = {"LL": 0, "LL128": 1, "SIMPLE": 2}
+DTYPE = {"int32": 0, "float32": 1, "bfloat16": 2}
+SUM = 0
+
+
+class Tuning(ctypes.Structure):
+    _fields_ = [("lanes_per_channel", ctypes.c_int), ("waves_per_lane", ctypes.c_int),
+                ("spin_timeout_us", ctypes.c_int), ("debug_flags", ctypes.c_int)]
+
+
+class Piece(ctypes.Structure):
+    _fields_ = [("channel", ctypes.c_int32), ("channel_id", ctypes.c_int32),
+                ("work", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("grid_offset", ctypes.c_int64), ("channel_count", ctypes.c_int64),
+                ("chunk_count", ctypes.c_int64)]
+
+
+class RarError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+_lib = None
+
+# (name, restype, argtypes) of every entry point in include/rar.h
+_c = ctypes
+_vpp = _c.POINTER(_c.c_void_p)
+_ip = _c.POINTER(_c.c_int)
+SIGNATURES = [
+    ("rar_comm_create", _c.c_int, [_c.POINTER(_c.c_void_p), _c.c_int, _ip, _c.c_uint64, _c.c_int,
+                                   _c.c_size_t, _c.c_int, _c.POINTER(Tuning)]),
+    ("rar_allreduce", _c.c_int, [_c.c_void_p, _vpp, _vpp, _c.c_size_t, _c.c_int, _c.c_int,
+                                 _c.c_void_p]),
+    ("rar_group_start", _c.c_int, [_c.c_void_p]),
+    ("rar_group_end", _c.c_int, [_c.c_void_p, _c.c_void_p]),
+    ("rar_comm_destroy", _c.c_int, [_c.c_void_p]),
+    ("ring_allreduce", _c.c_int, [_vpp, _vpp, _c.c_int, _c.c_size_t, _c.c_int, _c.c_int, _ip,
+                                  _c.c_int, _c.c_int, _c.c_size_t, _c.c_int, _c.c_void_p]),
+    ("rar_comm_get_async_error", _c.c_int, [_c.c_void_p]),
+    ("rar_comm_query_state", _c.c_int, [_c.c_void_p, _c.POINTER(_c.c_int64), _c.c_size_t,
+                                        _c.POINTER(_c.c_size_t)]),
+    ("rar_comm_shape", _c.c_int, [_c.c_void_p, _ip, _ip, _ip, _ip]),
+    ("rar_ring_info", _c.c_int, [_c.c_int, _ip, _ip, _ip, _ip]),
+    ("rar_plan_pieces", _c.c_int, [_c.c_int, _c.c_uint64, _c.c_int, _c.c_size_t, _c.c_int,
+                                   _c.c_int, _c.c_int, _c.POINTER(_c.c_size_t),
+                                   _c.POINTER(Piece), _c.c_int, _ip, _c.POINTER(_c.c_int64)]),
+    ("rar_get_error_string", _c.c_char_p, [_c.c_int]),
+    ("rar_get_last_error", _c.c_char_p, []),
+]
+
+
+def load():
+    """Load librar.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- one HIP runtime per process: torch's
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python ring_all_reduce_channelmask_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, res, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(code):
+    if code != SUCCESS:
+        lib = load()
+        detail = lib.rar_get_last_error().decode()
+        name = lib.rar_get_error_string(code).decode()
+        raise RarError(code, f"{name}: {detail}")

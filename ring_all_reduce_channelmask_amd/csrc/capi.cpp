@@ -1,0 +1,488 @@
+// capi.cpp -- the C ABI declared in include/rar.h.
+//
+// A communicator owns, on one HIP device: the FIFOs of every (rank, channel),
+// the head/tail counters of every connector lane, the abort words, the
+// workgroup map, and a small arena into which each launch's work batches,
+// works and buffer pointers are copied before the kernel runs.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "plan.h"
+#include "rar.h"
+#include "rar_device.h"
+
+namespace rar {
+const void* get_kernel(int dtype, int proto);
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rar_result_t fail(rar_result_t r, const std::string& msg) {
+  g_last_error = msg;
+  return r;
+}
+
+#define RAR_HIP(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess)                                                                  \
+      return fail(RAR_HIP_ERROR, std::string(#expr) + " failed: " + hipGetErrorString(e_)); \
+  } while (0)
+
+struct QueuedCall {
+  std::vector<void*> send, recv;
+  size_t count;
+  int dtype;
+};
+
+size_t align_to(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+struct rar_comm {
+  int device = 0;
+  int nranks = 0;
+  std::vector<int> order;
+  rar::RingInfo ring;
+  uint64_t mask = 0;
+  int C = 0, P = 0, W = 0, grid = 0;
+  int proto = 0;
+  size_t buff = 0;
+  int chunk_steps = 4;
+  uint64_t timeout_ticks = 0;
+  rar::DevComm* d_comm = nullptr;
+  uint8_t* d_fifo = nullptr;
+  rar::ConnCounters* d_counters = nullptr;
+  uint32_t* d_abort = nullptr;
+  uint32_t* h_abort = nullptr;
+  uint32_t* d_abort_host = nullptr;
+  uint32_t* d_wgmap = nullptr;
+  uint8_t* d_arena = nullptr;
+  size_t arena_cap = 0;
+  uint8_t* h_stage = nullptr;
+  size_t stage_cap = 0;
+  std::vector<uint8_t> last_upload;
+  hipEvent_t upload_done = nullptr;
+  bool upload_pending = false;
+  bool in_group = false;
+  std::vector<QueuedCall> queue;
+};
+
+namespace {
+
+void release(rar_comm* c) {
+  if (!c) return;
+  if (c->upload_done) (void)hipEventDestroy(c->upload_done);
+  if (c->h_stage) (void)hipHostFree(c->h_stage);
+  if (c->h_abort) (void)hipHostFree(c->h_abort);
+  (void)hipFree(c->d_arena);
+  (void)hipFree(c->d_wgmap);
+  (void)hipFree(c->d_abort);
+  (void)hipFree(c->d_counters);
+  (void)hipFree(c->d_fifo);
+  (void)hipFree(c->d_comm);
+  delete c;
+}
+
+rar_result_t check_dtype(int dtype) {
+  if (dtype != RAR_INT32 && dtype != RAR_FLOAT32 && dtype != RAR_BFLOAT16)
+    return fail(RAR_INVALID_ARGUMENT, "unknown dtype");
+  return RAR_SUCCESS;
+}
+
+rar_result_t check_buffers(const rar_comm* c, const void* const* sendbufs, void* const* recvbufs) {
+  if (!sendbufs || !recvbufs) return fail(RAR_INVALID_ARGUMENT, "sendbufs/recvbufs is NULL");
+  for (int r = 0; r < c->nranks; ++r) {
+    if (!sendbufs[r] || !recvbufs[r])
+      return fail(RAR_INVALID_ARGUMENT, "buffer of rank " + std::to_string(r) + " is NULL");
+    if ((reinterpret_cast<uintptr_t>(sendbufs[r]) & 15) ||
+        (reinterpret_cast<uintptr_t>(recvbufs[r]) & 15))
+      return fail(RAR_INVALID_ARGUMENT,
+                  "buffer of rank " + std::to_string(r) + " is not 16-byte aligned");
+  }
+  return RAR_SUCCESS;
+}
+
+// Copy the launch description into the device arena (skipped when it is
+// byte-identical to the previous launch's) and launch the kernel.
+rar_result_t launch(rar_comm* c, const std::vector<QueuedCall>& calls, hipStream_t stream) {
+  const int dtype = calls.front().dtype;
+  const int64_t es = rar::elem_size(dtype);
+  std::vector<size_t> counts;
+  for (const QueuedCall& q : calls) counts.push_back(q.count);
+  const std::vector<rar::Piece> pieces =
+      rar::split_channels(c->mask, c->proto, c->buff, c->chunk_steps, es, counts);
+  if (pieces.empty()) return RAR_SUCCESS;  // nothing to move: no launch, no step advance
+  if (__atomic_load_n(c->h_abort, __ATOMIC_ACQUIRE))
+    return fail(RAR_ABORTED, "a previous launch on this communicator hit the wait watchdog");
+  const rar::BatchPlan plan = rar::encode_batches(pieces, c->C, c->W);
+
+  const size_t off_batches = 0;
+  const size_t off_works = align_to(off_batches + plan.batches.size() * sizeof(rar::DevBatch), 64);
+  const size_t off_ptrs = align_to(off_works + plan.works.size() * sizeof(rar::DevWork), 64);
+  const size_t nptrs = calls.size() * (size_t)c->nranks * 2;
+  const size_t off_first = align_to(off_ptrs + nptrs * sizeof(void*), 64);
+  const size_t total = align_to(off_first + plan.first_batch.size() * sizeof(uint32_t), 64);
+  std::vector<uint8_t> bytes(total, 0);
+  std::memcpy(bytes.data() + off_batches, plan.batches.data(), plan.batches.size() * sizeof(rar::DevBatch));
+  std::memcpy(bytes.data() + off_works, plan.works.data(), plan.works.size() * sizeof(rar::DevWork));
+  void** ptrs = reinterpret_cast<void**>(bytes.data() + off_ptrs);
+  for (size_t w = 0; w < calls.size(); ++w)
+    for (int r = 0; r < c->nranks; ++r) {
+      ptrs[(w * c->nranks + r) * 2] = calls[w].send[r];
+      ptrs[(w * c->nranks + r) * 2 + 1] = calls[w].recv[r];
+    }
+  std::memcpy(bytes.data() + off_first, plan.first_batch.data(), plan.first_batch.size() * sizeof(uint32_t));
+
+  if (bytes != c->last_upload) {
+    if (total > c->arena_cap) {
+      RAR_HIP(hipDeviceSynchronize());  // the old arena may still be read by a running launch
+      (void)hipFree(c->d_arena);
+      c->d_arena = nullptr;
+      c->arena_cap = 0;
+      RAR_HIP(hipMalloc(&c->d_arena, total * 2));
+      c->arena_cap = total * 2;
+      c->last_upload.clear();
+    }
+    if (c->upload_pending) RAR_HIP(hipEventSynchronize(c->upload_done));
+    c->upload_pending = false;
+    if (total > c->stage_cap) {
+      if (c->h_stage) RAR_HIP(hipHostFree(c->h_stage));
+      c->h_stage = nullptr;
+      c->stage_cap = 0;
+      RAR_HIP(hipHostMalloc(reinterpret_cast<void**>(&c->h_stage), total * 2, hipHostMallocDefault));
+      c->stage_cap = total * 2;
+    }
+    std::memcpy(c->h_stage, bytes.data(), total);
+    RAR_HIP(hipMemcpyAsync(c->d_arena, c->h_stage, total, hipMemcpyHostToDevice, stream));
+    RAR_HIP(hipEventRecord(c->upload_done, stream));
+    c->upload_pending = true;
+    c->last_upload.swap(bytes);
+  }
+
+  rar::KernelArgs args;
+  args.comm = c->d_comm;
+  args.batches = reinterpret_cast<const rar::DevBatch*>(c->d_arena + off_batches);
+  args.works = reinterpret_cast<const rar::DevWork*>(c->d_arena + off_works);
+  args.ptrs = reinterpret_cast<void* const*>(c->d_arena + off_ptrs);
+  args.first_batch = reinterpret_cast<const uint32_t*>(c->d_arena + off_first);
+  args.wg_map = c->d_wgmap;
+  void* params[] = {&args};
+  const void* fn = rar::get_kernel(dtype, c->proto);
+  if (!fn) return fail(RAR_INTERNAL_ERROR, "no kernel for this dtype/protocol");
+  RAR_HIP(hipLaunchCooperativeKernel(fn, dim3(c->grid), dim3(c->W * rar::kWaveSize), params, 0, stream));
+  return RAR_SUCCESS;
+}
+
+std::mutex g_cache_mu;
+std::map<std::vector<int64_t>, rar_comm*> g_cache;
+
+}  // namespace
+
+extern "C" {
+
+const char* rar_get_error_string(rar_result_t r) {
+  switch (r) {
+    case RAR_SUCCESS: return "success";
+    case RAR_INVALID_ARGUMENT: return "invalid argument";
+    case RAR_UNSUPPORTED: return "unsupported";
+    case RAR_HIP_ERROR: return "HIP runtime error";
+    case RAR_INTERNAL_ERROR: return "internal error";
+    case RAR_ABORTED: return "aborted by the wait watchdog";
+  }
+  return "unknown result code";
+}
+
+const char* rar_get_last_error(void) { return g_last_error.c_str(); }
+
+rar_result_t rar_ring_info(int nranks, const int* ring_order, int* index, int* prev, int* next) {
+  g_last_error.clear();
+  rar::RingInfo ring;
+  std::string err;
+  if (!rar::build_ring(nranks, ring_order, &ring, &err)) return fail(RAR_INVALID_ARGUMENT, err);
+  for (int r = 0; r < nranks; ++r) {
+    if (index) index[r] = ring.index[r];
+    if (prev) prev[r] = ring.prev[r];
+    if (next) next[r] = ring.next[r];
+  }
+  return RAR_SUCCESS;
+}
+
+rar_result_t rar_plan_pieces(int nranks, uint64_t channel_mask, rar_proto_t proto, size_t buff_size,
+                             int chunk_steps, rar_dtype_t dtype, int nworks, const size_t* counts,
+                             rar_piece_t* pieces, int cap, int* npieces, int64_t* chunk_max) {
+  g_last_error.clear();
+  if (buff_size == 0) buff_size = rar::default_buff_size(proto);
+  if (chunk_steps == 0) chunk_steps = 4;
+  std::string err;
+  if (!rar::check_shape(nranks, channel_mask, proto, buff_size, chunk_steps, &err))
+    return fail(RAR_INVALID_ARGUMENT, err);
+  if (rar_result_t r = check_dtype(dtype)) return r;
+  if (nworks < 1 || !counts || !npieces) return fail(RAR_INVALID_ARGUMENT, "bad work list");
+  std::vector<size_t> cv(counts, counts + nworks);
+  const int64_t es = rar::elem_size(dtype);
+  const std::vector<rar::Piece> ps = rar::split_channels(channel_mask, proto, buff_size, chunk_steps, es, cv);
+  *npieces = (int)ps.size();
+  if (chunk_max) *chunk_max = rar::chunk_max_elems(proto, buff_size, chunk_steps, es);
+  for (int i = 0; i < (int)ps.size() && i < cap; ++i) {
+    pieces[i].channel = ps[i].channel;
+    pieces[i].channel_id = ps[i].channel_id;
+    pieces[i].work = ps[i].work;
+    pieces[i].pad = 0;
+    pieces[i].grid_offset = ps[i].grid_offset;
+    pieces[i].channel_count = ps[i].channel_count;
+    pieces[i].chunk_count = ps[i].chunk_count;
+  }
+  return RAR_SUCCESS;
+}
+
+rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order, uint64_t channel_mask,
+                             rar_proto_t proto, size_t buff_size, int chunk_steps,
+                             const rar_tuning_t* tuning) {
+  g_last_error.clear();
+  if (!out) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
+  *out = nullptr;
+  if (buff_size == 0) buff_size = rar::default_buff_size(proto);
+  if (chunk_steps == 0) chunk_steps = 4;
+  std::string err;
+  if (!rar::check_shape(nranks, channel_mask, proto, buff_size, chunk_steps, &err))
+    return fail(RAR_INVALID_ARGUMENT, err);
+  rar::RingInfo ring;
+  if (!rar::build_ring(nranks, ring_order, &ring, &err)) return fail(RAR_INVALID_ARGUMENT, err);
+  rar_tuning_t tune{0, 0, 0, 0};
+  if (tuning) tune = *tuning;
+  if (tune.lanes_per_channel < 0 || tune.lanes_per_channel > rar::kMaxLanes)
+    return fail(RAR_INVALID_ARGUMENT, "lanes_per_channel must be in [0, 16]");
+  if (tune.waves_per_lane < 0 || tune.waves_per_lane > rar::kMaxWaves)
+    return fail(RAR_INVALID_ARGUMENT, "waves_per_lane must be in [0, 8]");
+  if (tune.spin_timeout_us < 0) return fail(RAR_INVALID_ARGUMENT, "spin_timeout_us is negative");
+
+  int dev = 0;
+  RAR_HIP(hipGetDevice(&dev));
+  int cus = 0, coop = 0;
+  RAR_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+  RAR_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+  if (!coop) return fail(RAR_UNSUPPORTED, "device has no cooperative launch");
+
+  rar_comm* c = new rar_comm();
+  c->device = dev;
+  c->nranks = nranks;
+  c->order.assign(ring_order, ring_order + nranks);
+  c->ring = ring;
+  c->mask = channel_mask;
+  c->C = __builtin_popcountll(channel_mask);
+  c->proto = proto;
+  c->buff = buff_size;
+  c->chunk_steps = chunk_steps;
+  c->P = tune.lanes_per_channel ? tune.lanes_per_channel : rar::auto_lanes(nranks, c->C, cus);
+  c->W = tune.waves_per_lane ? tune.waves_per_lane : ((int)proto == rar::kLL ? 4 : 8);
+  const uint64_t timeout_us = tune.spin_timeout_us ? (uint64_t)tune.spin_timeout_us : 10000000ull;
+  c->timeout_ticks = timeout_us * 100ull;  // s_memrealtime runs at 100 MHz
+  const std::vector<uint32_t> wg = rar::make_wg_map(nranks, c->C, c->P);
+  c->grid = (int)wg.size();
+
+  // every workgroup must be resident at once: the ranks wait on each other
+  for (int dt = 0; dt < 3; ++dt) {
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rar::get_kernel(dt, proto),
+                                                                c->W * rar::kWaveSize, 0);
+    if (e != hipSuccess) {
+      release(c);
+      return fail(RAR_HIP_ERROR, std::string("occupancy query failed: ") + hipGetErrorString(e));
+    }
+    if ((int64_t)per_cu * cus < c->grid) {
+      const int g = c->grid;
+      release(c);
+      return fail(RAR_UNSUPPORTED, "grid of " + std::to_string(g) +
+                                       " workgroups cannot be co-resident; lower lanes or waves");
+    }
+  }
+
+  auto guard = [&](hipError_t e, const char* what) -> rar_result_t {
+    if (e == hipSuccess) return RAR_SUCCESS;
+    release(c);
+    return fail(RAR_HIP_ERROR, std::string(what) + " failed: " + hipGetErrorString(e));
+  };
+  const int64_t lane_step = rar::lane_step_bytes(proto, buff_size, c->P);
+  const size_t fifo_bytes = (size_t)nranks * c->C * c->P * rar::kSteps * (size_t)lane_step;
+  const size_t counter_bytes = (size_t)nranks * c->C * c->P * sizeof(rar::ConnCounters);
+  rar_result_t r;
+  if ((r = guard(hipMalloc(&c->d_fifo, fifo_bytes), "hipMalloc(fifo)"))) return r;
+  if ((r = guard(hipMalloc(&c->d_counters, counter_bytes), "hipMalloc(counters)"))) return r;
+  if ((r = guard(hipMalloc(&c->d_abort, 256), "hipMalloc(abort)"))) return r;
+  if ((r = guard(hipMalloc(&c->d_wgmap, wg.size() * sizeof(uint32_t)), "hipMalloc(wgmap)"))) return r;
+  if ((r = guard(hipMalloc(&c->d_comm, sizeof(rar::DevComm)), "hipMalloc(comm)"))) return r;
+  if ((r = guard(hipHostMalloc(reinterpret_cast<void**>(&c->h_abort), 256, hipHostMallocMapped),
+                 "hipHostMalloc(abort)")))
+    return r;
+  std::memset(c->h_abort, 0, 256);
+  if ((r = guard(hipHostGetDevicePointer(reinterpret_cast<void**>(&c->d_abort_host), c->h_abort, 0),
+                 "hipHostGetDevicePointer")))
+    return r;
+  if ((r = guard(hipEventCreateWithFlags(&c->upload_done, hipEventDisableTiming), "hipEventCreate")))
+    return r;
+  if ((r = guard(hipMemset(c->d_fifo, 0, fifo_bytes), "hipMemset(fifo)"))) return r;
+  if ((r = guard(hipMemset(c->d_counters, 0, counter_bytes), "hipMemset(counters)"))) return r;
+  if ((r = guard(hipMemset(c->d_abort, 0, 256), "hipMemset(abort)"))) return r;
+  if ((r = guard(hipMemcpy(c->d_wgmap, wg.data(), wg.size() * sizeof(uint32_t), hipMemcpyHostToDevice),
+                 "hipMemcpy(wgmap)")))
+    return r;
+  rar::DevComm hc;
+  std::memset(&hc, 0, sizeof(hc));
+  hc.hot.n_ranks = nranks;
+  hc.hot.n_channels = c->C;
+  hc.hot.n_lanes = c->P;
+  hc.hot.proto = proto;
+  hc.hot.buff_size = (int64_t)buff_size;
+  hc.hot.step_bytes = (int64_t)buff_size / rar::kSteps;
+  hc.hot.lane_step_bytes = lane_step;
+  hc.hot.lane_buff_bytes = lane_step * rar::kSteps;
+  hc.hot.chunk_steps = chunk_steps;
+  hc.hot.step_per_slice = (int)proto == rar::kSimple ? chunk_steps / 2 : 1;
+  hc.hot.channel_mask = channel_mask;
+  hc.hot.fifo = c->d_fifo;
+  hc.hot.counters = c->d_counters;
+  hc.hot.abort_flag = c->d_abort;
+  hc.hot.abort_host = c->d_abort_host;
+  hc.hot.spin_timeout_ticks = c->timeout_ticks;
+  hc.hot.debug_flags = tune.debug_flags;
+  for (int i = 0; i < nranks; ++i) {
+    hc.ranks[i].index = ring.index[i];
+    hc.ranks[i].prev = ring.prev[i];
+    hc.ranks[i].next = ring.next[i];
+  }
+  if ((r = guard(hipMemcpy(c->d_comm, &hc, sizeof(hc), hipMemcpyHostToDevice), "hipMemcpy(comm)")))
+    return r;
+  if ((r = guard(hipDeviceSynchronize(), "hipDeviceSynchronize"))) return r;
+  *out = c;
+  return RAR_SUCCESS;
+}
+
+rar_result_t rar_comm_destroy(rar_comm_t c) {
+  g_last_error.clear();
+  if (!c) return RAR_SUCCESS;
+  {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    for (auto it = g_cache.begin(); it != g_cache.end(); ++it)
+      if (it->second == c) {
+        g_cache.erase(it);
+        break;
+      }
+  }
+  release(c);
+  return RAR_SUCCESS;
+}
+
+rar_result_t rar_allreduce(rar_comm_t c, const void* const* sendbufs, void* const* recvbufs,
+                           size_t count, rar_dtype_t dtype, rar_redop_t op, void* stream) {
+  g_last_error.clear();
+  if (!c) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
+  if (rar_result_t r = check_dtype(dtype)) return r;
+  if (op != RAR_SUM) return fail(RAR_UNSUPPORTED, "only RAR_SUM is implemented");
+  if (c->in_group && !c->queue.empty() && c->queue.front().dtype != dtype)
+    return fail(RAR_UNSUPPORTED, "all AllReduces of a group must share one dtype");
+  // nothing to move: no launch, no step advance, pointers are not looked at
+  if (count == 0) return RAR_SUCCESS;
+  if (rar_result_t r = check_buffers(c, sendbufs, recvbufs)) return r;
+  if (count > (size_t(1) << 40)) return fail(RAR_INVALID_ARGUMENT, "count too large");
+  QueuedCall q;
+  for (int r = 0; r < c->nranks; ++r) q.send.push_back(const_cast<void*>(sendbufs[r]));
+  q.recv.assign(recvbufs, recvbufs + c->nranks);
+  q.count = count;
+  q.dtype = dtype;
+  if (c->in_group) {
+    c->queue.push_back(std::move(q));
+    return RAR_SUCCESS;
+  }
+  std::vector<QueuedCall> one;
+  one.push_back(std::move(q));
+  return launch(c, one, reinterpret_cast<hipStream_t>(stream));
+}
+
+rar_result_t rar_group_start(rar_comm_t c) {
+  g_last_error.clear();
+  if (!c) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
+  if (c->in_group) return fail(RAR_INVALID_ARGUMENT, "group already open");
+  c->in_group = true;
+  c->queue.clear();
+  return RAR_SUCCESS;
+}
+
+rar_result_t rar_group_end(rar_comm_t c, void* stream) {
+  g_last_error.clear();
+  if (!c) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
+  if (!c->in_group) return fail(RAR_INVALID_ARGUMENT, "no open group");
+  c->in_group = false;
+  std::vector<QueuedCall> calls;
+  calls.swap(c->queue);
+  if (calls.empty()) return RAR_SUCCESS;
+  return launch(c, calls, reinterpret_cast<hipStream_t>(stream));
+}
+
+rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                            rar_dtype_t dtype, rar_redop_t op, const int* ring_order, rar_proto_t proto,
+                            int nchannels, size_t buff_size, int chunk_steps, void* stream) {
+  g_last_error.clear();
+  if (nchannels < 1 || nchannels > 64) return fail(RAR_INVALID_ARGUMENT, "nchannels must be in [1, 64]");
+  if (nranks < 2 || nranks > 64 || !ring_order)
+    return fail(RAR_INVALID_ARGUMENT, "nranks must be in [2, 64] with a ring_order");
+  const uint64_t mask = nchannels == 64 ? ~0ull : ((1ull << nchannels) - 1);
+  if (buff_size == 0) buff_size = rar::default_buff_size(proto);
+  if (chunk_steps == 0) chunk_steps = 4;
+  int dev = 0;
+  RAR_HIP(hipGetDevice(&dev));
+  std::vector<int64_t> key = {dev, nranks, (int64_t)mask, (int64_t)proto, (int64_t)buff_size, chunk_steps};
+  key.insert(key.end(), ring_order, ring_order + nranks);
+  rar_comm* c = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    auto it = g_cache.find(key);
+    if (it != g_cache.end()) c = it->second;
+  }
+  if (!c) {
+    rar_result_t r = rar_comm_create(&c, nranks, ring_order, mask, proto, buff_size, chunk_steps, nullptr);
+    if (r != RAR_SUCCESS) return r;
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    g_cache[key] = c;
+  }
+  return rar_allreduce(c, sendbufs, recvbufs, count, dtype, op, stream);
+}
+
+rar_result_t rar_comm_get_async_error(rar_comm_t c) {
+  if (!c) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
+  return __atomic_load_n(c->h_abort, __ATOMIC_ACQUIRE) ? RAR_ABORTED : RAR_SUCCESS;
+}
+
+rar_result_t rar_comm_query_state(rar_comm_t c, int64_t* out, size_t cap, size_t* written) {
+  g_last_error.clear();
+  if (!c || !out || !written) return fail(RAR_INVALID_ARGUMENT, "NULL argument");
+  RAR_HIP(hipDeviceSynchronize());
+  const size_t lanes = (size_t)c->nranks * c->C * c->P;
+  std::vector<rar::ConnCounters> h(lanes);
+  RAR_HIP(hipMemcpy(h.data(), c->d_counters, lanes * sizeof(rar::ConnCounters), hipMemcpyDeviceToHost));
+  size_t k = 0;
+  for (size_t i = 0; i < lanes && k + 2 <= cap; ++i) {
+    out[k++] = (int64_t)h[i].tail.value;
+    out[k++] = (int64_t)h[i].head.value;
+  }
+  *written = k;
+  return RAR_SUCCESS;
+}
+
+rar_result_t rar_comm_shape(rar_comm_t c, int* nchannels, int* lanes, int* waves, int* grid) {
+  if (!c) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
+  if (nchannels) *nchannels = c->C;
+  if (lanes) *lanes = c->P;
+  if (waves) *waves = c->W;
+  if (grid) *grid = c->grid;
+  return RAR_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// plan.h -- host planner of one ring AllReduce launch.
+//
+// Computes, on the host and before any launch: the ring position of every
+// rank, the active channels, the channel split of the launch into
+// (collective, channel) pieces, the encoding of those pieces into work
+// batches, and the workgroup -> (rank, channel, lane) map of the grid.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "rar_device.h"
+
+namespace rar {
+
+struct RingInfo {
+  std::vector<int> index, prev, next;
+};
+
+// Ring set-up [NCCL 专家课程 12, "Graph 如何变成完整 ring" and "ring index 如何
+// 计算"]: ring_order lists user ranks along next.  Returns false (with a
+// message) unless every rank appears exactly once and the walk loops back.
+bool build_ring(int nranks, const int* ring_order, RingInfo* out, std::string* err);
+
+int64_t elem_size(int dtype);
+
+// Largest chunk in elements [NCCL 专家课程 23, "Buffer 到 Chunk 的实测公式";
+// LL and LL128 sections]: Simple = chunkSteps steps of buff/8 bytes; LL and
+// LL128 = one step of payload (8 of every 16, 120 of every 128 bytes).
+int64_t chunk_max_elems(int proto, size_t buff_size, int chunk_steps, int64_t es);
+
+// Parameter checks shared by every entry point.
+bool check_shape(int nranks, uint64_t mask, int proto, size_t buff_size, int chunk_steps,
+                 std::string* err);
+
+size_t default_buff_size(int proto);
+
+struct Piece {
+  int channel;     // dense index n
+  int channel_id;  // n-th set bit of the mask
+  int work;
+  int64_t grid_offset, channel_count, chunk_count;
+};
+
+// Channel split of the launch: the collectives are laid end to end, each
+// starting 16-byte aligned, and the element stream is cut into one
+// contiguous 16-byte aligned range per active channel, in channel order.
+std::vector<Piece> split_channels(uint64_t mask, int proto, size_t buff_size, int chunk_steps,
+                                  int64_t es, const std::vector<size_t>& counts);
+
+struct BatchPlan {
+  std::vector<DevBatch> batches;       // batches[0] is an unused sentinel
+  std::vector<DevWork> works;
+  std::vector<uint32_t> first_batch;   // per channel id, 64 entries (0 = no work)
+};
+
+// Pack each channel's pieces, in order, into batches of at most kBatchWorks
+// works (1024 bytes), chained by next_jump.
+BatchPlan encode_batches(const std::vector<Piece>& pieces, int n_channels, int n_waves);
+
+
+// Workgroup map: the N ranks of one (channel, lane) pipeline are placed on
+// the same XCD (workgroups are dispatched to the 8 XCDs round robin by
+// blockIdx), so their FIFO traffic stays in one L2.  Idle slots pad the grid.
+std::vector<uint32_t> make_wg_map(int nranks, int n_channels, int n_lanes);
+
+// Bytes of one slot of one lane's FIFO.  A channel's step is split among its
+// lanes in whole 16-byte vectors (Simple), 16-byte lines (LL) or 128-byte
+// lines (LL128); every lane owns 8 such slots, so the lanes of a channel never
+// touch each other's FIFO bytes.
+int64_t lane_step_bytes(int proto, size_t buff_size, int lanes);
+
+// Default lanes per channel: fill about one workgroup per CU.
+int auto_lanes(int nranks, int n_channels, int cus);
+
+}  // namespace rar

@@ -1,0 +1,103 @@
+// rar_device.h -- layouts shared by the host planner and the gfx950 kernel.
+//
+// Everything the kernel reads lives in device memory in the structures below.
+// Sizes are fixed and 16-byte multiples so that one wave can copy them into
+// LDS in 16-byte packs.
+#pragma once
+
+#include <stdint.h>
+
+namespace rar {
+
+constexpr int kSteps = 8;            // NCCL_STEPS: FIFO slots per connector
+constexpr int kSlicesPerChunk = 2;   // Simple: slices per chunk (StepPerSlice = chunkSteps/2)
+constexpr int kMaxRanks = 64;
+constexpr int kMaxChannels = 64;     // channelMask is 64 bits
+constexpr int kMaxLanes = 16;
+constexpr int kMaxWaves = 8;         // 512 threads: keeps the kernel free of register spills
+constexpr int kWaveSize = 64;
+constexpr int kBatchWorks = 16;      // 16 works x 64 B = a 1024-byte batch
+constexpr uint32_t kIdleWg = 0xFFFFFFFFu;
+
+enum Proto : int32_t { kLL = 0, kLL128 = 1, kSimple = 2 };
+
+// One (collective, channel) piece: what ncclDevWorkColl carries for runRing.
+struct alignas(16) DevWork {
+  int64_t grid_offset;    // first element of the piece in its collective
+  int64_t channel_count;  // elements of the piece
+  int64_t chunk_count;    // protocol maximum chunk (elements); the tail loop shrinks it
+  uint32_t buf_index;     // collective index into the pointer table
+  uint16_t n_waves;       // waves that move data for this work
+  uint16_t flags;
+  uint32_t pad[6];
+};
+static_assert(sizeof(DevWork) == 64, "DevWork must be 64 bytes");
+
+// Header of a work batch: works are the set bits of offset_bitset, counted
+// from offset_base in the work array.  next_jump chains the next batch of
+// the same channel (0 = end of the chain; batch 0 is a sentinel).
+struct alignas(16) DevBatch {
+  uint32_t next_jump;
+  uint32_t offset_base;
+  uint64_t offset_bitset;
+};
+static_assert(sizeof(DevBatch) == 16, "DevBatch must be 16 bytes");
+
+// Head/tail counters of one connector lane, each on its own 128-byte line.
+struct alignas(128) Counter {
+  uint64_t value;
+  uint64_t pad[15];
+};
+struct ConnCounters {
+  Counter tail;  // producer progress, written by the sending lane of prev(r)
+  Counter head;  // consumer progress, written by the receiving lane of r
+};
+static_assert(sizeof(ConnCounters) == 256, "counter layout");
+
+// Per-rank ring position, as setupChannel computes it.
+struct alignas(16) DevRank {
+  int32_t index;  // ring distance from rank 0
+  int32_t prev;
+  int32_t next;
+  int32_t pad;
+};
+
+// Communicator hot fields (copied into LDS by one wave at kernel entry).
+struct alignas(16) DevCommHot {
+  int32_t n_ranks;
+  int32_t n_channels;   // popcount(mask)
+  int32_t n_lanes;      // workgroups per (rank, channel)
+  int32_t proto;
+  int64_t buff_size;    // FIFO bytes per (rank, channel) as requested
+  int64_t step_bytes;   // buff_size / kSteps: one slot of the channel
+  int64_t lane_step_bytes;  // one slot of one lane's own FIFO (>= step_bytes / n_lanes)
+  int64_t lane_buff_bytes;  // kSteps * lane_step_bytes
+  int32_t chunk_steps;  // Simple
+  int32_t step_per_slice;
+  uint64_t channel_mask;
+  uint8_t* fifo;               // lane FIFO of (r, n, p) at ((r * C + n) * P + p) * lane_buff_bytes
+  ConnCounters* counters;      // ((r * C + n) * P + p)
+  uint32_t* abort_flag;        // device word, nonzero = stop
+  uint32_t* abort_host;        // host-mapped word, mirrors abort_flag for the host
+  uint64_t spin_timeout_ticks; // s_memrealtime ticks (100 MHz)
+  int32_t debug_flags;         // bit 0: receivers never publish head (fault test)
+  int32_t pad0;
+};
+static_assert(sizeof(DevCommHot) % 16 == 0, "hot fields are copied in 16-byte packs");
+
+struct alignas(16) DevComm {
+  DevCommHot hot;
+  DevRank ranks[kMaxRanks];
+};
+
+// Kernel arguments (by value).
+struct KernelArgs {
+  const DevComm* comm;
+  const DevBatch* batches;
+  const DevWork* works;
+  void* const* ptrs;            // [(buf_index * N + rank) * 2 + {0 send, 1 recv}]
+  const uint32_t* first_batch;  // [64] first batch of each channel id (0 = none)
+  const uint32_t* wg_map;       // [grid] rank | n << 8 | lane << 16, or kIdleWg
+};
+
+}  // namespace rar

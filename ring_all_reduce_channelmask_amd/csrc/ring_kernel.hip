@@ -1,0 +1,657 @@
+// ring_kernel.hip -- the ring AllReduce device path for gfx950 (MI355X, wave64).
+//
+// One cooperative launch runs every virtual rank.  Workgroup = (rank r, dense
+// channel n, lane p).  The lanes of a channel split every slice (Simple) or
+// step (LL, LL128) into contiguous parts, each with its own head/tail
+// counters, so they run as independent pipelines of identical geometry.
+//
+// Structure follows the two NCCL course pages:
+//   [C23] "NCCL 专家课程 23：Device Kernel、Primitives、Step/Credit 与 LL Flag"
+//   [C12] "NCCL 专家课程 12：Ring AllReduce 逐步推导、真实 Ring 与 Channel 并行"
+// Memory ordering uses HIP's scoped atomics: agent scope (all XCDs of this
+// GPU) is the widest observer set, since every rank lives on this device.
+#include <hip/hip_runtime.h>
+
+#include "rar_device.h"
+
+namespace rar {
+namespace {
+
+enum Op : int { kOpSend = 0, kOpRecvReduceSend, kOpRecvReduceCopySend, kOpRecvCopySend, kOpRecv };
+
+__device__ __forceinline__ int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__device__ __forceinline__ int64_t align_up(int64_t a, int64_t b) { return div_up(a, b) * b; }
+__device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// ---------------------------------------------------------------- ordering
+__device__ __forceinline__ uint64_t load_relaxed(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_relaxed(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void acquire_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void release_fence() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+// Wait until every vector memory operation this wave issued has completed,
+// so that a barrier that follows also covers this wave's payload stores.
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------- arithmetic
+// A 16-byte vector is four 32-bit words; each word holds one fp32 / int32 or
+// two bf16.  bf16 sums are formed in fp32 (exact for the operands' product
+// of two bf16 values' alignment) and rounded to nearest-even bf16 per hop.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;  // quiet NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+struct TyF32 {
+  using S = uint32_t;
+  static __device__ __forceinline__ uint32_t add_word(uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }
+  static __device__ __forceinline__ S add_elem(S a, S b) { return add_word(a, b); }
+};
+struct TyI32 {
+  using S = uint32_t;
+  static __device__ __forceinline__ uint32_t add_word(uint32_t a, uint32_t b) { return a + b; }
+  static __device__ __forceinline__ S add_elem(S a, S b) { return a + b; }
+};
+struct TyBF16 {
+  using S = uint16_t;
+  static __device__ __forceinline__ uint16_t add_elem(uint16_t a, uint16_t b) {
+    return (uint16_t)bf16_rne(__uint_as_float((uint32_t)a << 16) + __uint_as_float((uint32_t)b << 16));
+  }
+  static __device__ __forceinline__ uint32_t add_word(uint32_t a, uint32_t b) {
+    const uint32_t lo = bf16_rne(__uint_as_float(a << 16) + __uint_as_float(b << 16));
+    const uint32_t hi = bf16_rne(__uint_as_float(a & 0xffff0000u) + __uint_as_float(b & 0xffff0000u));
+    return lo | (hi << 16);
+  }
+};
+
+template <class Ty>
+__device__ __forceinline__ uint4 add16(uint4 a, uint4 b) {
+  return make_uint4(Ty::add_word(a.x, b.x), Ty::add_word(a.y, b.y), Ty::add_word(a.z, b.z),
+                    Ty::add_word(a.w, b.w));
+}
+template <class Ty>
+__device__ __forceinline__ uint64_t add8(uint64_t a, uint64_t b) {
+  return (uint64_t)Ty::add_word((uint32_t)a, (uint32_t)b) |
+         ((uint64_t)Ty::add_word((uint32_t)(a >> 32), (uint32_t)(b >> 32)) << 32);
+}
+
+template <int OP> struct OpTraits {
+  static constexpr bool kRecv = OP != kOpSend;
+  static constexpr bool kSend = OP != kOpRecv;
+  static constexpr bool kSrc = OP == kOpSend || OP == kOpRecvReduceSend || OP == kOpRecvReduceCopySend;
+  static constexpr bool kDst = OP == kOpRecvReduceCopySend || OP == kOpRecvCopySend || OP == kOpRecv;
+};
+
+// ---------------------------------------------------------------- LDS state
+struct alignas(16) Shmem {
+  DevCommHot comm;
+  DevBatch batch;
+  DevWork works[kBatchWorks];
+  int32_t slot_bit[kBatchWorks];
+  int32_t channel_id;
+  int32_t n_works;
+  int32_t abort;
+  int32_t pad;
+};
+
+// Per-thread view of the workgroup's channel (values are uniform).
+struct Ctx {
+  Shmem* sh;
+  void* const* ptrs;
+  int tid, nthreads, workers;
+  int rank, nranks, ring_index, lane, nlanes, sps;
+  int64_t step_bytes;       // channel slot: sets the slice geometry
+  int64_t lane_step_bytes;  // this lane's slot in its own FIFO
+  uint8_t* recv_fifo;
+  uint8_t* send_fifo;
+  uint64_t* recv_tail;
+  uint64_t* recv_head;
+  uint64_t* send_tail;
+  uint64_t* send_head;
+  uint64_t recv_step, send_step;
+  uint32_t* abort_flag;
+  uint32_t* abort_host;
+  uint64_t timeout;
+  bool drop_head;  // fault test: never publish head credit
+  bool aborted;
+};
+
+// ---------------------------------------------------------------- waits
+// Every wait is bounded [C23 "Simple 的 Credit 与 Step": the wait loop checks
+// abort]: after `timeout` ticks of the 100 MHz clock the waiter raises the
+// communicator's abort word and every other waiter leaves on seeing it.
+__device__ void raise_abort(Ctx& cx) {
+  __hip_atomic_store(cx.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(cx.abort_host, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+__device__ __forceinline__ bool should_stop(Ctx& cx, uint64_t t0) {
+  if (__hip_atomic_load(cx.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return true;
+  if (__builtin_amdgcn_s_memrealtime() - t0 > cx.timeout) {
+    raise_abort(cx);
+    return true;
+  }
+  return false;
+}
+
+// Spin until *p >= want (relaxed reads; the caller issues the acquire fence).
+__device__ bool wait_geq(const uint64_t* p, uint64_t want, Ctx& cx) {
+  if (load_relaxed(p) >= want) return true;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (uint32_t it = 1;; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    if (load_relaxed(p) >= want) return true;
+    if ((it & 31u) == 0 && should_stop(cx, t0)) return false;
+  }
+}
+
+// Sender credit [C23 "Simple 的 Credit 与 Step"]: head + NCCL_STEPS >= step + n.
+__device__ __forceinline__ bool wait_credit(Ctx& cx, uint64_t n) {
+  const uint64_t need = cx.send_step + n;
+  return need <= (uint64_t)kSteps ? true : wait_geq(cx.send_head, need - kSteps, cx);
+}
+
+// ---------------------------------------------------------------- Simple
+// reduceCopy over n elements with 16-byte vectors, four in flight per thread.
+template <class Ty, bool kRecv, bool kSrc, bool kDst, bool kSend>
+__device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typename Ty::S* src,
+                                            typename Ty::S* dst, typename Ty::S* fout, int64_t n,
+                                            int tid, int nthr) {
+  using S = typename Ty::S;
+  constexpr int kVec = 16 / sizeof(S);
+  constexpr int kUnroll = 4;
+  const int64_t nv = n / kVec;
+  const uint4* vin = reinterpret_cast<const uint4*>(fin);
+  const uint4* vsrc = reinterpret_cast<const uint4*>(src);
+  uint4* vdst = reinterpret_cast<uint4*>(dst);
+  uint4* vout = reinterpret_cast<uint4*>(fout);
+  int64_t i = tid;
+  for (; i + (int64_t)(kUnroll - 1) * nthr < nv; i += (int64_t)kUnroll * nthr) {
+    uint4 a[kUnroll], b[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (kRecv) a[u] = vin[i + (int64_t)u * nthr];
+      if (kSrc) b[u] = vsrc[i + (int64_t)u * nthr];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint4 r = (kRecv && kSrc) ? add16<Ty>(a[u], b[u]) : (kRecv ? a[u] : b[u]);
+      if (kDst) vdst[i + (int64_t)u * nthr] = r;
+      if (kSend) vout[i + (int64_t)u * nthr] = r;
+    }
+  }
+  for (; i < nv; i += nthr) {
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (kRecv) a = vin[i];
+    if (kSrc) b = vsrc[i];
+    const uint4 r = (kRecv && kSrc) ? add16<Ty>(a, b) : (kRecv ? a : b);
+    if (kDst) vdst[i] = r;
+    if (kSend) vout[i] = r;
+  }
+  for (int64_t e = nv * kVec + tid; e < n; e += nthr) {
+    S a = 0, b = 0;
+    if (kRecv) a = fin[e];
+    if (kSrc) b = src[e];
+    const S r = (kRecv && kSrc) ? Ty::add_elem(a, b) : (kRecv ? a : b);
+    if (kDst) dst[e] = r;
+    if (kSend) fout[e] = r;
+  }
+}
+
+// One Simple primitive call: SlicePerChunk slices; each slice waits (role
+// threads of wave 0), moves data (all workers), then publishes (role thread
+// of the last wave) [C23 "Primitive API 是模板组合", "Simple 的线程角色",
+// "发布顺序与 Fence", "Slice Size"].  Empty slices still wait and post.
+template <class Ty, int OP>
+__device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem) {
+  using S = typename Ty::S;
+  using O = OpTraits<OP>;
+  constexpr int kVec = 16 / sizeof(S);
+  const int sps = cx.sps;
+  const int64_t step_elems = cx.step_bytes / (int64_t)sizeof(S);
+  int64_t slice = div_up(nelem, 16 * kSlicesPerChunk) * 16;
+  const int64_t floor_slice = step_elems * sps / 32;
+  if (slice < floor_slice) slice = floor_slice;
+  for (int s = 0; s < kSlicesPerChunk; ++s) {
+    const int64_t s_off = (int64_t)s * slice;
+    const int64_t s_n = clamp64(nelem - s_off, 0, slice);
+    // this lane's part of the slice, in whole 16-byte vectors
+    const int64_t part = kVec * div_up(div_up(s_n, kVec), cx.nlanes);
+    const int64_t lo = clamp64((int64_t)cx.lane * part, 0, s_n);
+    const int64_t hi = clamp64(lo + part, 0, s_n);
+    // wait roles (lanes 0 and 1 of wave 0): the receiver needs
+    // tail >= step + StepPerSlice, the sender head + NCCL_STEPS >= step + StepPerSlice
+    if (cx.tid < 2) {
+      bool ok = true;
+      if (cx.tid == 0 && O::kRecv) ok = wait_geq(cx.recv_tail, cx.recv_step + sps, cx);
+      if (cx.tid == 1 && O::kSend) ok = wait_credit(cx, sps);
+      acquire_fence();
+      if (!ok) cx.sh->abort = 1;
+    }
+    __syncthreads();
+    if (cx.sh->abort) {
+      cx.aborted = true;
+      return;
+    }
+    if (cx.tid < cx.workers && hi > lo) {
+      const S* fin = reinterpret_cast<const S*>(cx.recv_fifo + (cx.recv_step % kSteps) * cx.lane_step_bytes);
+      S* fout = reinterpret_cast<S*>(cx.send_fifo + (cx.send_step % kSteps) * cx.lane_step_bytes);
+      reduce_copy<Ty, O::kRecv, O::kSrc, O::kDst, O::kSend>(fin, src + s_off + lo, dst + s_off + lo,
+                                                             fout, hi - lo, cx.tid, cx.workers);
+    }
+    drain_vmem();
+    __syncthreads();
+    if (O::kRecv) cx.recv_step += sps;
+    if (O::kSend) cx.send_step += sps;
+    // post roles (the last two lanes, one release fence for both): the
+    // slice's payload stores and FIFO reads happen before tail / head move
+    if (cx.tid >= cx.nthreads - 2) {
+      release_fence();
+      if (cx.tid == cx.nthreads - 2 && O::kRecv && !cx.drop_head) store_relaxed(cx.recv_head, cx.recv_step);
+      if (cx.tid == cx.nthreads - 1 && O::kSend) store_relaxed(cx.send_tail, cx.send_step);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- LL
+// 16-byte line: {data1, flag1, data2, flag2}, flags = step+1 [C23 "LL：Data
+// 与 Flag 同 Line"].  Each half is one 64-bit atomic access, so a half whose
+// flag matches carries that step's data.
+__device__ __forceinline__ bool ll_read(const uint64_t* line, uint32_t flag, uint64_t* out, Ctx& cx) {
+  uint64_t a = load_relaxed(line), b = load_relaxed(line + 1);
+  if ((uint32_t)(a >> 32) != flag || (uint32_t)(b >> 32) != flag) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (uint32_t it = 1;; ++it) {
+      a = load_relaxed(line);
+      b = load_relaxed(line + 1);
+      if ((uint32_t)(a >> 32) == flag && (uint32_t)(b >> 32) == flag) break;
+      if ((it & 63u) == 0 && should_stop(cx, t0)) return false;
+    }
+  }
+  *out = (a & 0xffffffffull) | (b << 32);
+  return true;
+}
+
+template <class S>
+__device__ __forceinline__ uint64_t load_bytes8(const uint8_t* p, int64_t valid) {
+  if (valid >= 8) return *reinterpret_cast<const uint64_t*>(p);
+  uint64_t v = 0;
+  for (int64_t b = 0; b < valid; b += sizeof(S))
+    v |= (uint64_t)(*reinterpret_cast<const S*>(p + b)) << (8 * b);
+  return v;
+}
+template <class S>
+__device__ __forceinline__ void store_bytes8(uint8_t* p, uint64_t v, int64_t valid) {
+  if (valid >= 8) {
+    *reinterpret_cast<uint64_t*>(p) = v;
+    return;
+  }
+  for (int64_t b = 0; b < valid; b += sizeof(S)) *reinterpret_cast<S*>(p + b) = (S)(v >> (8 * b));
+}
+
+template <class Ty, int OP>
+__device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem) {
+  using S = typename Ty::S;
+  using O = OpTraits<OP>;
+  const int64_t nbytes = nelem * (int64_t)sizeof(S);
+  const int64_t nlines = div_up(nbytes, 8);
+  const int64_t part = div_up(nlines, cx.nlanes);
+  const int64_t lo = clamp64((int64_t)cx.lane * part, 0, nlines);
+  const int64_t hi = clamp64(lo + part, 0, nlines);
+  if (O::kSend && cx.tid == 0) {
+    const bool ok = wait_credit(cx, 1);
+    acquire_fence();
+    if (!ok) cx.sh->abort = 1;
+  }
+  __syncthreads();
+  if (cx.sh->abort) {
+    cx.aborted = true;
+    return;
+  }
+  const uint32_t rflag = (uint32_t)(cx.recv_step + 1), sflag = (uint32_t)(cx.send_step + 1);
+  // line j of the step sits at line j - lo of this lane's slot
+  const uint64_t* rl = reinterpret_cast<const uint64_t*>(cx.recv_fifo + (cx.recv_step % kSteps) * cx.lane_step_bytes) - 2 * lo;
+  uint64_t* sl = reinterpret_cast<uint64_t*>(cx.send_fifo + (cx.send_step % kSteps) * cx.lane_step_bytes) - 2 * lo;
+  const uint8_t* sb = reinterpret_cast<const uint8_t*>(src);
+  uint8_t* db = reinterpret_cast<uint8_t*>(dst);
+  if (cx.tid < cx.workers) {
+    for (int64_t j = lo + cx.tid; j < hi; j += cx.workers) {
+      uint64_t in = 0;
+      if (O::kRecv && !ll_read(rl + 2 * j, rflag, &in, cx)) {
+        cx.sh->abort = 1;
+        break;
+      }
+      const int64_t valid = nbytes - 8 * j;
+      uint64_t own = 0;
+      if (O::kSrc) own = load_bytes8<S>(sb + 8 * j, valid);
+      const uint64_t v = (O::kRecv && O::kSrc) ? add8<Ty>(in, own) : (O::kRecv ? in : own);
+      if (O::kDst) store_bytes8<S>(db + 8 * j, v, valid);
+      if (O::kSend) {
+        store_relaxed(sl + 2 * j, (v & 0xffffffffull) | ((uint64_t)sflag << 32));
+        store_relaxed(sl + 2 * j + 1, (v >> 32) | ((uint64_t)sflag << 32));
+      }
+    }
+  }
+  drain_vmem();
+  __syncthreads();
+  if (cx.sh->abort) {
+    cx.aborted = true;
+    return;
+  }
+  if (O::kRecv) cx.recv_step += 1;
+  if (O::kSend) cx.send_step += 1;
+  if (O::kRecv && cx.tid == cx.nthreads - 1 && !cx.drop_head) {
+    release_fence();
+    store_relaxed(cx.recv_head, cx.recv_step);
+  }
+}
+
+// ---------------------------------------------------------------- LL128
+// 128-byte line = 16 words: words 0..14 payload, word 15 = step+1 [C23
+// "LL128：15/16 Payload"].  A wave covers 8 lines per pass, 8 lanes per line,
+// 16 bytes per lane; lane 7 of each line holds word 14 and the flag word.
+// The sender stores the data words of all its lines, then one release fence,
+// then the flags; the receiver's flag lanes poll, the wave votes (reload
+// until no lane still waits), then an acquire fence precedes the data loads.
+template <class S>
+__device__ __forceinline__ uint4 load_bytes16(const uint8_t* p, int64_t valid, int64_t cap) {
+  // 8-byte aligned source; `cap` = 16 or 8 bytes owned by the lane
+  uint64_t lo = 0, hi = 0;
+  if (valid > 0) lo = load_bytes8<S>(p, valid);
+  if (cap > 8 && valid > 8) hi = load_bytes8<S>(p + 8, valid - 8);
+  return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+}
+template <class S>
+__device__ __forceinline__ void store_bytes16(uint8_t* p, uint4 v, int64_t valid, int64_t cap) {
+  if (valid > 0) store_bytes8<S>(p, (uint64_t)v.x | ((uint64_t)v.y << 32), valid);
+  if (cap > 8 && valid > 8) store_bytes8<S>(p + 8, (uint64_t)v.z | ((uint64_t)v.w << 32), valid - 8);
+}
+
+template <class Ty, int OP>
+__device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem) {
+  using S = typename Ty::S;
+  using O = OpTraits<OP>;
+  const int64_t nbytes = nelem * (int64_t)sizeof(S);
+  const int64_t nlines = div_up(nbytes, 120);
+  const int64_t part = div_up(nlines, cx.nlanes);
+  const int64_t lo = clamp64((int64_t)cx.lane * part, 0, nlines);
+  const int64_t hi = clamp64(lo + part, 0, nlines);
+  if (O::kSend && cx.tid == 0) {
+    const bool ok = wait_credit(cx, 1);
+    acquire_fence();
+    if (!ok) cx.sh->abort = 1;
+  }
+  __syncthreads();
+  if (cx.sh->abort) {
+    cx.aborted = true;
+    return;
+  }
+  const uint64_t rflag = cx.recv_step + 1, sflag = cx.send_step + 1;
+  // line j of the step sits at line j - lo of this lane's slot
+  const uint64_t* rl = reinterpret_cast<const uint64_t*>(cx.recv_fifo + (cx.recv_step % kSteps) * cx.lane_step_bytes) - 16 * lo;
+  uint64_t* sl = reinterpret_cast<uint64_t*>(cx.send_fifo + (cx.send_step % kSteps) * cx.lane_step_bytes) - 16 * lo;
+  const uint8_t* sb = reinterpret_cast<const uint8_t*>(src);
+  uint8_t* db = reinterpret_cast<uint8_t*>(dst);
+  const int wave = cx.tid >> 6, lid = cx.tid & 63, nw = cx.workers >> 6;
+  const int sub = lid >> 3;  // line within the wave's group of 8
+  const int k = lid & 7;     // 16-byte segment of the line
+  const int64_t cap = k < 7 ? 16 : 8;
+  bool stop = false;
+  if (wave < nw) {
+    for (int64_t g = lo + (int64_t)wave * 8; g < hi; g += (int64_t)nw * 8) {
+      const int64_t j = g + sub;
+      const bool have = j < hi;
+      uint4 in = make_uint4(0, 0, 0, 0);
+      if (O::kRecv) {
+        bool wait = have && k == 7 && load_relaxed(rl + 16 * j + 15) != rflag;
+        if (__any(wait)) {
+          const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+          for (uint32_t it = 1;; ++it) {
+            wait = have && k == 7 && load_relaxed(rl + 16 * j + 15) != rflag;
+            if (!__any(wait)) break;
+            if ((it & 63u) == 0 && should_stop(cx, t0)) {
+              stop = true;
+              break;
+            }
+          }
+          if (stop) break;
+        }
+        acquire_fence();
+        if (have) {
+          const uint64_t* w = rl + 16 * j + 2 * k;
+          const uint64_t w0 = w[0];
+          const uint64_t w1 = k < 7 ? w[1] : 0;
+          in = make_uint4((uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32));
+        }
+      }
+      const int64_t b0 = 120 * j + 16 * k;
+      const int64_t valid = nbytes - b0;
+      uint4 own = make_uint4(0, 0, 0, 0);
+      if (O::kSrc && have) own = load_bytes16<S>(sb + b0, valid, cap);
+      const uint4 v = (O::kRecv && O::kSrc) ? add16<Ty>(in, own) : (O::kRecv ? in : own);
+      if (O::kDst && have) store_bytes16<S>(db + b0, v, valid, cap);
+      if (O::kSend && have) {
+        uint64_t* w = sl + 16 * j + 2 * k;
+        w[0] = (uint64_t)v.x | ((uint64_t)v.y << 32);
+        if (k < 7) w[1] = (uint64_t)v.z | ((uint64_t)v.w << 32);
+      }
+    }
+    if (O::kSend && !stop) {
+      release_fence();
+      for (int64_t g = lo + (int64_t)wave * 8; g < hi; g += (int64_t)nw * 8) {
+        const int64_t j = g + sub;
+        if (j < hi && k == 7) store_relaxed(sl + 16 * j + 15, sflag);
+      }
+    }
+  }
+  if (stop) cx.sh->abort = 1;
+  drain_vmem();
+  __syncthreads();
+  if (cx.sh->abort) {
+    cx.aborted = true;
+    return;
+  }
+  if (O::kRecv) cx.recv_step += 1;
+  if (O::kSend) cx.send_step += 1;
+  if (O::kRecv && cx.tid == cx.nthreads - 1 && !cx.drop_head) {
+    release_fence();
+    store_relaxed(cx.recv_head, cx.recv_step);
+  }
+}
+
+// ---------------------------------------------------------------- runRing
+template <class Ty, int PROTO, int OP>
+__device__ __forceinline__ void prim(Ctx& cx, const typename Ty::S* sendbuf, typename Ty::S* recvbuf,
+                                     int64_t base, int64_t cc, int64_t rem, int chunk) {
+  const int64_t chunk_off = (int64_t)chunk * cc;
+  const int64_t nelem = clamp64(rem - chunk_off, 0, cc);
+  const int64_t off = base + chunk_off;
+  if (PROTO == kSimple)
+    simple_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem);
+  else if (PROTO == kLL)
+    ll_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem);
+  else
+    ll128_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem);
+}
+
+// runRing [C12 "runRing 的数据切分" and steps one to five; C23 "Ring
+// AllReduce 到 Primitive"]: loops of N chunks; the tail loop shrinks the
+// chunk to alignUp(divUp(rem, N), 16 bytes); per loop the 2N-1 calls with
+// chunk indices in ring-position coordinates.
+template <class Ty, int PROTO>
+__device__ void run_ring(Ctx& cx, const DevWork& w) {
+  using S = typename Ty::S;
+  constexpr int kVec = 16 / sizeof(S);
+  const int N = cx.nranks, ix = cx.ring_index;
+  const S* sendbuf = reinterpret_cast<const S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.rank) * 2]);
+  S* recvbuf = reinterpret_cast<S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.rank) * 2 + 1]);
+  int workers = (int)w.n_waves * kWaveSize;
+  cx.workers = workers < cx.nthreads ? workers : cx.nthreads;
+  const int64_t loop_count = (int64_t)N * w.chunk_count;
+  for (int64_t eo = 0; eo < w.channel_count; eo += loop_count) {
+    const int64_t rem = w.channel_count - eo;
+    const int64_t cc = rem < loop_count ? align_up(div_up(rem, N), kVec) : w.chunk_count;
+    const int64_t base = w.grid_offset + eo;
+    auto mod = [N](int x) { return ((x % N) + N) % N; };
+    prim<Ty, PROTO, kOpSend>(cx, sendbuf, recvbuf, base, cc, rem, mod(ix - 1));
+    for (int j = 2; j < N && !cx.aborted; ++j)
+      prim<Ty, PROTO, kOpRecvReduceSend>(cx, sendbuf, recvbuf, base, cc, rem, mod(ix - j));
+    if (cx.aborted) return;
+    prim<Ty, PROTO, kOpRecvReduceCopySend>(cx, sendbuf, recvbuf, base, cc, rem, ix);
+    for (int j = 1; j < N - 1 && !cx.aborted; ++j)
+      prim<Ty, PROTO, kOpRecvCopySend>(cx, sendbuf, recvbuf, base, cc, rem, mod(ix - j));
+    if (cx.aborted) return;
+    prim<Ty, PROTO, kOpRecv>(cx, sendbuf, recvbuf, base, cc, rem, mod(ix + 1));
+    if (cx.aborted) return;
+  }
+}
+
+// ---------------------------------------------------------------- staging
+// Copy `bytes` (multiple of 16) with one wave in 16-byte packs.
+__device__ __forceinline__ void copy16(void* dst, const void* src, int bytes, int lid) {
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  for (int i = lid; i < bytes / 16; i += kWaveSize) d[i] = s[i];
+}
+
+// Load batch `b` into LDS with one wave [C23 "前两个 Warp 与 Work Loader"]:
+// the k-th set bit of offset_bitset names the k-th work (found through an LDS
+// scratch table), then 64 lanes x 16 bytes move up to 16 works of 64 bytes.
+__device__ void load_batch(Shmem& sh, const KernelArgs& a, uint32_t b, int lid) {
+  const DevBatch hdr = a.batches[b];
+  const uint64_t bits = hdr.offset_bitset;
+  if (lid == 0) {
+    sh.batch = hdr;
+    sh.n_works = __popcll(bits);
+  }
+  if ((bits >> lid) & 1ull) sh.slot_bit[__popcll(bits & ((1ull << lid) - 1ull))] = lid;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int nw = __popcll(bits);
+  const int k = lid >> 2, pack = lid & 3;
+  if (k < nw) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.works + hdr.offset_base + sh.slot_bit[k]) + pack;
+    reinterpret_cast<uint4*>(&sh.works[k])[pack] = *src;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- entry
+template <class Ty, int PROTO>
+__global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
+  __shared__ Shmem sh;
+  const uint32_t m = args.wg_map[blockIdx.x];
+  if (m == kIdleWg) return;
+  const int tid = threadIdx.x, nthreads = blockDim.x;
+  const int wave = tid >> 6, lid = tid & 63, nwaves = nthreads >> 6;
+  const int rank = (int)(m & 0xFFu), n = (int)((m >> 8) & 0xFFu), lane = (int)((m >> 16) & 0xFFu);
+  const DevComm* comm = args.comm;
+  // Block -> channel [C23 "Kernel 如何把 Block 映射到 Channel"]: the lanes of
+  // wave 0 scan the 64 mask bits; the dense index n picks the n-th set bit.
+  if (wave == 0) {
+    if (lid == 0) {
+      sh.channel_id = -1;
+      sh.abort = 0;
+    }
+    const uint64_t mask = comm->hot.channel_mask;
+    if (((mask >> lid) & 1ull) && __popcll(mask & ((1ull << lid) - 1ull)) == n) sh.channel_id = lid;
+  }
+  __syncthreads();
+  if (sh.channel_id < 0) return;  // n beyond popcount(mask): not a channel of this launch
+  // Staging [C23 "前两个 Warp 与 Work Loader"]: wave 0 copies the
+  // communicator hot fields, another wave the channel's first work batch.
+  const uint32_t first = args.first_batch[sh.channel_id];
+  if (wave == 0) copy16(&sh.comm, &comm->hot, (int)sizeof(DevCommHot), lid);
+  const int loader = nwaves > 1 ? 1 : 0;
+  if (wave == loader) {
+    if (first != 0) {
+      load_batch(sh, args, first, lid);
+    } else if (lid == 0) {
+      sh.n_works = 0;
+      sh.batch = DevBatch{0, 0, 0};
+    }
+  }
+  __syncthreads();
+
+  Ctx cx;
+  cx.sh = &sh;
+  cx.ptrs = args.ptrs;
+  cx.tid = tid;
+  cx.nthreads = nthreads;
+  cx.workers = nthreads;
+  cx.rank = rank;
+  cx.nranks = sh.comm.n_ranks;
+  const DevRank me = comm->ranks[rank];
+  cx.ring_index = me.index;
+  cx.lane = lane;
+  cx.nlanes = sh.comm.n_lanes;
+  cx.sps = sh.comm.step_per_slice;
+  cx.step_bytes = sh.comm.step_bytes;
+  cx.lane_step_bytes = sh.comm.lane_step_bytes;
+  const int C = sh.comm.n_channels;
+  // each lane of a connector has its own FIFO of kSteps slots
+  cx.recv_fifo = sh.comm.fifo + (((int64_t)rank * C + n) * cx.nlanes + lane) * sh.comm.lane_buff_bytes;
+  cx.send_fifo = sh.comm.fifo + (((int64_t)me.next * C + n) * cx.nlanes + lane) * sh.comm.lane_buff_bytes;
+  ConnCounters* rc = sh.comm.counters + ((int64_t)rank * C + n) * cx.nlanes + lane;
+  ConnCounters* sc = sh.comm.counters + ((int64_t)me.next * C + n) * cx.nlanes + lane;
+  cx.recv_tail = &rc->tail.value;
+  cx.recv_head = &rc->head.value;
+  cx.send_tail = &sc->tail.value;
+  cx.send_head = &sc->head.value;
+  // Steps persist across launches: this workgroup alone writes its receive
+  // head and its send tail, so they hold where it stopped last time.
+  cx.recv_step = load_relaxed(cx.recv_head);
+  cx.send_step = load_relaxed(cx.send_tail);
+  cx.abort_flag = sh.comm.abort_flag;
+  cx.abort_host = sh.comm.abort_host;
+  cx.timeout = sh.comm.spin_timeout_ticks;
+  cx.drop_head = (sh.comm.debug_flags & 1) != 0;
+  cx.aborted = false;
+
+  // RunWorkBatch [C23 "RunWorkBatch 与 Fused Work"]: the works of a batch run
+  // in order; a change of active waves is fenced by a barrier; next_jump
+  // chains the channel's next batch.
+  uint32_t b = first;
+  while (b != 0) {
+    const int nworks = sh.n_works;
+    for (int w = 0; w < nworks; ++w) {
+      if (w > 0 && sh.works[w].n_waves != sh.works[w - 1].n_waves) __syncthreads();
+      run_ring<Ty, PROTO>(cx, sh.works[w]);
+      if (cx.aborted) break;
+    }
+    if (cx.aborted) break;
+    b = sh.batch.next_jump;
+    __syncthreads();
+    if (b != 0 && wave == loader) load_batch(sh, args, b, lid);
+    __syncthreads();
+  }
+  // LL and LL128 publish no tail while running; record the sender step.
+  if (PROTO != kSimple && tid == 0 && !cx.aborted) store_relaxed(cx.send_tail, cx.send_step);
+}
+
+using KernelFn = void (*)(KernelArgs);
+
+// Kernel table by (dtype, protocol): dtype 0 int32, 1 float32, 2 bfloat16.
+const void* get_kernel(int dtype, int proto) {
+  static const KernelFn table[3][3] = {
+      {ring_allreduce_kernel<TyI32, kLL>, ring_allreduce_kernel<TyI32, kLL128>,
+       ring_allreduce_kernel<TyI32, kSimple>},
+      {ring_allreduce_kernel<TyF32, kLL>, ring_allreduce_kernel<TyF32, kLL128>,
+       ring_allreduce_kernel<TyF32, kSimple>},
+      {ring_allreduce_kernel<TyBF16, kLL>, ring_allreduce_kernel<TyBF16, kLL128>,
+       ring_allreduce_kernel<TyBF16, kSimple>},
+  };
+  if (dtype < 0 || dtype > 2 || proto < 0 || proto > 2) return nullptr;
+  return reinterpret_cast<const void*>(table[dtype][proto]);
+}
+
+}  // namespace rar

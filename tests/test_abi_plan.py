@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI library: it loads, exports every entry point
+that include/rar.h declares, and its host planner agrees with the oracle and
+with the pages' tables.  No GPU needed (no compute call is made)."""
+import itertools
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import ring_all_reduce_channelmask_amd as rar
+from ring_all_reduce_channelmask_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "rar.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:rar_result_t|const char\*)\s+(\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(n for n, _, _ in _lib.SIGNATURES) == names
+
+
+def test_error_strings():
+    lib = _lib.load()
+    for code in range(6):
+        assert lib.rar_get_error_string(code)
+
+
+def test_ring_info_matches_pages_and_oracle():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "ring_tables.json")))
+    for key in ("0-1-2-3", "0-2-3-1"):
+        t = g["ring_index_tables"][key]
+        idx, prv, nxt = rar.ring_info(t["order"])
+        for rank, ix, p, n in t["rows"]:
+            assert (idx[rank], prv[rank], nxt[rank]) == (ix, p, n)
+    rng = np.random.default_rng(1)
+    for N in (2, 3, 5, 8, 13, 64):
+        for _ in range(5):
+            order = [int(x) for x in rng.permutation(N)]
+            assert [list(v) for v in rar.ring_info(order)] == \
+                [list(v) for v in oracle.ring_setup(order)]
+
+
+@pytest.mark.parametrize("order", [[0, 1, 1, 2], [0, 1, 2, 4], [0], [-1, 0]])
+def test_ring_info_rejects(order):
+    with pytest.raises(rar.RarError) as e:
+        rar.ring_info(order)
+    assert e.value.code == _lib.INVALID_ARGUMENT
+
+
+PLAN_CASES = [
+    (4, 0x1, "SIMPLE", 65536, 4, "float32", [1024]),
+    (4, 0xF, "LL", 512 * 1024, 4, "float32", [131072]),
+    (4, 0xFFF, "SIMPLE", 4 << 20, 4, "float32", [16 << 20]),
+    (4, 0xFFF, "LL128", 4915200, 4, "float32", [16 << 20]),
+    (8, 0xFFFF, "SIMPLE", 4 << 20, 4, "bfloat16", [32 << 20]),
+    (8, 0xFFFF, "SIMPLE", 4 << 20, 2, "int32", [32 << 20]),
+    (4, 0b101101010011, "LL", 512 * 1024, 4, "bfloat16", [7168] * 104),
+    (3, 0x5, "LL128", 8 * 2048, 4, "int32", [1, 0, 77, 4099, 3]),
+    (2, 1 << 63, "SIMPLE", 8 * 512, 2, "float32", [0, 5]),
+]
+
+
+@pytest.mark.parametrize("case", PLAN_CASES, ids=[f"{c[2]}-{c[5]}-{len(c[6])}" for c in PLAN_CASES])
+def test_planner_matches_oracle_split(case):
+    N, mask, proto, buff, cs, dt, counts = case
+    ours, cmax = rar.plan_pieces(N, mask, proto, buff, cs, dt, counts)
+    theirs, ocmax = oracle.geometry(N, mask, proto, buff, cs, dt, counts)
+    assert cmax == ocmax
+    assert ours == theirs
+
+
+def test_planner_pages_geometry():
+    """Course 23 "Buffer 到 Chunk 的实测公式" and the LL/LL128 default chunks."""
+    for buff, chunk_bytes in [(65536, 32768), (1 << 20, 512 << 10), (4 << 20, 2 << 20)]:
+        _, cmax = rar.plan_pieces(4, 0xF, "SIMPLE", buff, 4, "float32", [16 << 20])
+        assert cmax * 4 == chunk_bytes
+    _, cmax = rar.plan_pieces(4, 0xF, "LL", 0, 0, "float32", [1])
+    assert cmax * 4 == 32768
+    _, cmax = rar.plan_pieces(4, 0xF, "LL128", 0, 0, "float32", [1])
+    assert cmax * 4 == 576000
+
+
+@pytest.mark.parametrize("args,why", [
+    ((4, 0, "SIMPLE", 65536, 4), "empty mask"),
+    ((4, 1, "SIMPLE", 65536, 8), "chunk of 8 steps deadlocks"),
+    ((4, 1, "SIMPLE", 65536, 3), "odd chunkSteps"),
+    ((4, 1, "SIMPLE", 65536 + 128, 4), "Simple buffer not a multiple of 512"),
+    ((4, 1, "LL", 65536 + 128, 4), "LL buffer not a multiple of 256"),
+    ((4, 1, "LL128", 4915200 + 1024, 4), "LL128 buffer not a multiple of 2048"),
+    ((1, 1, "SIMPLE", 65536, 4), "one rank"),
+    ((65, 1, "SIMPLE", 65536, 4), "too many ranks"),
+])
+def test_planner_rejects(args, why):
+    with pytest.raises(rar.RarError) as e:
+        rar.plan_pieces(*args, "float32", [100])
+    assert e.value.code == _lib.INVALID_ARGUMENT, why
+
+
+def test_comm_create_validates_before_touching_a_device():
+    """Invalid arguments are rejected on the host, before any HIP call."""
+    for kwargs in [dict(nranks=4, ring_order=[0, 1, 2, 2], mask=1),
+                   dict(nranks=4, ring_order=[0, 1, 2, 3], mask=0),
+                   dict(nranks=4, ring_order=[0, 1, 2, 3], mask=1, chunk_steps=8),
+                   dict(nranks=4, ring_order=[0, 1, 2, 3], mask=1, lanes=99),
+                   dict(nranks=4, ring_order=[0, 1, 2, 3], mask=1, waves=9)]:
+        with pytest.raises(rar.RarError) as e:
+            rar.Comm(**kwargs)
+        assert e.value.code == _lib.INVALID_ARGUMENT, kwargs
+
+
+def test_package_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The product path has no fallback: a missing librar.so is an error."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "librar.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()

@@ -1,0 +1,249 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer and floating results must match bit for bit: the kernel follows the
+same ring fold order as the oracle, so max-abs error is 0 by construction and
+any difference is a bug.  Small cases compare against the state-machine
+simulator; full-size workloads compare every element against the oracle's
+closed form (int32: against the plain sum)."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import closed_form as cf
+from ring_all_reduce_channelmask_amd import workloads as wl
+
+from .gpu_util import assert_bits_equal, run_hip
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BUFF = {"SIMPLE": 8 * 1024, "LL": 8 * 512, "LL128": 8 * 2048}
+
+
+def _comm(**kw):
+    import ring_all_reduce_channelmask_amd as rar
+    return rar.Comm(**kw)
+
+
+def _rand(dtype, shape, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    if dtype == "int32":
+        return rng.integers(-2 ** 31, 2 ** 31, size=shape).astype(np.int32)
+    v = (rng.standard_normal(shape) * scale).astype(np.float32)
+    if dtype == "float32":
+        return v
+    return wl._bf16_bits(v.ravel()).reshape(shape)
+
+
+def _check_vs_sim(comm, inputs, dtype, buff, cs, in_place=False, sched=0):
+    got = run_hip(comm, inputs, dtype, in_place=in_place)
+    rc, want, _, _ = oracle.allreduce(inputs, comm.ring_order, comm.mask, comm.proto, buff, cs,
+                                      dtype, sched=sched)
+    assert rc == oracle.OK
+    for w in range(len(inputs)):
+        assert_bits_equal(got[w], want[w], f"work {w}")
+
+
+SMALL = []
+for proto in ("SIMPLE", "LL", "LL128"):
+    for dtype in ("float32", "bfloat16", "int32"):
+        for (N, order, mask, count) in [(2, [1, 0], 0x1, 1), (3, [2, 0, 1], 0x5, 1001),
+                                        (4, [0, 2, 3, 1], 0xF, 65539),
+                                        (8, [0, 3, 1, 6, 2, 7, 5, 4], 0x3, 40000)]:
+            SMALL.append((proto, dtype, N, order, mask, count))
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"{c[0]}-{c[1]}-N{c[2]}-{c[5]}" for c in SMALL])
+def test_small_vs_simulator(case):
+    proto, dtype, N, order, mask, count = case
+    buff = SMALL_BUFF[proto]
+    comm = _comm(nranks=N, ring_order=order, mask=mask, proto=proto, buff_size=buff,
+                 chunk_steps=4 if proto == "SIMPLE" else 0, lanes=2, waves=4)
+    x = _rand(dtype, (N, count), count + N)
+    _check_vs_sim(comm, [x], dtype, buff, 4)
+    comm.close()
+
+
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128"])
+def test_in_place_equals_out_of_place(proto):
+    buff = SMALL_BUFF[proto]
+    comm = _comm(nranks=4, ring_order=[0, 2, 3, 1], mask=0x7, proto=proto, buff_size=buff,
+                 chunk_steps=2 if proto == "SIMPLE" else 0)
+    x = _rand("float32", (4, 30011), 5)
+    _check_vs_sim(comm, [x], "float32", buff, 2, in_place=True)
+    _check_vs_sim(comm, [x], "float32", buff, 2, in_place=False)
+    comm.close()
+
+
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128"])
+def test_lanes_and_waves_do_not_change_bits(proto):
+    """Lanes split slices across workgroups and waves across threads; the
+    result bits must not depend on either."""
+    buff = SMALL_BUFF[proto] * 4
+    x = _rand("bfloat16", (4, 100003), 6)
+    ref = None
+    for lanes, waves in [(1, 1), (1, 8), (3, 2), (4, 4), (8, 8)]:
+        comm = _comm(nranks=4, ring_order=[0, 2, 3, 1], mask=0xA, proto=proto, buff_size=buff,
+                     lanes=lanes, waves=waves)
+        got = run_hip(comm, [x], "bfloat16")[0]
+        comm.close()
+        if ref is None:
+            rc, want, _, _ = oracle.allreduce([x], [0, 2, 3, 1], 0xA, proto, buff, 4, "bfloat16")
+            assert rc == oracle.OK
+            assert_bits_equal(got, want[0], f"lanes {lanes} waves {waves}")
+            ref = got
+        assert_bits_equal(got, ref, f"lanes {lanes} waves {waves}")
+
+
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128"])
+def test_edge_counts(proto):
+    """Empty and tiny inputs: count 0 launches nothing and moves no step;
+    8 elements over 8 ranks leave most chunks empty (empty slices post)."""
+    import torch
+    buff = SMALL_BUFF[proto]
+    comm = _comm(nranks=8, ring_order=list(range(8)), mask=0x3, proto=proto, buff_size=buff)
+    before = comm.query_state()
+    t = [torch.zeros(0, device="cuda") for _ in range(8)]
+    comm.allreduce(t, [torch.zeros(0, device="cuda") for _ in range(8)])
+    torch.cuda.synchronize()
+    assert comm.query_state() == before
+    for count in (1, 3, 8, 17, 64, 129):
+        x = np.random.default_rng(count).integers(-8, 9, size=(8, count)).astype(np.float32)
+        got = run_hip(comm, [x], "float32")[0]
+        for r in range(8):
+            np.testing.assert_array_equal(got[r], x.sum(axis=0))
+    comm.close()
+
+
+def test_subnormal_and_signed_zero_fp32_bf16():
+    """IEEE behaviour without flush-to-zero: subnormal sums and -0.0."""
+    rng = np.random.default_rng(8)
+    f = (rng.standard_normal((4, 4096)) * 2.0 ** -140).astype(np.float32)
+    f[:, :16] = -0.0
+    comm = _comm(nranks=4, ring_order=[0, 1, 2, 3], mask=0x1, proto="SIMPLE",
+                 buff_size=SMALL_BUFF["SIMPLE"])
+    _check_vs_sim(comm, [f], "float32", SMALL_BUFF["SIMPLE"], 4)
+    b = wl._bf16_bits((rng.standard_normal(4 * 4096) * 2.0 ** -128).astype(np.float32))
+    _check_vs_sim(comm, [b.reshape(4, 4096)], "bfloat16", SMALL_BUFF["SIMPLE"], 4)
+    comm.close()
+
+
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128"])
+def test_many_launches_on_one_comm(proto):
+    """Steps persist across launches (monotonic head/tail/flags, no reset):
+    1000 back-to-back collectives of varying size on one communicator, so
+    slots and LL flag generations wrap many times over."""
+    import torch
+    buff = SMALL_BUFF[proto]
+    comm = _comm(nranks=4, ring_order=[0, 2, 3, 1], mask=0x3, proto=proto, buff_size=buff,
+                 lanes=2, waves=2)
+    x = np.random.default_rng(9).integers(-1000, 1000, size=(4, 3001)).astype(np.int32)
+    from .gpu_util import to_device, to_host
+    sends = [to_device(x[r], "int32") for r in range(4)]
+    recvs = [torch.zeros_like(s) for s in sends]
+    sizes = [3001, 1, 2048, 777, 0, 3000]
+    for i in range(1000):
+        n = sizes[i % len(sizes)]
+        comm.allreduce([s[:n] for s in sends], [r[:n] for r in recvs])
+    torch.cuda.synchronize()
+    assert comm.async_error() == 0
+    n = sizes[999 % len(sizes)]
+    for r in range(4):
+        np.testing.assert_array_equal(to_host(recvs[r], "int32")[:n], x[:, :n].sum(axis=0))
+    got = run_hip(comm, [x], "int32")[0]
+    for r in range(4):
+        np.testing.assert_array_equal(got[r], x.sum(axis=0))
+    comm.close()
+
+
+def test_group_fused_and_chained_batches():
+    """Fused works over a sparse mask; 300 works give more than 16 pieces per
+    channel, so batches chain through next_jump."""
+    mask = 0b101101010011
+    comm = _comm(nranks=4, ring_order=[0, 1, 2, 3], mask=mask, proto="LL")
+    xs = [_rand("bfloat16", (4, c), 50 + i) for i, c in enumerate([7168] * 8 + [1, 5, 4096])]
+    _check_vs_sim(comm, xs, "bfloat16", 512 * 1024, 4)
+    xs = [_rand("float32", (4, 100 + 37 * i), 500 + i) for i in range(300)]
+    _check_vs_sim(comm, xs, "float32", 512 * 1024, 4)
+    comm.close()
+
+
+def test_ring_allreduce_one_shot_entry():
+    import ring_all_reduce_channelmask_amd as rar
+    import torch
+    from .gpu_util import to_device, to_host
+    x = _rand("float32", (4, 50000), 12)
+    sends = [to_device(x[r], "float32") for r in range(4)]
+    recvs = [torch.empty_like(s) for s in sends]
+    for _ in range(2):  # second call reuses the cached communicator
+        rar.ring_allreduce(sends, recvs, [0, 2, 3, 1], proto="SIMPLE", nchannels=3,
+                           buff_size=SMALL_BUFF["SIMPLE"], chunk_steps=4)
+    torch.cuda.synchronize()
+    rc, want, _, _ = oracle.allreduce([x], [0, 2, 3, 1], 0x7, "SIMPLE", SMALL_BUFF["SIMPLE"], 4,
+                                      "float32")
+    for r in range(4):
+        assert_bits_equal(to_host(recvs[r], "float32"), want[0][r], f"rank {r}")
+
+
+def test_dropped_head_credit_stalls_after_nccl_steps_and_watchdog_ends_it():
+    """The pages' fault model on the real kernel (Course 23, "状态机故障注入":
+    dropping recv head deadlocks after exactly NCCL_STEPS slots), forced from
+    the host by a test flag.  Every sender lane stops with tail = 8 and head =
+    0, the kernel's bounded waits give up after 2 ms, every workgroup exits,
+    the communicator reports RAR_ABORTED, and a fresh one still works."""
+    import ring_all_reduce_channelmask_amd as rar
+    import torch
+    from ring_all_reduce_channelmask_amd import _lib
+    from .gpu_util import to_device
+    comm = _comm(nranks=4, ring_order=[0, 1, 2, 3], mask=0x3, proto="SIMPLE",
+                 buff_size=SMALL_BUFF["SIMPLE"], lanes=2, waves=2, timeout_us=2000,
+                 debug_flags=1)
+    x = _rand("float32", (4, 1 << 16), 13)
+    sends = [to_device(x[r], "float32") for r in range(4)]
+    recvs = [torch.empty_like(s) for s in sends]
+    comm.allreduce(sends, recvs)
+    torch.cuda.synchronize()
+    assert comm.async_error() == _lib.ABORTED
+    state = comm.query_state()
+    tails, heads = state[0::2], state[1::2]
+    assert len(tails) == 4 * 2 * 2
+    assert set(tails) == {8} and set(heads) == {0}
+    with pytest.raises(rar.RarError) as e:
+        comm.allreduce(sends, recvs)
+    assert e.value.code == _lib.ABORTED
+    comm.close()
+    fresh = _comm(nranks=4, ring_order=[0, 1, 2, 3], mask=0x3, proto="SIMPLE",
+                  buff_size=SMALL_BUFF["SIMPLE"])
+    _check_vs_sim(fresh, [x[:, :5000].copy()], "float32", SMALL_BUFF["SIMPLE"], 4)
+    fresh.close()
+
+
+# ------------------------------------------------------------- full sizes
+BENCH_TUNING = {"simple_64m": dict(lanes=4, waves=8)}
+
+
+@pytest.mark.parametrize("key", list(wl.WORKLOADS))
+def test_workload_full_size(key):
+    """Every workload at its full size; the 64 MiB Simple case in the launch
+    configuration the benchmark times.  Compared element by element with the
+    oracle's closed form (int32 with the plain sum)."""
+    w = wl.WORKLOADS[key]
+    xs = wl.inputs_for(w)
+    tune = BENCH_TUNING.get(key, {})
+    comm = _comm(nranks=w.nranks, ring_order=list(w.ring_order), mask=w.mask, proto=w.proto,
+                 buff_size=w.buff_size, chunk_steps=w.chunk_steps if w.proto == "SIMPLE" else 0,
+                 **tune)
+    got = run_hip(comm, xs, w.dtype)
+    comm.close()
+    want = cf.allreduce(xs, list(w.ring_order), w.mask, w.proto, w.buff_size, w.chunk_steps,
+                        w.dtype)
+    for i in range(len(xs)):
+        if w.dtype == "int32":
+            s = (xs[i].astype(np.int64).sum(axis=0) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+            np.testing.assert_array_equal(want[i], s)
+        for r in range(w.nranks):
+            assert_bits_equal(got[i][r], want[i], f"{key} work {i} rank {r}")
+    if w.dtype != "int32":
+        # max-abs error against the oracle is exactly zero
+        diff = max(float(np.max(np.abs(cf._to_f64(got[i][0], w.dtype) -
+                                       cf._to_f64(want[i], w.dtype)))) for i in range(len(xs)))
+        assert diff == 0.0
