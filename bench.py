@@ -23,7 +23,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # Tuned launch shape per workload (performance only; no result bit depends on it).
-TUNING = {"simple_64m": dict(lanes=4, waves=8)}
+# launch_mode 1 = plain launch: the benchmark owns the device, so the grid
+# (which fits the device at once) is resident without the cooperative-launch
+# guarantee, and consecutive launches are ~20 us closer together.
+TUNING = {"simple_64m": dict(lanes=4, waves=8, launch_mode=1)}
 KERNEL_SRC = os.path.join(ROOT, "ring_all_reduce_channelmask_amd", "csrc", "ring_kernel.hip")
 
 
@@ -81,7 +84,11 @@ def main():
     ap.add_argument("--workload", default="simple_64m")
     ap.add_argument("--lanes", type=int, default=None)
     ap.add_argument("--waves", type=int, default=None)
+    ap.add_argument("--launch-mode", type=int, default=None, choices=[0, 1])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead of the AllReduce, time a plain device copy of MIB MiB "
+                         "(used to calibrate the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the N virtual ranks all live on a single MI355X "
@@ -94,12 +101,33 @@ def main():
     import ring_all_reduce_channelmask_amd as rar
     from ring_all_reduce_channelmask_amd import metrics, workloads
 
+    if args.copy_probe:
+        n = args.copy_probe << 18  # fp32 elements
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(args.warmup):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / args.steps
+        print(json.dumps({"copy_probe_MiB": args.copy_probe, "bytes_read": n * 4,
+                          "bytes_written": n * 4, "ms": round(t * 1e3, 4),
+                          "GBps_read_plus_write": round(2 * n * 4 / t / 1e9, 1)}), flush=True)
+        return
+
     w = workloads.WORKLOADS[args.workload]
     tune = dict(TUNING.get(args.workload, {}))
     if args.lanes is not None:
         tune["lanes"] = args.lanes
     if args.waves is not None:
         tune["waves"] = args.waves
+    if args.launch_mode is not None:
+        tune["launch_mode"] = args.launch_mode
     torch.cuda.set_device(0)
     xs = workloads.inputs_for(w)
     N = w.nranks
@@ -176,6 +204,7 @@ def main():
             "elems_per_rank": sum(w.counts), "collectives_per_step": len(w.counts),
             "lanes_per_channel": shape["lanes"], "waves_per_lane": shape["waves"],
             "grid": shape["grid"], "parallelism": f"{N} virtual ranks on 1 GPU",
+            "launch": "plain" if tune.get("launch_mode", 0) == 1 else "cooperative",
         },
         "algbw_GBps": round(algbw, 3),
         "busbw_GBps": round(busbw, 3),

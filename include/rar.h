@@ -67,10 +67,25 @@ typedef struct {
                             never publish head credit (the pages' "drop recv
                             head" fault), so senders stall after exactly
                             NCCL_STEPS slots and the watchdog ends the launch
-                            with RAR_ABORTED [C23 "状态机故障注入"]        */
+                            with RAR_ABORTED [C23 "状态机故障注入"].  Bit 1:
+                            record a timeline (rar_comm_read_trace)        */
+  int launch_mode;       /* 0: cooperative launch, the runtime guarantees that
+                            every workgroup is resident (or fails the launch).
+                            1: plain launch, shorter gaps between launches; the
+                            grid still fits the device at once (checked), but
+                            residency relies on no other kernel holding CUs;
+                            the watchdog turns starvation into RAR_ABORTED  */
+  int placement;         /* 0: the N ranks of each (channel, lane) pipeline
+                            share one XCD, so their FIFO traffic stays in one
+                            L2 and a slice is published without an L2
+                            write-back (checked on the device every launch;
+                            a pipeline found split falls back to the
+                            agent-scope release).  1: spread the ranks over
+                            different XCDs (every hop crosses L2s)         */
 } rar_tuning_t;
 
 #define RAR_DEBUG_DROP_RECV_HEAD 1
+#define RAR_DEBUG_TRACE 2
 
 /* Create a communicator: the ring, the active channels, the protocol and the
  * FIFOs for every (rank, channel).  Allocates N * popcount(mask) * buffSize
@@ -148,6 +163,23 @@ rar_result_t rar_comm_get_async_error(rar_comm_t comm);
  * end of a launch) and head (consumer step).  `cap` is the number of int64
  * slots available; *written receives the number used. */
 rar_result_t rar_comm_query_state(rar_comm_t comm, int64_t* out, size_t cap, size_t* written);
+
+/* Timeline of the last launch, recorded when tuning.debug_flags has
+ * RAR_DEBUG_TRACE: one record per Simple slice or LL/LL128 step of every
+ * workgroup, at most 4096 per workgroup.  Times are 100 MHz ticks of the
+ * device clock.  Synchronizes the device.  op: 0 send, 1 recvReduceSend,
+ * 2 recvReduceCopySend, 3 recvCopySend, 4 recv [C12 steps one to five]. */
+typedef struct {
+  int32_t rank, channel_id, lane, op;
+  int32_t chunk;         /* ring-position chunk index of the call          */
+  uint32_t nelem;        /* elements of the unit over all lanes            */
+  uint64_t t_begin;      /* start of the unit's wait                       */
+  uint32_t wait_ticks;   /* until the workgroup passed its wait             */
+  uint32_t data_ticks;   /* moving data until the workgroup's last barrier  */
+  uint64_t recv_step;    /* receive step at the start of the unit (low bits)*/
+} rar_trace_rec_t;
+rar_result_t rar_comm_read_trace(rar_comm_t comm, rar_trace_rec_t* out, size_t cap,
+                                 size_t* written);
 
 /* Geometry of a communicator: active channels C, lanes per channel P, waves
  * per lane W, workgroups in the grid G (including idle padding). */

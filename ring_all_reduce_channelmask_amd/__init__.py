@@ -58,7 +58,7 @@ class Comm:
     channel mask and a protocol; owns the FIFOs between ring neighbours."""
 
     def __init__(self, nranks, ring_order, mask, proto="SIMPLE", buff_size=0, chunk_steps=0,
-                 lanes=0, waves=0, timeout_us=0, debug_flags=0):
+                 lanes=0, waves=0, timeout_us=0, debug_flags=0, launch_mode=0, placement=0):
         lib = _lib.load()
         if len(ring_order) != nranks:
             raise ValueError("ring_order must list every rank once")
@@ -67,7 +67,7 @@ class Comm:
         self.mask = mask
         self.proto = proto
         order = (ctypes.c_int * nranks)(*self.ring_order)
-        tune = _lib.Tuning(lanes, waves, timeout_us, debug_flags)
+        tune = _lib.Tuning(lanes, waves, timeout_us, debug_flags, launch_mode, placement)
         h = ctypes.c_void_p()
         _lib.check(lib.rar_comm_create(ctypes.byref(h), nranks, order, mask, _lib.PROTO[proto],
                                        buff_size, chunk_steps, ctypes.byref(tune)))
@@ -110,6 +110,17 @@ class Comm:
         written = ctypes.c_size_t()
         _lib.check(_lib.load().rar_comm_query_state(self._h, out, cap, ctypes.byref(written)))
         return list(out[:written.value])
+
+    def read_trace(self):
+        """Timeline of the last launch (needs debug_flags bit 1): a list of
+        dicts, one per Simple slice or LL/LL128 step of every workgroup."""
+        s = self.shape()
+        cap = s["grid"] * 4096
+        out = (_lib.TraceRec * cap)()
+        written = ctypes.c_size_t()
+        _lib.check(_lib.load().rar_comm_read_trace(self._h, out, cap, ctypes.byref(written)))
+        names = [f for f, _ in _lib.TraceRec._fields_]
+        return [{f: getattr(r, f) for f in names} for r in out[:written.value]]
 
     def close(self):
         if getattr(self, "_h", None):

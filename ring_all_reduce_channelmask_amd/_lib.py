@@ -17,7 +17,16 @@ SUM = 0
 
 class Tuning(ctypes.Structure):
     _fields_ = [("lanes_per_channel", ctypes.c_int), ("waves_per_lane", ctypes.c_int),
-                ("spin_timeout_us", ctypes.c_int), ("debug_flags", ctypes.c_int)]
+                ("spin_timeout_us", ctypes.c_int), ("debug_flags", ctypes.c_int),
+                ("launch_mode", ctypes.c_int), ("placement", ctypes.c_int)]
+
+
+class TraceRec(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("channel_id", ctypes.c_int32),
+                ("lane", ctypes.c_int32), ("op", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("nelem", ctypes.c_uint32), ("t_begin", ctypes.c_uint64),
+                ("wait_ticks", ctypes.c_uint32), ("data_ticks", ctypes.c_uint32),
+                ("recv_step", ctypes.c_uint64)]
 
 
 class Piece(ctypes.Structure):
@@ -53,6 +62,8 @@ SIGNATURES = [
     ("rar_comm_query_state", _c.c_int, [_c.c_void_p, _c.POINTER(_c.c_int64), _c.c_size_t,
                                         _c.POINTER(_c.c_size_t)]),
     ("rar_comm_shape", _c.c_int, [_c.c_void_p, _ip, _ip, _ip, _ip]),
+    ("rar_comm_read_trace", _c.c_int, [_c.c_void_p, _c.POINTER(TraceRec), _c.c_size_t,
+                                       _c.POINTER(_c.c_size_t)]),
     ("rar_ring_info", _c.c_int, [_c.c_int, _ip, _ip, _ip, _ip]),
     ("rar_plan_pieces", _c.c_int, [_c.c_int, _c.c_uint64, _c.c_int, _c.c_size_t, _c.c_int,
                                    _c.c_int, _c.c_int, _c.POINTER(_c.c_size_t),

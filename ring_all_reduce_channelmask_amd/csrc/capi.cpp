@@ -64,6 +64,14 @@ struct rar_comm {
   uint32_t* h_abort = nullptr;
   uint32_t* d_abort_host = nullptr;
   uint32_t* d_wgmap = nullptr;
+  std::vector<uint32_t> wgmap;
+  int launch_mode = 0;
+  int debug_flags = 0;
+  rar::TraceRec* d_trace = nullptr;
+  uint64_t* d_placement = nullptr;
+  uint32_t* d_wg_of = nullptr;
+  uint64_t epoch = 0;
+  uint32_t* d_trace_count = nullptr;
   uint8_t* d_arena = nullptr;
   size_t arena_cap = 0;
   uint8_t* h_stage = nullptr;
@@ -83,6 +91,10 @@ void release(rar_comm* c) {
   if (c->h_stage) (void)hipHostFree(c->h_stage);
   if (c->h_abort) (void)hipHostFree(c->h_abort);
   (void)hipFree(c->d_arena);
+  (void)hipFree(c->d_trace);
+  (void)hipFree(c->d_placement);
+  (void)hipFree(c->d_wg_of);
+  (void)hipFree(c->d_trace_count);
   (void)hipFree(c->d_wgmap);
   (void)hipFree(c->d_abort);
   (void)hipFree(c->d_counters);
@@ -174,10 +186,14 @@ rar_result_t launch(rar_comm* c, const std::vector<QueuedCall>& calls, hipStream
   args.ptrs = reinterpret_cast<void* const*>(c->d_arena + off_ptrs);
   args.first_batch = reinterpret_cast<const uint32_t*>(c->d_arena + off_first);
   args.wg_map = c->d_wgmap;
+  args.epoch = ++c->epoch;
   void* params[] = {&args};
   const void* fn = rar::get_kernel(dtype, c->proto);
   if (!fn) return fail(RAR_INTERNAL_ERROR, "no kernel for this dtype/protocol");
-  RAR_HIP(hipLaunchCooperativeKernel(fn, dim3(c->grid), dim3(c->W * rar::kWaveSize), params, 0, stream));
+  if (c->launch_mode == 0)
+    RAR_HIP(hipLaunchCooperativeKernel(fn, dim3(c->grid), dim3(c->W * rar::kWaveSize), params, 0, stream));
+  else
+    RAR_HIP(hipLaunchKernel(fn, dim3(c->grid), dim3(c->W * rar::kWaveSize), params, 0, stream));
   return RAR_SUCCESS;
 }
 
@@ -256,13 +272,18 @@ rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order,
     return fail(RAR_INVALID_ARGUMENT, err);
   rar::RingInfo ring;
   if (!rar::build_ring(nranks, ring_order, &ring, &err)) return fail(RAR_INVALID_ARGUMENT, err);
-  rar_tuning_t tune{0, 0, 0, 0};
+  rar_tuning_t tune{0, 0, 0, 0, 0, 0};
   if (tuning) tune = *tuning;
   if (tune.lanes_per_channel < 0 || tune.lanes_per_channel > rar::kMaxLanes)
     return fail(RAR_INVALID_ARGUMENT, "lanes_per_channel must be in [0, 16]");
   if (tune.waves_per_lane < 0 || tune.waves_per_lane > rar::kMaxWaves)
     return fail(RAR_INVALID_ARGUMENT, "waves_per_lane must be in [0, 8]");
   if (tune.spin_timeout_us < 0) return fail(RAR_INVALID_ARGUMENT, "spin_timeout_us is negative");
+  if (tune.launch_mode != 0 && tune.launch_mode != 1)
+    return fail(RAR_INVALID_ARGUMENT, "launch_mode must be 0 or 1");
+  if (tune.debug_flags & ~3) return fail(RAR_INVALID_ARGUMENT, "unknown debug_flags bits");
+  if (tune.placement != 0 && tune.placement != 1)
+    return fail(RAR_INVALID_ARGUMENT, "placement must be 0 or 1");
 
   int dev = 0;
   RAR_HIP(hipGetDevice(&dev));
@@ -285,8 +306,11 @@ rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order,
   c->W = tune.waves_per_lane ? tune.waves_per_lane : ((int)proto == rar::kLL ? 4 : 8);
   const uint64_t timeout_us = tune.spin_timeout_us ? (uint64_t)tune.spin_timeout_us : 10000000ull;
   c->timeout_ticks = timeout_us * 100ull;  // s_memrealtime runs at 100 MHz
-  const std::vector<uint32_t> wg = rar::make_wg_map(nranks, c->C, c->P);
+  const std::vector<uint32_t> wg = rar::make_wg_map(nranks, c->C, c->P, tune.placement == 1);
   c->grid = (int)wg.size();
+  c->wgmap = wg;
+  c->launch_mode = tune.launch_mode;
+  c->debug_flags = tune.debug_flags;
 
   // every workgroup must be resident at once: the ranks wait on each other
   for (int dt = 0; dt < 3; ++dt) {
@@ -319,6 +343,28 @@ rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order,
   if ((r = guard(hipMalloc(&c->d_abort, 256), "hipMalloc(abort)"))) return r;
   if ((r = guard(hipMalloc(&c->d_wgmap, wg.size() * sizeof(uint32_t)), "hipMalloc(wgmap)"))) return r;
   if ((r = guard(hipMalloc(&c->d_comm, sizeof(rar::DevComm)), "hipMalloc(comm)"))) return r;
+  std::vector<uint32_t> wg_of((size_t)nranks * c->C * c->P, 0);
+  for (size_t g = 0; g < wg.size(); ++g)
+    if (wg[g] != rar::kIdleWg) {
+      const uint32_t m = wg[g];
+      wg_of[((size_t)(m & 0xFF) * c->C + ((m >> 8) & 0xFF)) * c->P + ((m >> 16) & 0xFF)] = (uint32_t)g;
+    }
+  if ((r = guard(hipMalloc(&c->d_placement, wg.size() * sizeof(uint64_t)), "hipMalloc(placement)"))) return r;
+  if ((r = guard(hipMemset(c->d_placement, 0, wg.size() * sizeof(uint64_t)), "hipMemset(placement)"))) return r;
+  if ((r = guard(hipMalloc(&c->d_wg_of, wg_of.size() * sizeof(uint32_t)), "hipMalloc(wg_of)"))) return r;
+  if ((r = guard(hipMemcpy(c->d_wg_of, wg_of.data(), wg_of.size() * sizeof(uint32_t), hipMemcpyHostToDevice),
+                 "hipMemcpy(wg_of)")))
+    return r;
+  constexpr int kTraceCap = 4096;
+  if (tune.debug_flags & 2) {
+    if ((r = guard(hipMalloc(&c->d_trace, (size_t)c->grid * kTraceCap * sizeof(rar::TraceRec)),
+                   "hipMalloc(trace)")))
+      return r;
+    if ((r = guard(hipMalloc(&c->d_trace_count, (size_t)c->grid * sizeof(uint32_t)), "hipMalloc(trace count)")))
+      return r;
+    if ((r = guard(hipMemset(c->d_trace_count, 0, (size_t)c->grid * sizeof(uint32_t)), "hipMemset(trace)")))
+      return r;
+  }
   if ((r = guard(hipHostMalloc(reinterpret_cast<void**>(&c->h_abort), 256, hipHostMallocMapped),
                  "hipHostMalloc(abort)")))
     return r;
@@ -353,6 +399,11 @@ rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order,
   hc.hot.abort_host = c->d_abort_host;
   hc.hot.spin_timeout_ticks = c->timeout_ticks;
   hc.hot.debug_flags = tune.debug_flags;
+  hc.hot.trace_cap = (tune.debug_flags & 2) ? kTraceCap : 0;
+  hc.hot.trace = c->d_trace;
+  hc.hot.trace_count = c->d_trace_count;
+  hc.hot.placement = c->d_placement;
+  hc.hot.wg_of = c->d_wg_of;
   for (int i = 0; i < nranks; ++i) {
     hc.ranks[i].index = ring.index[i];
     hc.ranks[i].prev = ring.prev[i];
@@ -471,6 +522,45 @@ rar_result_t rar_comm_query_state(rar_comm_t c, int64_t* out, size_t cap, size_t
   for (size_t i = 0; i < lanes && k + 2 <= cap; ++i) {
     out[k++] = (int64_t)h[i].tail.value;
     out[k++] = (int64_t)h[i].head.value;
+  }
+  *written = k;
+  return RAR_SUCCESS;
+}
+
+rar_result_t rar_comm_read_trace(rar_comm_t c, rar_trace_rec_t* out, size_t cap, size_t* written) {
+  g_last_error.clear();
+  if (!c || !written || (cap && !out)) return fail(RAR_INVALID_ARGUMENT, "NULL argument");
+  *written = 0;
+  if (!(c->debug_flags & 2)) return fail(RAR_INVALID_ARGUMENT, "communicator created without tracing");
+  RAR_HIP(hipDeviceSynchronize());
+  std::vector<uint32_t> counts(c->grid);
+  RAR_HIP(hipMemcpy(counts.data(), c->d_trace_count, counts.size() * sizeof(uint32_t), hipMemcpyDeviceToHost));
+  std::vector<int> ids;
+  for (int b = 0; b < rar::kMaxChannels; ++b)
+    if ((c->mask >> b) & 1ull) ids.push_back(b);
+  const int cap_per_wg = 4096;
+  std::vector<rar::TraceRec> buf;
+  size_t k = 0;
+  for (int g = 0; g < c->grid && k < cap; ++g) {
+    const uint32_t m = c->wgmap[g];
+    if (m == rar::kIdleWg || counts[g] == 0) continue;
+    const uint32_t n_rec = std::min<uint32_t>(counts[g], cap_per_wg);
+    buf.resize(n_rec);
+    RAR_HIP(hipMemcpy(buf.data(), c->d_trace + (size_t)g * cap_per_wg, n_rec * sizeof(rar::TraceRec),
+                      hipMemcpyDeviceToHost));
+    for (uint32_t i = 0; i < n_rec && k < cap; ++i, ++k) {
+      rar_trace_rec_t& o = out[k];
+      o.rank = (int32_t)(m & 0xFF);
+      o.channel_id = ids[(m >> 8) & 0xFF];
+      o.lane = (int32_t)((m >> 16) & 0xFF);
+      o.op = buf[i].op;
+      o.chunk = buf[i].chunk;
+      o.nelem = buf[i].nelem;
+      o.t_begin = buf[i].t_begin;
+      o.wait_ticks = buf[i].wait_ticks;
+      o.data_ticks = buf[i].data_ticks;
+      o.recv_step = buf[i].recv_step;
+    }
   }
   *written = k;
   return RAR_SUCCESS;

@@ -65,7 +65,9 @@ BatchPlan encode_batches(const std::vector<Piece>& pieces, int n_channels, int n
 // Workgroup map: the N ranks of one (channel, lane) pipeline are placed on
 // the same XCD (workgroups are dispatched to the 8 XCDs round robin by
 // blockIdx), so their FIFO traffic stays in one L2.  Idle slots pad the grid.
-std::vector<uint32_t> make_wg_map(int nranks, int n_channels, int n_lanes);
+// With `spread`, the ranks of a pipeline go to different XCDs instead (each
+// connector then crosses L2s; used to test that path).
+std::vector<uint32_t> make_wg_map(int nranks, int n_channels, int n_lanes, bool spread = false);
 
 // Bytes of one slot of one lane's FIFO.  A channel's step is split among its
 // lanes in whole 16-byte vectors (Simple), 16-byte lines (LL) or 128-byte

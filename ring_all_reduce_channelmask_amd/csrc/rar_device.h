@@ -54,6 +54,20 @@ struct ConnCounters {
 };
 static_assert(sizeof(ConnCounters) == 256, "counter layout");
 
+// One traced primitive unit (a Simple slice or an LL/LL128 step), written by
+// thread 0 of a workgroup when tracing is on.  Times are s_memrealtime ticks
+// (100 MHz).
+struct alignas(16) TraceRec {
+  uint64_t t_begin;     // before the unit's wait
+  uint32_t wait_ticks;  // waiting for tail / credit (until the first barrier)
+  uint32_t data_ticks;  // moving data, line polls included, until the last barrier
+  uint32_t recv_step;   // low bits of the receive step at the unit
+  uint16_t op, chunk;
+  uint32_t nelem;       // elements of the unit (all lanes together)
+  uint32_t pad;
+};
+static_assert(sizeof(TraceRec) == 32, "trace record layout");
+
 // Per-rank ring position, as setupChannel computes it.
 struct alignas(16) DevRank {
   int32_t index;  // ring distance from rank 0
@@ -81,7 +95,12 @@ struct alignas(16) DevCommHot {
   uint32_t* abort_host;        // host-mapped word, mirrors abort_flag for the host
   uint64_t spin_timeout_ticks; // s_memrealtime ticks (100 MHz)
   int32_t debug_flags;         // bit 0: receivers never publish head (fault test)
-  int32_t pad0;
+                               // bit 1: record a TraceRec per unit
+  int32_t trace_cap;           // records per workgroup
+  TraceRec* trace;             // [grid][trace_cap]
+  uint32_t* trace_count;       // [grid] records written by the last launch
+  uint64_t* placement;         // [grid] epoch << 8 | XCC id, written at kernel entry
+  const uint32_t* wg_of;       // [(r * C + n) * P + p] -> workgroup index in the grid
 };
 static_assert(sizeof(DevCommHot) % 16 == 0, "hot fields are copied in 16-byte packs");
 
@@ -98,6 +117,7 @@ struct KernelArgs {
   void* const* ptrs;            // [(buf_index * N + rank) * 2 + {0 send, 1 recv}]
   const uint32_t* first_batch;  // [64] first batch of each channel id (0 = none)
   const uint32_t* wg_map;       // [grid] rank | n << 8 | lane << 16, or kIdleWg
+  uint64_t epoch;               // launch counter of the communicator, from 1
 };
 
 }  // namespace rar

@@ -34,6 +34,12 @@ __device__ __forceinline__ void store_relaxed(uint64_t* p, uint64_t v) {
 }
 __device__ __forceinline__ void acquire_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void release_fence() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+// The XCD (and so the L2) this wave runs on.
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xFu;
+}
 // Wait until every vector memory operation this wave issued has completed,
 // so that a barrier that follows also covers this wave's payload stores.
 __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -99,7 +105,7 @@ struct alignas(16) Shmem {
   int32_t channel_id;
   int32_t n_works;
   int32_t abort;
-  int32_t pad;
+  int32_t local_send;
 };
 
 // Per-thread view of the workgroup's channel (values are uniform).
@@ -122,7 +128,33 @@ struct Ctx {
   uint64_t timeout;
   bool drop_head;  // fault test: never publish head credit
   bool aborted;
+  // The receiving workgroup of the send connector shares this workgroup's L2:
+  // payload stores that have completed (vmcnt drained) are already visible to
+  // it, so publishing needs no L2 write-back.
+  bool local_send;
+  // tracing (thread 0 only)
+  TraceRec* trace;
+  uint32_t trace_n, trace_cap;
 };
+
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Thread 0 appends one record when tracing is on (trace != nullptr).
+__device__ __forceinline__ void trace_unit(Ctx& cx, int op, int chunk, int64_t nelem,
+                                           uint64_t step, uint64_t t0, uint64_t t1, uint64_t t2) {
+  if (cx.trace && cx.tid == 0 && cx.trace_n < cx.trace_cap) {
+    TraceRec r;
+    r.t_begin = t0;
+    r.wait_ticks = (uint32_t)(t1 - t0);
+    r.data_ticks = (uint32_t)(t2 - t1);
+    r.recv_step = (uint32_t)step;
+    r.op = (uint16_t)op;
+    r.chunk = (uint16_t)chunk;
+    r.nelem = (uint32_t)nelem;
+    r.pad = 0;
+    cx.trace[cx.trace_n++] = r;
+  }
+}
 
 // ---------------------------------------------------------------- waits
 // Every wait is bounded [C23 "Simple 的 Credit 与 Step": the wait loop checks
@@ -160,41 +192,81 @@ __device__ __forceinline__ bool wait_credit(Ctx& cx, uint64_t n) {
 }
 
 // ---------------------------------------------------------------- Simple
-// reduceCopy over n elements with 16-byte vectors, four in flight per thread.
+// Loads in flight per thread and per source in reduceCopy, and whether the
+// user buffers (each read once, written once) and the FIFO slots are accessed
+// with the non-temporal hint, so that streaming user data does not push the
+// FIFO slots (re-read moments later on the same XCD) out of L2.  Measured on
+// MI355X at 64 MiB x 4 ranks: user-buffer hint on, FIFO hint off, 4 vectors in
+// flight is the fastest of the combinations tried.  Performance only.
+#ifndef RAR_UNROLL
+#define RAR_UNROLL 4
+#endif
+#ifndef RAR_NT_USER
+#define RAR_NT_USER 1
+#endif
+#ifndef RAR_NT_FIFO
+#define RAR_NT_FIFO 0
+#endif
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+template <class Ty>
+__device__ __forceinline__ v4u add16v(v4u a, v4u b) {
+  v4u r;
+  r.x = Ty::add_word(a.x, b.x);
+  r.y = Ty::add_word(a.y, b.y);
+  r.z = Ty::add_word(a.z, b.z);
+  r.w = Ty::add_word(a.w, b.w);
+  return r;
+}
+template <bool kNt>
+__device__ __forceinline__ v4u ld16(const v4u* p) {
+  if constexpr (kNt) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool kNt>
+__device__ __forceinline__ void st16(v4u* p, v4u v) {
+  if constexpr (kNt) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// reduceCopy over n elements with 16-byte vectors, RAR_UNROLL in flight per
+// thread and source; consecutive threads touch consecutive 16-byte vectors.
 template <class Ty, bool kRecv, bool kSrc, bool kDst, bool kSend>
 __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typename Ty::S* src,
                                             typename Ty::S* dst, typename Ty::S* fout, int64_t n,
                                             int tid, int nthr) {
   using S = typename Ty::S;
   constexpr int kVec = 16 / sizeof(S);
-  constexpr int kUnroll = 4;
+  constexpr int kUnroll = RAR_UNROLL;
+  constexpr bool kNu = RAR_NT_USER != 0, kNf = RAR_NT_FIFO != 0;
   const int64_t nv = n / kVec;
-  const uint4* vin = reinterpret_cast<const uint4*>(fin);
-  const uint4* vsrc = reinterpret_cast<const uint4*>(src);
-  uint4* vdst = reinterpret_cast<uint4*>(dst);
-  uint4* vout = reinterpret_cast<uint4*>(fout);
+  const v4u* vin = reinterpret_cast<const v4u*>(fin);
+  const v4u* vsrc = reinterpret_cast<const v4u*>(src);
+  v4u* vdst = reinterpret_cast<v4u*>(dst);
+  v4u* vout = reinterpret_cast<v4u*>(fout);
   int64_t i = tid;
   for (; i + (int64_t)(kUnroll - 1) * nthr < nv; i += (int64_t)kUnroll * nthr) {
-    uint4 a[kUnroll], b[kUnroll];
+    v4u a[kUnroll], b[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (kRecv) a[u] = vin[i + (int64_t)u * nthr];
-      if (kSrc) b[u] = vsrc[i + (int64_t)u * nthr];
+      if (kRecv) a[u] = ld16<kNf>(vin + i + (int64_t)u * nthr);
+      if (kSrc) b[u] = ld16<kNu>(vsrc + i + (int64_t)u * nthr);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint4 r = (kRecv && kSrc) ? add16<Ty>(a[u], b[u]) : (kRecv ? a[u] : b[u]);
-      if (kDst) vdst[i + (int64_t)u * nthr] = r;
-      if (kSend) vout[i + (int64_t)u * nthr] = r;
+      const v4u r = (kRecv && kSrc) ? add16v<Ty>(a[u], b[u]) : (kRecv ? a[u] : b[u]);
+      if (kDst) st16<kNu>(vdst + i + (int64_t)u * nthr, r);
+      if (kSend) st16<kNf>(vout + i + (int64_t)u * nthr, r);
     }
   }
   for (; i < nv; i += nthr) {
-    uint4 a = make_uint4(0, 0, 0, 0), b = a;
-    if (kRecv) a = vin[i];
-    if (kSrc) b = vsrc[i];
-    const uint4 r = (kRecv && kSrc) ? add16<Ty>(a, b) : (kRecv ? a : b);
-    if (kDst) vdst[i] = r;
-    if (kSend) vout[i] = r;
+    v4u a = {0, 0, 0, 0}, b = a;
+    if (kRecv) a = ld16<kNf>(vin + i);
+    if (kSrc) b = ld16<kNu>(vsrc + i);
+    const v4u r = (kRecv && kSrc) ? add16v<Ty>(a, b) : (kRecv ? a : b);
+    if (kDst) st16<kNu>(vdst + i, r);
+    if (kSend) st16<kNf>(vout + i, r);
   }
   for (int64_t e = nv * kVec + tid; e < n; e += nthr) {
     S a = 0, b = 0;
@@ -211,7 +283,8 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
 // of the last wave) [C23 "Primitive API 是模板组合", "Simple 的线程角色",
 // "发布顺序与 Fence", "Slice Size"].  Empty slices still wait and post.
 template <class Ty, int OP>
-__device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem) {
+__device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
+                            int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
   constexpr int kVec = 16 / sizeof(S);
@@ -227,6 +300,8 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
     const int64_t part = kVec * div_up(div_up(s_n, kVec), cx.nlanes);
     const int64_t lo = clamp64((int64_t)cx.lane * part, 0, s_n);
     const int64_t hi = clamp64(lo + part, 0, s_n);
+    const uint64_t t0 = cx.trace ? now_ticks() : 0;
+    const uint64_t step0 = cx.recv_step;
     // wait roles (lanes 0 and 1 of wave 0): the receiver needs
     // tail >= step + StepPerSlice, the sender head + NCCL_STEPS >= step + StepPerSlice
     if (cx.tid < 2) {
@@ -241,6 +316,7 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
       cx.aborted = true;
       return;
     }
+    const uint64_t t1 = cx.trace ? now_ticks() : 0;
     if (cx.tid < cx.workers && hi > lo) {
       const S* fin = reinterpret_cast<const S*>(cx.recv_fifo + (cx.recv_step % kSteps) * cx.lane_step_bytes);
       S* fout = reinterpret_cast<S*>(cx.send_fifo + (cx.send_step % kSteps) * cx.lane_step_bytes);
@@ -249,14 +325,17 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
     }
     drain_vmem();
     __syncthreads();
+    if (cx.trace) trace_unit(cx, OP, chunk, s_n, step0, t0, t1, now_ticks());
     if (O::kRecv) cx.recv_step += sps;
     if (O::kSend) cx.send_step += sps;
-    // post roles (the last two lanes, one release fence for both): the
-    // slice's payload stores and FIFO reads happen before tail / head move
-    if (cx.tid >= cx.nthreads - 2) {
-      release_fence();
-      if (cx.tid == cx.nthreads - 2 && O::kRecv && !cx.drop_head) store_relaxed(cx.recv_head, cx.recv_step);
-      if (cx.tid == cx.nthreads - 1 && O::kSend) store_relaxed(cx.send_tail, cx.send_step);
+    // post roles (the last two lanes).  Every wave drained its memory
+    // operations before the barrier, so the slice's FIFO reads are complete
+    // (head needs nothing more) and its payload stores sit in this XCD's L2;
+    // a receiver on another XCD additionally needs them written back.
+    if (cx.tid == cx.nthreads - 2 && O::kRecv && !cx.drop_head) store_relaxed(cx.recv_head, cx.recv_step);
+    if (cx.tid == cx.nthreads - 1 && O::kSend) {
+      if (!cx.local_send) release_fence();
+      store_relaxed(cx.send_tail, cx.send_step);
     }
   }
 }
@@ -298,7 +377,8 @@ __device__ __forceinline__ void store_bytes8(uint8_t* p, uint64_t v, int64_t val
 }
 
 template <class Ty, int OP>
-__device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem) {
+__device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
+                        int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
   const int64_t nbytes = nelem * (int64_t)sizeof(S);
@@ -306,6 +386,8 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
   const int64_t part = div_up(nlines, cx.nlanes);
   const int64_t lo = clamp64((int64_t)cx.lane * part, 0, nlines);
   const int64_t hi = clamp64(lo + part, 0, nlines);
+  const uint64_t t0 = cx.trace ? now_ticks() : 0;
+  const uint64_t step0 = cx.recv_step;
   if (O::kSend && cx.tid == 0) {
     const bool ok = wait_credit(cx, 1);
     acquire_fence();
@@ -316,6 +398,7 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
     cx.aborted = true;
     return;
   }
+  const uint64_t t1 = cx.trace ? now_ticks() : 0;
   const uint32_t rflag = (uint32_t)(cx.recv_step + 1), sflag = (uint32_t)(cx.send_step + 1);
   // line j of the step sits at line j - lo of this lane's slot
   const uint64_t* rl = reinterpret_cast<const uint64_t*>(cx.recv_fifo + (cx.recv_step % kSteps) * cx.lane_step_bytes) - 2 * lo;
@@ -346,12 +429,11 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
     cx.aborted = true;
     return;
   }
+  if (cx.trace) trace_unit(cx, OP, chunk, nelem, step0, t0, t1, now_ticks());
   if (O::kRecv) cx.recv_step += 1;
   if (O::kSend) cx.send_step += 1;
-  if (O::kRecv && cx.tid == cx.nthreads - 1 && !cx.drop_head) {
-    release_fence();
-    store_relaxed(cx.recv_head, cx.recv_step);
-  }
+  // the step's line reads completed before the barrier: free the slot
+  if (O::kRecv && cx.tid == cx.nthreads - 1 && !cx.drop_head) store_relaxed(cx.recv_head, cx.recv_step);
 }
 
 // ---------------------------------------------------------------- LL128
@@ -376,7 +458,8 @@ __device__ __forceinline__ void store_bytes16(uint8_t* p, uint4 v, int64_t valid
 }
 
 template <class Ty, int OP>
-__device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem) {
+__device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
+                        int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
   const int64_t nbytes = nelem * (int64_t)sizeof(S);
@@ -384,6 +467,8 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
   const int64_t part = div_up(nlines, cx.nlanes);
   const int64_t lo = clamp64((int64_t)cx.lane * part, 0, nlines);
   const int64_t hi = clamp64(lo + part, 0, nlines);
+  const uint64_t t0 = cx.trace ? now_ticks() : 0;
+  const uint64_t step0 = cx.recv_step;
   if (O::kSend && cx.tid == 0) {
     const bool ok = wait_credit(cx, 1);
     acquire_fence();
@@ -394,6 +479,7 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
     cx.aborted = true;
     return;
   }
+  const uint64_t t1 = cx.trace ? now_ticks() : 0;
   const uint64_t rflag = cx.recv_step + 1, sflag = cx.send_step + 1;
   // line j of the step sits at line j - lo of this lane's slot
   const uint64_t* rl = reinterpret_cast<const uint64_t*>(cx.recv_fifo + (cx.recv_step % kSteps) * cx.lane_step_bytes) - 16 * lo;
@@ -445,7 +531,10 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
       }
     }
     if (O::kSend && !stop) {
-      release_fence();
+      // data words before flag words: drained into this L2, and written back
+      // when the receiver runs on another XCD
+      drain_vmem();
+      if (!cx.local_send) release_fence();
       for (int64_t g = lo + (int64_t)wave * 8; g < hi; g += (int64_t)nw * 8) {
         const int64_t j = g + sub;
         if (j < hi && k == 7) store_relaxed(sl + 16 * j + 15, sflag);
@@ -459,12 +548,11 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
     cx.aborted = true;
     return;
   }
+  if (cx.trace) trace_unit(cx, OP, chunk, nelem, step0, t0, t1, now_ticks());
   if (O::kRecv) cx.recv_step += 1;
   if (O::kSend) cx.send_step += 1;
-  if (O::kRecv && cx.tid == cx.nthreads - 1 && !cx.drop_head) {
-    release_fence();
-    store_relaxed(cx.recv_head, cx.recv_step);
-  }
+  // the step's line reads completed before the barrier: free the slot
+  if (O::kRecv && cx.tid == cx.nthreads - 1 && !cx.drop_head) store_relaxed(cx.recv_head, cx.recv_step);
 }
 
 // ---------------------------------------------------------------- runRing
@@ -475,11 +563,11 @@ __device__ __forceinline__ void prim(Ctx& cx, const typename Ty::S* sendbuf, typ
   const int64_t nelem = clamp64(rem - chunk_off, 0, cc);
   const int64_t off = base + chunk_off;
   if (PROTO == kSimple)
-    simple_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem);
+    simple_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem, chunk);
   else if (PROTO == kLL)
-    ll_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem);
+    ll_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem, chunk);
   else
-    ll128_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem);
+    ll128_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem, chunk);
 }
 
 // runRing [C12 "runRing 的数据切分" and steps one to five; C23 "Ring
@@ -616,6 +704,25 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.timeout = sh.comm.spin_timeout_ticks;
   cx.drop_head = (sh.comm.debug_flags & 1) != 0;
   cx.aborted = false;
+  cx.trace = (sh.comm.debug_flags & 2) ? sh.comm.trace + (int64_t)blockIdx.x * sh.comm.trace_cap : nullptr;
+  cx.trace_n = 0;
+  cx.trace_cap = (uint32_t)sh.comm.trace_cap;
+
+  // Placement handshake: publish this workgroup's XCD for this launch, then
+  // learn the XCD of the workgroup that receives from it.  Same XCD = same
+  // L2 = the cheap publication path; anything else takes the agent-scope
+  // release.  The dispatcher is not trusted: the check runs every launch.
+  if (tid == 0) {
+    const uint32_t my_xcc = xcc_id();
+    store_relaxed(&sh.comm.placement[blockIdx.x], (args.epoch << 8) | my_xcc);
+    const uint32_t peer = sh.comm.wg_of[((int64_t)me.next * C + n) * cx.nlanes + lane];
+    const bool ok = wait_geq(&sh.comm.placement[peer], args.epoch << 8, cx);
+    sh.abort = ok ? 0 : 1;
+    sh.local_send = ok && (load_relaxed(&sh.comm.placement[peer]) & 0xFFu) == my_xcc;
+  }
+  __syncthreads();
+  cx.local_send = sh.local_send;
+  if (sh.abort) return;
 
   // RunWorkBatch [C23 "RunWorkBatch 与 Fused Work"]: the works of a batch run
   // in order; a change of active waves is fenced by a barrier; next_jump
@@ -636,6 +743,7 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   }
   // LL and LL128 publish no tail while running; record the sender step.
   if (PROTO != kSimple && tid == 0 && !cx.aborted) store_relaxed(cx.send_tail, cx.send_step);
+  if (cx.trace && tid == 0) sh.comm.trace_count[blockIdx.x] = cx.trace_n;
 }
 
 using KernelFn = void (*)(KernelArgs);

@@ -218,7 +218,9 @@ def test_dropped_head_credit_stalls_after_nccl_steps_and_watchdog_ends_it():
 
 
 # ------------------------------------------------------------- full sizes
-BENCH_TUNING = {"simple_64m": dict(lanes=4, waves=8)}
+def _bench_tuning():
+    import bench  # the launch shapes bench.py times
+    return bench.TUNING
 
 
 @pytest.mark.parametrize("key", list(wl.WORKLOADS))
@@ -228,7 +230,7 @@ def test_workload_full_size(key):
     oracle's closed form (int32 with the plain sum)."""
     w = wl.WORKLOADS[key]
     xs = wl.inputs_for(w)
-    tune = BENCH_TUNING.get(key, {})
+    tune = _bench_tuning().get(key, {})
     comm = _comm(nranks=w.nranks, ring_order=list(w.ring_order), mask=w.mask, proto=w.proto,
                  buff_size=w.buff_size, chunk_steps=w.chunk_steps if w.proto == "SIMPLE" else 0,
                  **tune)
@@ -247,3 +249,17 @@ def test_workload_full_size(key):
         diff = max(float(np.max(np.abs(cf._to_f64(got[i][0], w.dtype) -
                                        cf._to_f64(want[i], w.dtype)))) for i in range(len(xs)))
         assert diff == 0.0
+
+
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128"])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_ranks_spread_over_xcds(proto, dtype):
+    """Placement 1 puts the ranks of every (channel, lane) pipeline on
+    different XCDs, so every hop crosses L2s and the publication must take
+    the agent-scope release; results must not change."""
+    buff = SMALL_BUFF[proto] * 2
+    comm = _comm(nranks=4, ring_order=[0, 2, 3, 1], mask=0xF, proto=proto, buff_size=buff,
+                 lanes=2, waves=4, placement=1)
+    x = _rand(dtype, (4, 120001), 21)
+    _check_vs_sim(comm, [x], dtype, buff, 4)
+    comm.close()
