@@ -26,7 +26,15 @@ sys.path.insert(0, ROOT)
 # launch_mode 1 = plain launch: the benchmark owns the device, so the grid
 # (which fits the device at once) is resident without the cooperative-launch
 # guarantee, and consecutive launches are ~20 us closer together.
-TUNING = {"simple_64m": dict(lanes=4, waves=8, launch_mode=1)}
+TUNING = {
+    "simple_64m": dict(lanes=5, waves=8, launch_mode=1),
+    "ll128_64m": dict(lanes=4, waves=8, launch_mode=1),
+    "bf16_n8": dict(lanes=2, waves=8, launch_mode=1),
+    "int32_n8": dict(lanes=2, waves=8, launch_mode=1),
+    "ll_512k": dict(lanes=16, waves=2, launch_mode=1),
+    "fused_ll": dict(lanes=1, waves=4, launch_mode=1),
+    "simple_4k": dict(lanes=1, waves=4, launch_mode=1),
+}
 KERNEL_SRC = os.path.join(ROOT, "ring_all_reduce_channelmask_amd", "csrc", "ring_kernel.hip")
 
 
@@ -85,6 +93,7 @@ def main():
     ap.add_argument("--lanes", type=int, default=None)
     ap.add_argument("--waves", type=int, default=None)
     ap.add_argument("--launch-mode", type=int, default=None, choices=[0, 1])
+    ap.add_argument("--slices", type=int, default=None, choices=[1, 2, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the AllReduce, time a plain device copy of MIB MiB "
@@ -98,7 +107,10 @@ def main():
     import numpy as np
     import torch
 
+    import ctypes
+
     import ring_all_reduce_channelmask_amd as rar
+    from ring_all_reduce_channelmask_amd import _lib as comm_lib
     from ring_all_reduce_channelmask_amd import metrics, workloads
 
     if args.copy_probe:
@@ -128,6 +140,8 @@ def main():
         tune["waves"] = args.waves
     if args.launch_mode is not None:
         tune["launch_mode"] = args.launch_mode
+    if args.slices is not None:
+        tune["slices_per_chunk"] = args.slices
     torch.cuda.set_device(0)
     xs = workloads.inputs_for(w)
     N = w.nranks
@@ -143,33 +157,43 @@ def main():
                     chunk_steps=w.chunk_steps if w.proto == "SIMPLE" else 0, **tune)
     shape = comm.shape()
 
-    def step():
+    stream = torch.cuda.current_stream()  # the stream every launch goes to
+
+    def step(a=None, b=None):
+        # A group is queued on the host and launched by group_end; the events
+        # bracket the launch only, so host-side queueing is not timed as GPU work.
         if len(xs) == 1:
+            if a is not None:
+                a.record(stream)
             comm.allreduce(sends[0], recvs[0])
         else:
-            with comm.group():
-                for s, r in zip(sends, recvs):
-                    comm.allreduce(s, r)
+            comm_lib.check(comm_lib.load().rar_group_start(comm.handle))
+            for s, r in zip(sends, recvs):
+                comm.allreduce(s, r)
+            if a is not None:
+                a.record(stream)
+            comm_lib.check(comm_lib.load().rar_group_end(comm.handle, ctypes.c_void_p(stream.cuda_stream)))
+        if b is not None:
+            b.record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()  # the stream every launch goes to
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
+        step(a, b)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if comm.async_error() != 0:
         raise RuntimeError("the wait watchdog fired during the timed region")
     per = [a.elapsed_time(b) * 1e-3 for a, b in ev]            # seconds, one launch each
     span = ev[0][0].elapsed_time(ev[-1][1]) * 1e-3
-    t_step = span / args.steps
+    # a fused group's step is its launch; a single collective's step is the
+    # span over back-to-back launches (launch gaps included)
+    t_step = statistics.mean(per) if len(xs) > 1 else span / args.steps
     t_kernel = statistics.mean(per)
     # the N receive buffers must agree (a property of the method, not an oracle)
     for s in recvs:

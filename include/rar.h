@@ -82,6 +82,12 @@ typedef struct {
                             a pipeline found split falls back to the
                             agent-scope release).  1: spread the ranks over
                             different XCDs (every hop crosses L2s)         */
+  int slices_per_chunk;  /* Simple: slices per chunk, 2 (0 = default) or 4
+                            (needs chunk_steps 4).  Each slice still moves
+                            StepPerSlice = chunk_steps / slices FIFO steps
+                            and every call still consumes chunk_steps steps;
+                            smaller slices keep fewer FIFO bytes in flight.
+                            Timing only: results are identical            */
 } rar_tuning_t;
 
 #define RAR_DEBUG_DROP_RECV_HEAD 1

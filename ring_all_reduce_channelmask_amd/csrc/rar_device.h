@@ -10,7 +10,7 @@
 namespace rar {
 
 constexpr int kSteps = 8;            // NCCL_STEPS: FIFO slots per connector
-constexpr int kSlicesPerChunk = 2;   // Simple: slices per chunk (StepPerSlice = chunkSteps/2)
+constexpr int kSlicesPerChunk = 2;   // Simple default: slices per chunk (StepPerSlice = chunkSteps/2)
 constexpr int kMaxRanks = 64;
 constexpr int kMaxChannels = 64;     // channelMask is 64 bits
 constexpr int kMaxLanes = 16;
@@ -87,7 +87,9 @@ struct alignas(16) DevCommHot {
   int64_t lane_step_bytes;  // one slot of one lane's own FIFO (>= step_bytes / n_lanes)
   int64_t lane_buff_bytes;  // kSteps * lane_step_bytes
   int32_t chunk_steps;  // Simple
-  int32_t step_per_slice;
+  int32_t step_per_slice;      // Simple: chunk_steps / slices_per_chunk
+  int32_t slices_per_chunk;    // Simple: 2 (default) or 4; timing only
+  int32_t pad1;
   uint64_t channel_mask;
   uint8_t* fifo;               // lane FIFO of (r, n, p) at ((r * C + n) * P + p) * lane_buff_bytes
   ConnCounters* counters;      // ((r * C + n) * P + p)

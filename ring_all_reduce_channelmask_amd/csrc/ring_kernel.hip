@@ -113,7 +113,7 @@ struct Ctx {
   Shmem* sh;
   void* const* ptrs;
   int tid, nthreads, workers;
-  int rank, nranks, ring_index, lane, nlanes, sps;
+  int rank, nranks, ring_index, lane, nlanes, sps, spc;
   int64_t step_bytes;       // channel slot: sets the slice geometry
   int64_t lane_step_bytes;  // this lane's slot in its own FIFO
   uint8_t* recv_fifo;
@@ -123,6 +123,9 @@ struct Ctx {
   uint64_t* send_tail;
   uint64_t* send_head;
   uint64_t recv_step, send_step;
+  // last values read of the receive tail and the send head (the pages'
+  // connStepCache): a wait that the cached value already satisfies loads nothing
+  uint64_t tail_cache, head_cache;
   uint32_t* abort_flag;
   uint32_t* abort_host;
   uint64_t timeout;
@@ -174,21 +177,31 @@ __device__ __forceinline__ bool should_stop(Ctx& cx, uint64_t t0) {
   return false;
 }
 
-// Spin until *p >= want (relaxed reads; the caller issues the acquire fence).
-__device__ bool wait_geq(const uint64_t* p, uint64_t want, Ctx& cx) {
-  if (load_relaxed(p) >= want) return true;
+// Spin until *p >= want (relaxed reads; the caller issues any acquire fence).
+// `cache` keeps the last value read [C23 "Simple 的 Credit 与 Step": the wait
+// loop reloads connStepCache only while it is short of the desired step].
+__device__ bool wait_cached(const uint64_t* p, uint64_t want, uint64_t& cache, Ctx& cx) {
+  if (cache >= want) return true;
+  cache = load_relaxed(p);
+  if (cache >= want) return true;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (uint32_t it = 1;; ++it) {
     __builtin_amdgcn_s_sleep(1);
-    if (load_relaxed(p) >= want) return true;
+    cache = load_relaxed(p);
+    if (cache >= want) return true;
     if ((it & 31u) == 0 && should_stop(cx, t0)) return false;
   }
+}
+
+__device__ __forceinline__ bool wait_geq(const uint64_t* p, uint64_t want, Ctx& cx) {
+  uint64_t cache = 0;
+  return wait_cached(p, want, cache, cx);
 }
 
 // Sender credit [C23 "Simple 的 Credit 与 Step"]: head + NCCL_STEPS >= step + n.
 __device__ __forceinline__ bool wait_credit(Ctx& cx, uint64_t n) {
   const uint64_t need = cx.send_step + n;
-  return need <= (uint64_t)kSteps ? true : wait_geq(cx.send_head, need - kSteps, cx);
+  return need <= (uint64_t)kSteps ? true : wait_cached(cx.send_head, need - kSteps, cx.head_cache, cx);
 }
 
 // ---------------------------------------------------------------- Simple
@@ -290,10 +303,11 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
   constexpr int kVec = 16 / sizeof(S);
   const int sps = cx.sps;
   const int64_t step_elems = cx.step_bytes / (int64_t)sizeof(S);
-  int64_t slice = div_up(nelem, 16 * kSlicesPerChunk) * 16;
+  const int spc = cx.spc;
+  int64_t slice = div_up(nelem, 16 * spc) * 16;
   const int64_t floor_slice = step_elems * sps / 32;
   if (slice < floor_slice) slice = floor_slice;
-  for (int s = 0; s < kSlicesPerChunk; ++s) {
+  for (int s = 0; s < spc; ++s) {
     const int64_t s_off = (int64_t)s * slice;
     const int64_t s_n = clamp64(nelem - s_off, 0, slice);
     // this lane's part of the slice, in whole 16-byte vectors
@@ -306,7 +320,7 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
     // tail >= step + StepPerSlice, the sender head + NCCL_STEPS >= step + StepPerSlice
     if (cx.tid < 2) {
       bool ok = true;
-      if (cx.tid == 0 && O::kRecv) ok = wait_geq(cx.recv_tail, cx.recv_step + sps, cx);
+      if (cx.tid == 0 && O::kRecv) ok = wait_cached(cx.recv_tail, cx.recv_step + sps, cx.tail_cache, cx);
       if (cx.tid == 1 && O::kSend) ok = wait_credit(cx, sps);
       acquire_fence();
       if (!ok) cx.sh->abort = 1;
@@ -343,20 +357,24 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
 // ---------------------------------------------------------------- LL
 // 16-byte line: {data1, flag1, data2, flag2}, flags = step+1 [C23 "LL：Data
 // 与 Flag 同 Line"].  Each half is one 64-bit atomic access, so a half whose
-// flag matches carries that step's data.
-__device__ __forceinline__ bool ll_read(const uint64_t* line, uint32_t flag, uint64_t* out, Ctx& cx) {
-  uint64_t a = load_relaxed(line), b = load_relaxed(line + 1);
-  if ((uint32_t)(a >> 32) != flag || (uint32_t)(b >> 32) != flag) {
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    for (uint32_t it = 1;; ++it) {
-      a = load_relaxed(line);
-      b = load_relaxed(line + 1);
-      if ((uint32_t)(a >> 32) == flag && (uint32_t)(b >> 32) == flag) break;
-      if ((it & 63u) == 0 && should_stop(cx, t0)) return false;
-    }
+// flag matches carries that step's data and no fence is needed on either
+// side.  Every worker thread checks the sender credit itself (cached, so
+// usually without a load) and keeps kLlUnroll lines in flight.
+constexpr int kLlUnroll = 4;
+
+__device__ __forceinline__ bool ll_ready(uint64_t a, uint64_t b, uint32_t flag) {
+  return (uint32_t)(a >> 32) == flag && (uint32_t)(b >> 32) == flag;
+}
+
+// Reload a line until both flags carry `flag`.
+__device__ bool ll_wait_line(const uint64_t* line, uint32_t flag, uint64_t& a, uint64_t& b, Ctx& cx) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (uint32_t it = 1;; ++it) {
+    a = load_relaxed(line);
+    b = load_relaxed(line + 1);
+    if (ll_ready(a, b, flag)) return true;
+    if ((it & 63u) == 0 && should_stop(cx, t0)) return false;
   }
-  *out = (a & 0xffffffffull) | (b << 32);
-  return true;
 }
 
 template <class S>
@@ -381,6 +399,7 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
                         int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
+  constexpr int U = kLlUnroll;
   const int64_t nbytes = nelem * (int64_t)sizeof(S);
   const int64_t nlines = div_up(nbytes, 8);
   const int64_t part = div_up(nlines, cx.nlanes);
@@ -388,16 +407,9 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
   const int64_t hi = clamp64(lo + part, 0, nlines);
   const uint64_t t0 = cx.trace ? now_ticks() : 0;
   const uint64_t step0 = cx.recv_step;
-  if (O::kSend && cx.tid == 0) {
-    const bool ok = wait_credit(cx, 1);
-    acquire_fence();
-    if (!ok) cx.sh->abort = 1;
-  }
-  __syncthreads();
-  if (cx.sh->abort) {
-    cx.aborted = true;
-    return;
-  }
+  bool ok = true;
+  const bool worker = cx.tid < cx.workers;
+  if (O::kSend && worker && lo < hi) ok = wait_credit(cx, 1);
   const uint64_t t1 = cx.trace ? now_ticks() : 0;
   const uint32_t rflag = (uint32_t)(cx.recv_step + 1), sflag = (uint32_t)(cx.send_step + 1);
   // line j of the step sits at line j - lo of this lane's slot
@@ -405,25 +417,46 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
   uint64_t* sl = reinterpret_cast<uint64_t*>(cx.send_fifo + (cx.send_step % kSteps) * cx.lane_step_bytes) - 2 * lo;
   const uint8_t* sb = reinterpret_cast<const uint8_t*>(src);
   uint8_t* db = reinterpret_cast<uint8_t*>(dst);
-  if (cx.tid < cx.workers) {
-    for (int64_t j = lo + cx.tid; j < hi; j += cx.workers) {
-      uint64_t in = 0;
-      if (O::kRecv && !ll_read(rl + 2 * j, rflag, &in, cx)) {
-        cx.sh->abort = 1;
-        break;
+  if (worker && ok) {
+    const int64_t stride = cx.workers;
+    for (int64_t j0 = lo + cx.tid; j0 < hi && ok; j0 += (int64_t)U * stride) {
+      uint64_t a[U], b[U], own[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = j0 + (int64_t)u * stride;
+        a[u] = b[u] = own[u] = 0;
+        if (j < hi) {
+          if (O::kRecv) {
+            a[u] = load_relaxed(rl + 2 * j);
+            b[u] = load_relaxed(rl + 2 * j + 1);
+          }
+          if (O::kSrc) own[u] = load_bytes8<S>(sb + 8 * j, nbytes - 8 * j);
+        }
       }
-      const int64_t valid = nbytes - 8 * j;
-      uint64_t own = 0;
-      if (O::kSrc) own = load_bytes8<S>(sb + 8 * j, valid);
-      const uint64_t v = (O::kRecv && O::kSrc) ? add8<Ty>(in, own) : (O::kRecv ? in : own);
-      if (O::kDst) store_bytes8<S>(db + 8 * j, v, valid);
-      if (O::kSend) {
-        store_relaxed(sl + 2 * j, (v & 0xffffffffull) | ((uint64_t)sflag << 32));
-        store_relaxed(sl + 2 * j + 1, (v >> 32) | ((uint64_t)sflag << 32));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = j0 + (int64_t)u * stride;
+        if (O::kRecv && j < hi && !ll_ready(a[u], b[u], rflag))
+          ok = ok && ll_wait_line(rl + 2 * j, rflag, a[u], b[u], cx);
+      }
+      if (!ok) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = j0 + (int64_t)u * stride;
+        if (j >= hi) continue;
+        const uint64_t in = (a[u] & 0xffffffffull) | (b[u] << 32);
+        const uint64_t v = (O::kRecv && O::kSrc) ? add8<Ty>(in, own[u]) : (O::kRecv ? in : own[u]);
+        if (O::kDst) store_bytes8<S>(db + 8 * j, v, nbytes - 8 * j);
+        if (O::kSend) {
+          store_relaxed(sl + 2 * j, (v & 0xffffffffull) | ((uint64_t)sflag << 32));
+          store_relaxed(sl + 2 * j + 1, (v >> 32) | ((uint64_t)sflag << 32));
+        }
       }
     }
   }
-  drain_vmem();
+  if (!ok) cx.sh->abort = 1;
+  // Every line value was consumed before this barrier, so every line read of
+  // the step has completed: the slot can be handed back.
   __syncthreads();
   if (cx.sh->abort) {
     cx.aborted = true;
@@ -432,7 +465,6 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
   if (cx.trace) trace_unit(cx, OP, chunk, nelem, step0, t0, t1, now_ticks());
   if (O::kRecv) cx.recv_step += 1;
   if (O::kSend) cx.send_step += 1;
-  // the step's line reads completed before the barrier: free the slot
   if (O::kRecv && cx.tid == cx.nthreads - 1 && !cx.drop_head) store_relaxed(cx.recv_head, cx.recv_step);
 }
 
@@ -440,28 +472,33 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
 // 128-byte line = 16 words: words 0..14 payload, word 15 = step+1 [C23
 // "LL128：15/16 Payload"].  A wave covers 8 lines per pass, 8 lanes per line,
 // 16 bytes per lane; lane 7 of each line holds word 14 and the flag word.
-// The sender stores the data words of all its lines, then one release fence,
-// then the flags; the receiver's flag lanes poll, the wave votes (reload
-// until no lane still waits), then an acquire fence precedes the data loads.
+// Sender: data words of all its lines, a drain (plus an L2 write-back when the
+// receiver is on another XCD), then the flag words.  Receiver: the flag lanes
+// poll every line of the wave, the wave votes until none is missing, then one
+// acquire fence precedes the data loads.
+constexpr int kLl128Unroll = 4;
+
 template <class S>
-__device__ __forceinline__ uint4 load_bytes16(const uint8_t* p, int64_t valid, int64_t cap) {
+__device__ __forceinline__ v4u load_bytes16(const uint8_t* p, int64_t valid, int64_t cap) {
   // 8-byte aligned source; `cap` = 16 or 8 bytes owned by the lane
   uint64_t lo = 0, hi = 0;
   if (valid > 0) lo = load_bytes8<S>(p, valid);
   if (cap > 8 && valid > 8) hi = load_bytes8<S>(p + 8, valid - 8);
-  return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+  v4u r = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+  return r;
 }
 template <class S>
-__device__ __forceinline__ void store_bytes16(uint8_t* p, uint4 v, int64_t valid, int64_t cap) {
+__device__ __forceinline__ void store_bytes16(uint8_t* p, v4u v, int64_t valid, int64_t cap) {
   if (valid > 0) store_bytes8<S>(p, (uint64_t)v.x | ((uint64_t)v.y << 32), valid);
   if (cap > 8 && valid > 8) store_bytes8<S>(p + 8, (uint64_t)v.z | ((uint64_t)v.w << 32), valid - 8);
 }
 
 template <class Ty, int OP>
 __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
-                        int chunk) {
+                           int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
+  constexpr int U = kLl128Unroll;
   const int64_t nbytes = nelem * (int64_t)sizeof(S);
   const int64_t nlines = div_up(nbytes, 120);
   const int64_t part = div_up(nlines, cx.nlanes);
@@ -469,16 +506,14 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
   const int64_t hi = clamp64(lo + part, 0, nlines);
   const uint64_t t0 = cx.trace ? now_ticks() : 0;
   const uint64_t step0 = cx.recv_step;
-  if (O::kSend && cx.tid == 0) {
-    const bool ok = wait_credit(cx, 1);
-    acquire_fence();
-    if (!ok) cx.sh->abort = 1;
-  }
-  __syncthreads();
-  if (cx.sh->abort) {
-    cx.aborted = true;
-    return;
-  }
+  const int wave = cx.tid >> 6, lid = cx.tid & 63, nw = cx.workers >> 6;
+  const int sub = lid >> 3;  // line within the wave's group of 8
+  const int k = lid & 7;     // 16-byte segment of the line
+  const int64_t cap = k < 7 ? 16 : 8;
+  const int64_t first = lo + (int64_t)wave * 8, stride = (int64_t)nw * 8;
+  const bool active = wave < nw && first < hi;
+  bool ok = true;
+  if (O::kSend && active) ok = wait_credit(cx, 1);
   const uint64_t t1 = cx.trace ? now_ticks() : 0;
   const uint64_t rflag = cx.recv_step + 1, sflag = cx.send_step + 1;
   // line j of the step sits at line j - lo of this lane's slot
@@ -486,63 +521,79 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
   uint64_t* sl = reinterpret_cast<uint64_t*>(cx.send_fifo + (cx.send_step % kSteps) * cx.lane_step_bytes) - 16 * lo;
   const uint8_t* sb = reinterpret_cast<const uint8_t*>(src);
   uint8_t* db = reinterpret_cast<uint8_t*>(dst);
-  const int wave = cx.tid >> 6, lid = cx.tid & 63, nw = cx.workers >> 6;
-  const int sub = lid >> 3;  // line within the wave's group of 8
-  const int k = lid & 7;     // 16-byte segment of the line
-  const int64_t cap = k < 7 ? 16 : 8;
-  bool stop = false;
-  if (wave < nw) {
-    for (int64_t g = lo + (int64_t)wave * 8; g < hi; g += (int64_t)nw * 8) {
-      const int64_t j = g + sub;
-      const bool have = j < hi;
-      uint4 in = make_uint4(0, 0, 0, 0);
-      if (O::kRecv) {
-        bool wait = have && k == 7 && load_relaxed(rl + 16 * j + 15) != rflag;
-        if (__any(wait)) {
-          const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-          for (uint32_t it = 1;; ++it) {
-            wait = have && k == 7 && load_relaxed(rl + 16 * j + 15) != rflag;
-            if (!__any(wait)) break;
-            if ((it & 63u) == 0 && should_stop(cx, t0)) {
-              stop = true;
-              break;
+  if (active && ok) {
+    if (O::kRecv) {
+      const uint64_t tp = __builtin_amdgcn_s_memrealtime();
+      for (uint32_t it = 1;; ++it) {
+        bool pending = false;
+        if (k == 7) {
+          for (int64_t g0 = first; g0 < hi; g0 += (int64_t)U * stride) {
+            uint64_t f[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              const int64_t j = g0 + (int64_t)u * stride + sub;
+              f[u] = j < hi ? load_relaxed(rl + 16 * j + 15) : rflag;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) pending = pending || f[u] != rflag;
+          }
+        }
+        if (!__any(pending)) break;
+        if ((it & 15u) == 0 && should_stop(cx, tp)) {
+          ok = false;
+          break;
+        }
+      }
+      if (ok) acquire_fence();
+    }
+    if (ok) {
+      for (int64_t g0 = first; g0 < hi; g0 += (int64_t)U * stride) {
+        v4u in[U], own[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t j = g0 + (int64_t)u * stride + sub;
+          const v4u zero = {0, 0, 0, 0};
+          in[u] = zero;
+          own[u] = zero;
+          if (j < hi) {
+            if (O::kRecv) {
+              in[u] = *reinterpret_cast<const v4u*>(rl + 16 * j + 2 * k);
+              if (k == 7) in[u].z = in[u].w = 0;  // the flag word is not payload
+            }
+            if (O::kSrc) own[u] = load_bytes16<S>(sb + 120 * j + 16 * k, nbytes - (120 * j + 16 * k), cap);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t j = g0 + (int64_t)u * stride + sub;
+          if (j >= hi) continue;
+          const v4u v = (O::kRecv && O::kSrc) ? add16v<Ty>(in[u], own[u]) : (O::kRecv ? in[u] : own[u]);
+          const int64_t b0 = 120 * j + 16 * k;
+          if (O::kDst) store_bytes16<S>(db + b0, v, nbytes - b0, cap);
+          if (O::kSend) {
+            uint64_t* w = sl + 16 * j + 2 * k;
+            if (k < 7) {
+              *reinterpret_cast<v4u*>(w) = v;
+            } else {
+              w[0] = (uint64_t)v.x | ((uint64_t)v.y << 32);
             }
           }
-          if (stop) break;
-        }
-        acquire_fence();
-        if (have) {
-          const uint64_t* w = rl + 16 * j + 2 * k;
-          const uint64_t w0 = w[0];
-          const uint64_t w1 = k < 7 ? w[1] : 0;
-          in = make_uint4((uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32));
         }
       }
-      const int64_t b0 = 120 * j + 16 * k;
-      const int64_t valid = nbytes - b0;
-      uint4 own = make_uint4(0, 0, 0, 0);
-      if (O::kSrc && have) own = load_bytes16<S>(sb + b0, valid, cap);
-      const uint4 v = (O::kRecv && O::kSrc) ? add16<Ty>(in, own) : (O::kRecv ? in : own);
-      if (O::kDst && have) store_bytes16<S>(db + b0, v, valid, cap);
-      if (O::kSend && have) {
-        uint64_t* w = sl + 16 * j + 2 * k;
-        w[0] = (uint64_t)v.x | ((uint64_t)v.y << 32);
-        if (k < 7) w[1] = (uint64_t)v.z | ((uint64_t)v.w << 32);
-      }
-    }
-    if (O::kSend && !stop) {
-      // data words before flag words: drained into this L2, and written back
-      // when the receiver runs on another XCD
-      drain_vmem();
-      if (!cx.local_send) release_fence();
-      for (int64_t g = lo + (int64_t)wave * 8; g < hi; g += (int64_t)nw * 8) {
-        const int64_t j = g + sub;
-        if (j < hi && k == 7) store_relaxed(sl + 16 * j + 15, sflag);
+      if (O::kSend) {
+        // data words before flag words: drained into this L2, and written
+        // back when the receiver runs on another XCD
+        drain_vmem();
+        if (!cx.local_send) release_fence();
+        for (int64_t g = first; g < hi; g += stride) {
+          const int64_t j = g + sub;
+          if (j < hi && k == 7) store_relaxed(sl + 16 * j + 15, sflag);
+        }
       }
     }
   }
-  if (stop) cx.sh->abort = 1;
-  drain_vmem();
+  if (!ok) cx.sh->abort = 1;
+  // every data word of the step was consumed before this barrier
   __syncthreads();
   if (cx.sh->abort) {
     cx.aborted = true;
@@ -551,7 +602,6 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
   if (cx.trace) trace_unit(cx, OP, chunk, nelem, step0, t0, t1, now_ticks());
   if (O::kRecv) cx.recv_step += 1;
   if (O::kSend) cx.send_step += 1;
-  // the step's line reads completed before the barrier: free the slot
   if (O::kRecv && cx.tid == cx.nthreads - 1 && !cx.drop_head) store_relaxed(cx.recv_head, cx.recv_step);
 }
 
@@ -683,6 +733,7 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.lane = lane;
   cx.nlanes = sh.comm.n_lanes;
   cx.sps = sh.comm.step_per_slice;
+  cx.spc = sh.comm.slices_per_chunk;
   cx.step_bytes = sh.comm.step_bytes;
   cx.lane_step_bytes = sh.comm.lane_step_bytes;
   const int C = sh.comm.n_channels;
@@ -699,6 +750,8 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   // head and its send tail, so they hold where it stopped last time.
   cx.recv_step = load_relaxed(cx.recv_head);
   cx.send_step = load_relaxed(cx.send_tail);
+  cx.tail_cache = 0;
+  cx.head_cache = 0;
   cx.abort_flag = sh.comm.abort_flag;
   cx.abort_host = sh.comm.abort_host;
   cx.timeout = sh.comm.spin_timeout_ticks;

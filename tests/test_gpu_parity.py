@@ -263,3 +263,17 @@ def test_ranks_spread_over_xcds(proto, dtype):
     x = _rand(dtype, (4, 120001), 21)
     _check_vs_sim(comm, [x], dtype, buff, 4)
     comm.close()
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+@pytest.mark.parametrize("spc", [1, 4])
+def test_slices_per_chunk_same_bits(dtype, spc):
+    """Slicing is timing only: 1 slice of 4 steps or 4 slices of 1 step give
+    the same bits as the oracle's 2 slices of 2 steps (every call still
+    consumes 4 steps)."""
+    buff = SMALL_BUFF["SIMPLE"] * 4
+    comm = _comm(nranks=4, ring_order=[0, 2, 3, 1], mask=0x7, proto="SIMPLE", buff_size=buff,
+                 chunk_steps=4, lanes=3, waves=4, slices_per_chunk=spc)
+    x = _rand(dtype, (4, 200003), 31)
+    _check_vs_sim(comm, [x], dtype, buff, 4)
+    comm.close()
