@@ -94,6 +94,7 @@ def main():
     ap.add_argument("--waves", type=int, default=None)
     ap.add_argument("--launch-mode", type=int, default=None, choices=[0, 1])
     ap.add_argument("--slices", type=int, default=None, choices=[1, 2, 4])
+    ap.add_argument("--placement", type=int, default=None, choices=[0, 1])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the AllReduce, time a plain device copy of MIB MiB "
@@ -142,6 +143,8 @@ def main():
         tune["launch_mode"] = args.launch_mode
     if args.slices is not None:
         tune["slices_per_chunk"] = args.slices
+    if args.placement is not None:
+        tune["placement"] = args.placement
     torch.cuda.set_device(0)
     xs = workloads.inputs_for(w)
     N = w.nranks
