@@ -95,6 +95,7 @@ def main():
     ap.add_argument("--launch-mode", type=int, default=None, choices=[0, 1])
     ap.add_argument("--slices", type=int, default=None, choices=[1, 2, 4])
     ap.add_argument("--placement", type=int, default=None, choices=[0, 1])
+    ap.add_argument("--direct", type=int, default=None, choices=[0, 1])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the AllReduce, time a plain device copy of MIB MiB "
@@ -145,6 +146,8 @@ def main():
         tune["slices_per_chunk"] = args.slices
     if args.placement is not None:
         tune["placement"] = args.placement
+    if args.direct is not None:
+        tune["direct"] = args.direct
     torch.cuda.set_device(0)
     xs = workloads.inputs_for(w)
     N = w.nranks
@@ -208,7 +211,7 @@ def main():
     M = w.message_bytes
     algbw = metrics.algbw_gbps(M, t_step)
     busbw = metrics.busbw_gbps(M, t_step, N)
-    alg_bytes = metrics.algorithmic_bytes(M, N, w.proto)
+    alg_bytes = metrics.algorithmic_bytes(M, N, w.proto, direct=bool(tune.get("direct", 0)))
     achieved = alg_bytes / t_kernel / 1e9
     traffic = measured_traffic(args.workload, shape["lanes"], shape["waves"], alg_bytes)
     out = {

@@ -88,6 +88,16 @@ typedef struct {
                             and every call still consumes chunk_steps steps;
                             smaller slices keep fewer FIFO bytes in flight.
                             Timing only: results are identical            */
+  int direct;            /* Simple only, 0 or 1: the direct variants of the
+                            all-gather half [C23 "发布顺序与 Fence"].  The
+                            rank that completes a chunk, and every rank that
+                            forwards it, writes it straight into the next
+                            rank's receive buffer instead of the FIFO (no
+                            send credit needed); the final receive has nothing
+                            to copy.  Steps still advance on every connector.
+                            Same results; (5N-4)M instead of (6N-4)M bytes
+                            of traffic.  Receive buffers of different ranks
+                            must not overlap.                             */
 } rar_tuning_t;
 
 #define RAR_DEBUG_DROP_RECV_HEAD 1

@@ -135,7 +135,7 @@ def geometry(nranks, mask, proto, buff_size, chunk_steps, dtype, counts):
 
 def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
               in_place=False, slots=8, sched=0, seed=0, drop_recv_head=False,
-              log_calls=False):
+              direct=False, log_calls=False):
     """Run the simulator.
 
     ``inputs`` is a list over works of arrays shaped [N, count] holding the raw
@@ -168,9 +168,10 @@ def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
     if log_calls:
         cap = 1 << 20
         log = (Call * cap)()
+    options = (1 if drop_recv_head else 0) | (2 if direct else 0)
     rc = lib().orc_allreduce(N, _ints(ring_order), mask, PROTO[proto], buff_size, chunk_steps,
                              DTYPE[dtype], len(works), carr, send_ptrs, recv_ptrs, slots, sched,
-                             seed, int(drop_recv_head), ctypes.byref(stats), log, cap)
+                             seed, options, ctypes.byref(stats), log, cap)
     calls = []
     if log_calls:
         for c in log[:stats.calls_recorded]:

@@ -201,6 +201,7 @@ struct Sim {
   int N = 0, C = 0, proto = 0, dtype = 0, slots = 8, chunk_steps = 4;
   int64_t es = 4, step_bytes = 0, sps = 1;
   bool drop_head = false;
+  bool direct = false;  // Simple: all-gather half writes into the next rank's receive buffer
   std::vector<int> index, prev, next;
   std::vector<Conn> conn;  // conn[rank * C + n]: FIFO that `rank` receives on, channel n
   const void* const* sendbufs = nullptr;
@@ -301,11 +302,19 @@ struct Sim {
     const Unit& u = ag.prog[ag.pc];
     const bool recv = u.op != ORC_OP_SEND;
     const bool send = u.op != ORC_OP_RECV;
+    // Direct variants [C23 "发布顺序与 Fence"]: directRecvReduceCopySend and
+    // directRecvCopySend put their result straight into the next rank's
+    // receive buffer (no FIFO slot, so no send credit to wait for);
+    // directRecvCopySend and directRecv find their input already in their own
+    // receive buffer.  Steps still advance on both sides.
+    const bool direct_send =
+        direct && (u.op == ORC_OP_RECV_REDUCE_COPY_SEND || u.op == ORC_OP_RECV_COPY_SEND);
+    const bool direct_recv = direct && (u.op == ORC_OP_RECV_COPY_SEND || u.op == ORC_OP_RECV);
     Conn& rc = conn[(size_t)ag.rank * C + ag.n];
     Conn& sc = conn[(size_t)next[ag.rank] * C + ag.n];
     const uint64_t adv = (uint64_t)sps;
     // sender wait: head + NCCL_STEPS >= step + StepPerSlice
-    if (send && !(sc.head + (uint64_t)slots >= ag.send_step + adv)) return false;
+    if (send && !direct_send && !(sc.head + (uint64_t)slots >= ag.send_step + adv)) return false;
     // receiver wait: tail >= step + StepPerSlice (Simple) or line flags (LL, LL128)
     if (recv) {
       if (proto == ORC_PROTO_SIMPLE) {
@@ -314,11 +323,13 @@ struct Sim {
         return false;
       }
     }
-    std::vector<uint8_t> got;
-    if (recv) read_payload(rc, ag.recv_step, u.nelem, got);
     const uint8_t* src =
         (const uint8_t*)sendbufs[(size_t)u.work * N + ag.rank] + u.offset * es;
     uint8_t* dst = (uint8_t*)recvbufs[(size_t)u.work * N + ag.rank] + u.offset * es;
+    uint8_t* next_dst = (uint8_t*)recvbufs[(size_t)u.work * N + next[ag.rank]] + u.offset * es;
+    std::vector<uint8_t> got;
+    if (recv && direct_recv) got.assign(dst, dst + u.nelem * es);
+    else if (recv) read_payload(rc, ag.recv_step, u.nelem, got);
     std::vector<uint8_t> val((size_t)(u.nelem * es));
     for (int64_t i = 0; i < u.nelem; ++i) {
       uint8_t* v = val.data() + i * es;
@@ -335,11 +346,15 @@ struct Sim {
           break;
       }
     }
-    if (u.op == ORC_OP_RECV_REDUCE_COPY_SEND || u.op == ORC_OP_RECV_COPY_SEND ||
-        u.op == ORC_OP_RECV) {
+    if (u.op == ORC_OP_RECV_REDUCE_COPY_SEND ||
+        ((u.op == ORC_OP_RECV_COPY_SEND || u.op == ORC_OP_RECV) && !direct_recv)) {
       if (u.nelem > 0) std::memcpy(dst, val.data(), val.size());
     }
-    if (send) write_payload(sc, ag.send_step, val);
+    if (send && direct_send) {
+      if (u.nelem > 0) std::memcpy(next_dst, val.data(), val.size());
+    } else if (send) {
+      write_payload(sc, ag.send_step, val);
+    }
     // publish: receiver frees the slots (head), sender announces data (tail)
     if (recv) {
       ag.recv_step += adv;
@@ -497,7 +512,7 @@ int orc_geometry(int nranks, uint64_t channel_mask, int proto, size_t buff_size,
 int orc_allreduce(int nranks, const int* ring_order, uint64_t channel_mask, int proto,
                   size_t buff_size, int chunk_steps, int dtype, int nworks, const size_t* counts,
                   const void* const* sendbufs, void* const* recvbufs, int slots, int sched,
-                  uint64_t seed, int drop_recv_head, orc_stats* stats, orc_call* call_log,
+                  uint64_t seed, int options, orc_stats* stats, orc_call* call_log,
                   int64_t call_log_cap) {
   if (!valid_params(nranks, channel_mask, proto, buff_size, chunk_steps, dtype, slots))
     return ORC_INVALID;
@@ -511,7 +526,9 @@ int orc_allreduce(int nranks, const int* ring_order, uint64_t channel_mask, int 
   sim.es = (int64_t)elem_size(dtype);
   sim.step_bytes = (int64_t)(buff_size / (size_t)slots);
   sim.sps = proto == ORC_PROTO_SIMPLE ? chunk_steps / 2 : 1;
-  sim.drop_head = drop_recv_head != 0;
+  sim.drop_head = (options & ORC_OPT_DROP_RECV_HEAD) != 0;
+  sim.direct = (options & ORC_OPT_DIRECT) != 0;
+  if (sim.direct && proto != ORC_PROTO_SIMPLE) return ORC_INVALID;
   sim.sendbufs = sendbufs;
   sim.recvbufs = recvbufs;
   sim.stats = stats;

@@ -39,6 +39,14 @@ enum {
   ORC_OP_RECV = 4                   /* recv final chunk, write output               */
 };
 
+/* Options of orc_allreduce (bit flags). */
+enum {
+  ORC_OPT_DROP_RECV_HEAD = 1, /* fault hook: receivers never publish head           */
+  ORC_OPT_DIRECT = 2          /* Simple only: the all-gather half writes straight into
+                                 the next rank's receive buffer instead of its FIFO
+                                 [C23 "发布顺序与 Fence", direct read/write]        */
+};
+
 /* Return codes. */
 enum { ORC_OK = 0, ORC_DEADLOCK = 1, ORC_INVALID = 2, ORC_CORRUPT = 3 };
 
@@ -94,13 +102,13 @@ typedef struct {
  *   slots               : FIFO slots per connector (NCCL_STEPS, normally 8)
  *   sched               : 0 = round robin, each agent runs until it blocks
  *                          1 = seeded random choice of agent, one unit at a time
- *   drop_recv_head      : fault hook -- receivers never publish head
+ *   options             : ORC_OPT_* bits
  *   call_log            : optional, records every primitive call (may be NULL)
  */
 int orc_allreduce(int nranks, const int* ring_order, uint64_t channel_mask, int proto,
                   size_t buff_size, int chunk_steps, int dtype, int nworks, const size_t* counts,
                   const void* const* sendbufs, void* const* recvbufs, int slots, int sched,
-                  uint64_t seed, int drop_recv_head, orc_stats* stats, orc_call* call_log,
+                  uint64_t seed, int options, orc_stats* stats, orc_call* call_log,
                   int64_t call_log_cap);
 
 /* Single-connector fault model [C23 "状态机故障注入"]: a producer streams

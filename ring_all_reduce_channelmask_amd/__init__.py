@@ -59,7 +59,7 @@ class Comm:
 
     def __init__(self, nranks, ring_order, mask, proto="SIMPLE", buff_size=0, chunk_steps=0,
                  lanes=0, waves=0, timeout_us=0, debug_flags=0, launch_mode=0, placement=0,
-                 slices_per_chunk=0):
+                 slices_per_chunk=0, direct=0):
         lib = _lib.load()
         if len(ring_order) != nranks:
             raise ValueError("ring_order must list every rank once")
@@ -69,7 +69,7 @@ class Comm:
         self.proto = proto
         order = (ctypes.c_int * nranks)(*self.ring_order)
         tune = _lib.Tuning(lanes, waves, timeout_us, debug_flags, launch_mode, placement,
-                           slices_per_chunk)
+                           slices_per_chunk, direct)
         h = ctypes.c_void_p()
         _lib.check(lib.rar_comm_create(ctypes.byref(h), nranks, order, mask, _lib.PROTO[proto],
                                        buff_size, chunk_steps, ctypes.byref(tune)))

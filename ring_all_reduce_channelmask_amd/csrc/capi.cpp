@@ -272,7 +272,7 @@ rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order,
     return fail(RAR_INVALID_ARGUMENT, err);
   rar::RingInfo ring;
   if (!rar::build_ring(nranks, ring_order, &ring, &err)) return fail(RAR_INVALID_ARGUMENT, err);
-  rar_tuning_t tune{0, 0, 0, 0, 0, 0, 0};
+  rar_tuning_t tune{0, 0, 0, 0, 0, 0, 0, 0};
   if (tuning) tune = *tuning;
   if (tune.lanes_per_channel < 0 || tune.lanes_per_channel > rar::kMaxLanes)
     return fail(RAR_INVALID_ARGUMENT, "lanes_per_channel must be in [0, 16]");
@@ -288,6 +288,9 @@ rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order,
     return fail(RAR_INVALID_ARGUMENT, "slices_per_chunk must be 0, 1, 2 or 4");
   if (tune.slices_per_chunk == 4 && (int)proto == rar::kSimple && chunk_steps != 4)
     return fail(RAR_INVALID_ARGUMENT, "4 slices per chunk need chunk_steps 4");
+  if (tune.direct != 0 && tune.direct != 1) return fail(RAR_INVALID_ARGUMENT, "direct must be 0 or 1");
+  if (tune.direct && (int)proto != rar::kSimple)
+    return fail(RAR_UNSUPPORTED, "the direct variant exists for the Simple protocol only");
 
   int dev = 0;
   RAR_HIP(hipGetDevice(&dev));
@@ -397,6 +400,7 @@ rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order,
   hc.hot.chunk_steps = chunk_steps;
   const int spc = tune.slices_per_chunk ? tune.slices_per_chunk : rar::kSlicesPerChunk;
   hc.hot.slices_per_chunk = spc;
+  hc.hot.direct = tune.direct;
   hc.hot.step_per_slice = (int)proto == rar::kSimple ? chunk_steps / spc : 1;
   hc.hot.channel_mask = channel_mask;
   hc.hot.fifo = c->d_fifo;

@@ -88,8 +88,8 @@ struct alignas(16) DevCommHot {
   int64_t lane_buff_bytes;  // kSteps * lane_step_bytes
   int32_t chunk_steps;  // Simple
   int32_t step_per_slice;      // Simple: chunk_steps / slices_per_chunk
-  int32_t slices_per_chunk;    // Simple: 2 (default) or 4; timing only
-  int32_t pad1;
+  int32_t slices_per_chunk;    // Simple: 2 (default), 1 or 4; timing only
+  int32_t direct;              // Simple: direct all-gather (next rank's receive buffer)
   uint64_t channel_mask;
   uint8_t* fifo;               // lane FIFO of (r, n, p) at ((r * C + n) * P + p) * lane_buff_bytes
   ConnCounters* counters;      // ((r * C + n) * P + p)

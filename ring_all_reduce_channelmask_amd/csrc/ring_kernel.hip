@@ -113,7 +113,8 @@ struct Ctx {
   Shmem* sh;
   void* const* ptrs;
   int tid, nthreads, workers;
-  int rank, nranks, ring_index, lane, nlanes, sps, spc;
+  int rank, next, nranks, ring_index, lane, nlanes, sps, spc;
+  bool direct;  // Simple: all-gather half straight into the next rank's receive buffer
   int64_t step_bytes;       // channel slot: sets the slice geometry
   int64_t lane_step_bytes;  // this lane's slot in its own FIFO
   uint8_t* recv_fifo;
@@ -220,6 +221,11 @@ __device__ __forceinline__ bool wait_credit(Ctx& cx, uint64_t n) {
 #ifndef RAR_NT_FIFO
 #define RAR_NT_FIFO 0
 #endif
+// Direct variants: the chunk written into the next rank's receive buffer is
+// read back by that rank one hop later, like a FIFO slot.
+#ifndef RAR_NT_DIRECT
+#define RAR_NT_DIRECT 0
+#endif
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
@@ -245,14 +251,19 @@ __device__ __forceinline__ void st16(v4u* p, v4u v) {
 
 // reduceCopy over n elements with 16-byte vectors, RAR_UNROLL in flight per
 // thread and source; consecutive threads touch consecutive 16-byte vectors.
-template <class Ty, bool kRecv, bool kSrc, bool kDst, bool kSend>
+// `fin` / `fout` are FIFO slots, or user buffers in the direct variants
+// (kUserIn / kUserOut), which then take the user-buffer access hint.
+template <class Ty, bool kRecv, bool kSrc, bool kDst, bool kSend, bool kUserIn = false,
+          bool kUserOut = false>
 __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typename Ty::S* src,
                                             typename Ty::S* dst, typename Ty::S* fout, int64_t n,
                                             int tid, int nthr) {
   using S = typename Ty::S;
   constexpr int kVec = 16 / sizeof(S);
   constexpr int kUnroll = RAR_UNROLL;
-  constexpr bool kNu = RAR_NT_USER != 0, kNf = RAR_NT_FIFO != 0;
+  constexpr bool kNu = RAR_NT_USER != 0;
+  constexpr bool kNi = kUserIn ? RAR_NT_DIRECT != 0 : RAR_NT_FIFO != 0;
+  constexpr bool kNo = kUserOut ? RAR_NT_DIRECT != 0 : RAR_NT_FIFO != 0;
   const int64_t nv = n / kVec;
   const v4u* vin = reinterpret_cast<const v4u*>(fin);
   const v4u* vsrc = reinterpret_cast<const v4u*>(src);
@@ -263,23 +274,23 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
     v4u a[kUnroll], b[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (kRecv) a[u] = ld16<kNf>(vin + i + (int64_t)u * nthr);
+      if (kRecv) a[u] = ld16<kNi>(vin + i + (int64_t)u * nthr);
       if (kSrc) b[u] = ld16<kNu>(vsrc + i + (int64_t)u * nthr);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const v4u r = (kRecv && kSrc) ? add16v<Ty>(a[u], b[u]) : (kRecv ? a[u] : b[u]);
       if (kDst) st16<kNu>(vdst + i + (int64_t)u * nthr, r);
-      if (kSend) st16<kNf>(vout + i + (int64_t)u * nthr, r);
+      if (kSend) st16<kNo>(vout + i + (int64_t)u * nthr, r);
     }
   }
   for (; i < nv; i += nthr) {
     v4u a = {0, 0, 0, 0}, b = a;
-    if (kRecv) a = ld16<kNf>(vin + i);
+    if (kRecv) a = ld16<kNi>(vin + i);
     if (kSrc) b = ld16<kNu>(vsrc + i);
     const v4u r = (kRecv && kSrc) ? add16v<Ty>(a, b) : (kRecv ? a : b);
     if (kDst) st16<kNu>(vdst + i, r);
-    if (kSend) st16<kNf>(vout + i, r);
+    if (kSend) st16<kNo>(vout + i, r);
   }
   for (int64_t e = nv * kVec + tid; e < n; e += nthr) {
     S a = 0, b = 0;
@@ -296,10 +307,15 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
 // of the last wave) [C23 "Primitive API 是模板组合", "Simple 的线程角色",
 // "发布顺序与 Fence", "Slice Size"].  Empty slices still wait and post.
 template <class Ty, int OP>
-__device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
-                            int chunk) {
+__device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
+                            typename Ty::S* next_dst, int64_t nelem, int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
+  // Direct variants [C23 "发布顺序与 Fence"]: the final value goes straight
+  // into the next rank's receive buffer (no FIFO slot: no credit wait), and
+  // the all-gather receivers find their data in their own receive buffer.
+  const bool direct_send = cx.direct && (OP == kOpRecvReduceCopySend || OP == kOpRecvCopySend);
+  const bool direct_recv = cx.direct && (OP == kOpRecvCopySend || OP == kOpRecv);
   constexpr int kVec = 16 / sizeof(S);
   const int sps = cx.sps;
   const int64_t step_elems = cx.step_bytes / (int64_t)sizeof(S);
@@ -321,7 +337,7 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
     if (cx.tid < 2) {
       bool ok = true;
       if (cx.tid == 0 && O::kRecv) ok = wait_cached(cx.recv_tail, cx.recv_step + sps, cx.tail_cache, cx);
-      if (cx.tid == 1 && O::kSend) ok = wait_credit(cx, sps);
+      if (cx.tid == 1 && O::kSend && !direct_send) ok = wait_credit(cx, sps);
       acquire_fence();
       if (!ok) cx.sh->abort = 1;
     }
@@ -334,8 +350,21 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
     if (cx.tid < cx.workers && hi > lo) {
       const S* fin = reinterpret_cast<const S*>(cx.recv_fifo + (cx.recv_step % kSteps) * cx.lane_step_bytes);
       S* fout = reinterpret_cast<S*>(cx.send_fifo + (cx.send_step % kSteps) * cx.lane_step_bytes);
-      reduce_copy<Ty, O::kRecv, O::kSrc, O::kDst, O::kSend>(fin, src + s_off + lo, dst + s_off + lo,
-                                                             fout, hi - lo, cx.tid, cx.workers);
+      const int64_t e0 = s_off + lo;
+      if (!cx.direct || OP == kOpSend || OP == kOpRecvReduceSend) {
+        reduce_copy<Ty, O::kRecv, O::kSrc, O::kDst, O::kSend>(fin, src + e0, dst + e0, fout, hi - lo,
+                                                               cx.tid, cx.workers);
+      } else if (OP == kOpRecvReduceCopySend) {
+        // FIFO partial + own input -> own output and the next rank's output
+        reduce_copy<Ty, true, true, true, true, false, true>(fin, src + e0, dst + e0, next_dst + e0,
+                                                             hi - lo, cx.tid, cx.workers);
+      } else if (OP == kOpRecvCopySend) {
+        // already in the own output (written by prev) -> the next rank's output
+        reduce_copy<Ty, true, false, false, true, true, true>(dst + e0, src + e0, dst + e0,
+                                                              next_dst + e0, hi - lo, cx.tid,
+                                                              cx.workers);
+      }
+      // direct recv: the data is already in place
     }
     drain_vmem();
     __syncthreads();
@@ -608,12 +637,13 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
 // ---------------------------------------------------------------- runRing
 template <class Ty, int PROTO, int OP>
 __device__ __forceinline__ void prim(Ctx& cx, const typename Ty::S* sendbuf, typename Ty::S* recvbuf,
-                                     int64_t base, int64_t cc, int64_t rem, int chunk) {
+                                     typename Ty::S* next_recvbuf, int64_t base, int64_t cc,
+                                     int64_t rem, int chunk) {
   const int64_t chunk_off = (int64_t)chunk * cc;
   const int64_t nelem = clamp64(rem - chunk_off, 0, cc);
   const int64_t off = base + chunk_off;
   if (PROTO == kSimple)
-    simple_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem, chunk);
+    simple_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, next_recvbuf + off, nelem, chunk);
   else if (PROTO == kLL)
     ll_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem, chunk);
   else
@@ -631,6 +661,7 @@ __device__ void run_ring(Ctx& cx, const DevWork& w) {
   const int N = cx.nranks, ix = cx.ring_index;
   const S* sendbuf = reinterpret_cast<const S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.rank) * 2]);
   S* recvbuf = reinterpret_cast<S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.rank) * 2 + 1]);
+  S* next_recvbuf = reinterpret_cast<S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.next) * 2 + 1]);
   int workers = (int)w.n_waves * kWaveSize;
   cx.workers = workers < cx.nthreads ? workers : cx.nthreads;
   const int64_t loop_count = (int64_t)N * w.chunk_count;
@@ -639,15 +670,17 @@ __device__ void run_ring(Ctx& cx, const DevWork& w) {
     const int64_t cc = rem < loop_count ? align_up(div_up(rem, N), kVec) : w.chunk_count;
     const int64_t base = w.grid_offset + eo;
     auto mod = [N](int x) { return ((x % N) + N) % N; };
-    prim<Ty, PROTO, kOpSend>(cx, sendbuf, recvbuf, base, cc, rem, mod(ix - 1));
+    prim<Ty, PROTO, kOpSend>(cx, sendbuf, recvbuf, next_recvbuf, base, cc, rem, mod(ix - 1));
     for (int j = 2; j < N && !cx.aborted; ++j)
-      prim<Ty, PROTO, kOpRecvReduceSend>(cx, sendbuf, recvbuf, base, cc, rem, mod(ix - j));
+      prim<Ty, PROTO, kOpRecvReduceSend>(cx, sendbuf, recvbuf, next_recvbuf, base, cc, rem,
+                                         mod(ix - j));
     if (cx.aborted) return;
-    prim<Ty, PROTO, kOpRecvReduceCopySend>(cx, sendbuf, recvbuf, base, cc, rem, ix);
+    prim<Ty, PROTO, kOpRecvReduceCopySend>(cx, sendbuf, recvbuf, next_recvbuf, base, cc, rem, ix);
     for (int j = 1; j < N - 1 && !cx.aborted; ++j)
-      prim<Ty, PROTO, kOpRecvCopySend>(cx, sendbuf, recvbuf, base, cc, rem, mod(ix - j));
+      prim<Ty, PROTO, kOpRecvCopySend>(cx, sendbuf, recvbuf, next_recvbuf, base, cc, rem,
+                                       mod(ix - j));
     if (cx.aborted) return;
-    prim<Ty, PROTO, kOpRecv>(cx, sendbuf, recvbuf, base, cc, rem, mod(ix + 1));
+    prim<Ty, PROTO, kOpRecv>(cx, sendbuf, recvbuf, next_recvbuf, base, cc, rem, mod(ix + 1));
     if (cx.aborted) return;
   }
 }
@@ -730,6 +763,8 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.nranks = sh.comm.n_ranks;
   const DevRank me = comm->ranks[rank];
   cx.ring_index = me.index;
+  cx.next = me.next;
+  cx.direct = sh.comm.direct != 0;
   cx.lane = lane;
   cx.nlanes = sh.comm.n_lanes;
   cx.sps = sh.comm.step_per_slice;

@@ -277,3 +277,57 @@ def test_slices_per_chunk_same_bits(dtype, spc):
     x = _rand(dtype, (4, 200003), 31)
     _check_vs_sim(comm, [x], dtype, buff, 4)
     comm.close()
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("placement", [0, 1])
+def test_direct_variant_vs_oracle(dtype, in_place, placement):
+    """Direct all-gather (into the next rank's receive buffer) against the
+    oracle's direct simulation and its FIFO simulation: same bits; with the
+    ranks spread over XCDs the direct writes need the write-back publication."""
+    buff = SMALL_BUFF["SIMPLE"] * 2
+    comm = _comm(nranks=4, ring_order=[0, 2, 3, 1], mask=0x5, proto="SIMPLE", buff_size=buff,
+                 lanes=3, waves=4, direct=1, placement=placement)
+    x = _rand(dtype, (4, 150011), 41)
+    got = run_hip(comm, [x], dtype, in_place=in_place)[0]
+    comm.close()
+    for direct in (True, False):
+        rc, want, _, _ = oracle.allreduce([x], [0, 2, 3, 1], 0x5, "SIMPLE", buff, 4, dtype,
+                                          direct=direct)
+        assert rc == oracle.OK
+        assert_bits_equal(got, want[0], f"direct={direct}")
+
+
+def test_direct_variant_full_size_and_many_launches():
+    """The 64 MiB workload with the direct variant, bit for bit against the
+    closed form, then 200 back-to-back launches of a small one on one comm."""
+    import torch
+    from .gpu_util import to_device, to_host
+    w = wl.WORKLOADS["simple_64m"]
+    xs = wl.inputs_for(w)
+    comm = _comm(nranks=4, ring_order=list(w.ring_order), mask=w.mask, proto="SIMPLE",
+                 buff_size=w.buff_size, chunk_steps=4, lanes=5, waves=8, direct=1, launch_mode=1)
+    got = run_hip(comm, xs, "float32")[0]
+    want = cf.allreduce(xs, list(w.ring_order), w.mask, "SIMPLE", w.buff_size, 4, "float32")[0]
+    for r in range(4):
+        assert_bits_equal(got[r], want, f"rank {r}")
+    x = np.random.default_rng(3).integers(-1000, 1000, size=(4, 77777)).astype(np.int32)
+    sends = [to_device(x[r], "int32") for r in range(4)]
+    recvs = [torch.zeros_like(s) for s in sends]
+    for _ in range(200):
+        comm.allreduce(sends, recvs)
+    torch.cuda.synchronize()
+    assert comm.async_error() == 0
+    for r in range(4):
+        np.testing.assert_array_equal(to_host(recvs[r], "int32"), x.sum(axis=0))
+    comm.close()
+
+
+def test_direct_variant_rejected_for_ll():
+    import ring_all_reduce_channelmask_amd as rar
+    from ring_all_reduce_channelmask_amd import _lib
+    for proto in ("LL", "LL128"):
+        with pytest.raises(rar.RarError) as e:
+            _comm(nranks=4, ring_order=[0, 1, 2, 3], mask=1, proto=proto, direct=1)
+        assert e.value.code == _lib.UNSUPPORTED

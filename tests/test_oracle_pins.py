@@ -542,3 +542,52 @@ def test_algorithmic_bytes():
     assert metrics.algorithmic_bytes(M, 8, "SIMPLE") == 44 * M
     assert metrics.algorithmic_bytes(M, 4, "LL") == 32 * M
     assert abs(metrics.algorithmic_bytes(M, 4, "LL128") - 20.8 * M) < 1
+    for N in (2, 3, 4, 8):
+        assert metrics.algorithmic_bytes(M, N, "SIMPLE", direct=True) == (5 * N - 4) * M
+
+
+# ------------------------------------------------------------- direct variant
+@pytest.mark.parametrize("N", [2, 3, 4, 8])
+def test_direct_variant_same_result_and_completes(N):
+    """Direct read/write (Course 23, "发布顺序与 Fence": the direct primitives
+    place data in the peer's user buffer and skip the send-credit wait, but
+    steps and ordering remain): the all-gather half writes into the next rank's
+    receive buffer.  The values are the same as through the FIFO, in place
+    and out of place, under random interleavings, and nothing deadlocks."""
+    rng = np.random.default_rng(N)
+    order = [int(v) for v in rng.permutation(N)]
+    x = _draw("float32", (N, 30011), N)
+    base = oracle.allreduce([x], order, 0x5, "SIMPLE", SMALL_BUFF["SIMPLE"], 4, "float32")[1][0]
+    for in_place in (False, True):
+        for sched, seed in ((0, 0), (1, 1), (1, 2)):
+            rc, out, _, _ = oracle.allreduce([x], order, 0x5, "SIMPLE", SMALL_BUFF["SIMPLE"], 4,
+                                             "float32", in_place=in_place, sched=sched, seed=seed,
+                                             direct=True)
+            assert rc == oracle.OK
+            np.testing.assert_array_equal(out[0], base)
+    xi = rng.integers(-2 ** 31, 2 ** 31, size=(N, 5000)).astype(np.int32)
+    rc, out, _, _ = oracle.allreduce([xi], order, 0x3, "SIMPLE", SMALL_BUFF["SIMPLE"], 2, "int32",
+                                     direct=True)
+    assert rc == oracle.OK
+    for r in range(N):
+        np.testing.assert_array_equal(out[0][r], _wrap_sum(xi))
+
+
+def test_direct_variant_needs_simple():
+    x = np.ones((4, 64), dtype=np.float32)
+    for proto in ("LL", "LL128"):
+        assert oracle.allreduce([x], [0, 1, 2, 3], 1, proto, SMALL_BUFF[proto], 4, "float32",
+                                direct=True)[0] == oracle.INVALID
+
+
+def test_direct_variant_bytes():
+    """With direct all-gather each rank writes 2(N-1) chunks but reads its
+    FIFO only in the reduce-scatter half: FIFO payload per rank is N M/N."""
+    N, count = 4, 4 * 8192
+    x = np.ones((N, count), dtype=np.float32)
+    rc, _, st, _ = oracle.allreduce([x], [0, 1, 2, 3], 0x1, "SIMPLE", 65536, 4, "float32",
+                                    direct=True)
+    assert rc == oracle.OK
+    M = count * 4
+    for r in range(N):
+        assert st.payload_sent[r] == 2 * (N - 1) * M // N
