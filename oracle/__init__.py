@@ -82,6 +82,15 @@ def lib():
                                     ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int,
                                     ctypes.c_uint64, ctypes.c_int, ctypes.POINTER(Stats),
                                     ctypes.POINTER(Call), ctypes.c_int64]
+        L.orc_allreduce_rings.argtypes = [ctypes.c_int, ctypes.c_int, i32p, ctypes.c_uint64,
+                                          ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.POINTER(ctypes.c_void_p),
+                                          ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_uint64, ctypes.c_int,
+                                          ctypes.POINTER(Stats), ctypes.POINTER(Call),
+                                          ctypes.c_int64]
         L.orc_stream_fault.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_int64),
                                        ctypes.POINTER(ctypes.c_int64),
@@ -139,11 +148,14 @@ def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
     """Run the simulator.
 
     ``inputs`` is a list over works of arrays shaped [N, count] holding the raw
-    elements (int32, float32, or uint16 bit patterns for bfloat16).  Returns
-    (rc, outputs, stats, calls): outputs is a list over works of [N, count]
-    arrays in the same representation.
+    elements (int32, float32, or uint16 bit patterns for bfloat16).
+    ``ring_order`` is one ring, or a list of rings (channel id c runs ring
+    c mod len(rings)).  Returns (rc, outputs, stats, calls): outputs is a list
+    over works of [N, count] arrays in the same representation.
     """
-    N = len(ring_order)
+    rings = [list(r) for r in ring_order] if isinstance(ring_order[0], (list, tuple)) \
+        else [list(ring_order)]
+    N = len(rings[0])
     if isinstance(inputs, np.ndarray):
         inputs = [inputs]
     works = [np.ascontiguousarray(x) for x in inputs]
@@ -169,9 +181,12 @@ def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
         cap = 1 << 20
         log = (Call * cap)()
     options = (1 if drop_recv_head else 0) | (2 if direct else 0)
-    rc = lib().orc_allreduce(N, _ints(ring_order), mask, PROTO[proto], buff_size, chunk_steps,
-                             DTYPE[dtype], len(works), carr, send_ptrs, recv_ptrs, slots, sched,
-                             seed, options, ctypes.byref(stats), log, cap)
+    flat = [r for ring in rings for r in ring]
+    assert all(len(ring) == N for ring in rings)
+    rc = lib().orc_allreduce_rings(N, len(rings), _ints(flat), mask, PROTO[proto], buff_size,
+                                   chunk_steps, DTYPE[dtype], len(works), carr, send_ptrs,
+                                   recv_ptrs, slots, sched, seed, options, ctypes.byref(stats),
+                                   log, cap)
     calls = []
     if log_calls:
         for c in log[:stats.calls_recorded]:

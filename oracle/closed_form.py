@@ -43,9 +43,10 @@ def chunk_max(proto, buff_size, chunk_steps, dtype):
     return ((step // 128) * 120) // es  # 128-byte line = 15 payload words + flag
 
 
-def owner_positions(counts, nranks, nchannels, cmax, dtype):
+def owner_positions(counts, nranks, nchannels, cmax, dtype, with_channel=False):
     """For each collective of the launch, an int array giving the ring position
-    that owns each element (the chunk index of the element)."""
+    that owns each element (the chunk index of the element); with
+    ``with_channel``, also the dense channel index of each element."""
     vec = 16 // _elem_size(dtype)
     starts, total = [], 0
     for c in counts:
@@ -53,8 +54,9 @@ def owner_positions(counts, nranks, nchannels, cmax, dtype):
         starts.append(s)
         total = s + c
     owners = [np.full(c, -1, dtype=np.int64) for c in counts]
+    chans = [np.full(c, -1, dtype=np.int64) for c in counts]
     if total == 0:
-        return owners
+        return (owners, chans) if with_channel else owners
     per_ch = _align_up(_div_up(total, nchannels), vec)
     for n in range(nchannels):
         lo, hi = n * per_ch, min((n + 1) * per_ch, total)
@@ -74,10 +76,11 @@ def owner_positions(counts, nranks, nchannels, cmax, dtype):
                     if nel:
                         base = grid_off + elem_off + first
                         owners[w][base:base + nel] = chunk
+                        chans[w][base:base + nel] = n
                 elem_off += loop_count
     for o in owners:
         assert (o >= 0).all()
-    return owners
+    return (owners, chans) if with_channel else owners
 
 
 def _round_bf16(v64):
@@ -125,19 +128,27 @@ def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype):
     """
     if isinstance(inputs, np.ndarray):
         inputs = [inputs]
-    N = len(ring_order)
-    nch = bin(mask).count("1")
-    pos0 = list(ring_order).index(0)
-    # user rank at ring position p (positions counted from user rank 0)
-    rank_at = np.array([ring_order[(p + pos0) % N] for p in range(N)], dtype=np.int64)
+    # one ring, or one per channel id (channel c runs ring c mod len(rings))
+    rings = [list(r) for r in ring_order] if isinstance(ring_order[0], (list, tuple)) \
+        else [list(ring_order)]
+    N = len(rings[0])
+    ids = [b for b in range(64) if (mask >> b) & 1]
+    nch = len(ids)
+    # rank_at[n, p]: user rank at ring position p of dense channel n, positions
+    # counted from user rank 0 along that channel's ring
+    rank_at = np.zeros((nch, N), dtype=np.int64)
+    for n, cid in enumerate(ids):
+        ring = rings[cid % len(rings)]
+        pos0 = ring.index(0)
+        rank_at[n] = [ring[(p + pos0) % N] for p in range(N)]
     cmax = chunk_max(proto, buff_size, chunk_steps, dtype)
     counts = [int(x.shape[1]) for x in inputs]
-    owners = owner_positions(counts, N, nch, cmax, dtype)
+    owners, chans = owner_positions(counts, N, nch, cmax, dtype, with_channel=True)
     results = []
-    for x, own in zip(inputs, owners):
+    for x, own, ch in zip(inputs, owners, chans):
         cols = np.arange(x.shape[1])
-        acc = x[rank_at[(own + 1) % N], cols]
+        acc = x[rank_at[ch, (own + 1) % N], cols]
         for k in range(2, N + 1):
-            acc = _hop(acc, x[rank_at[(own + k) % N], cols], dtype)
+            acc = _hop(acc, x[rank_at[ch, (own + k) % N], cols], dtype)
         results.append(acc)
     return results

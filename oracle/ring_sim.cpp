@@ -202,6 +202,9 @@ struct Sim {
   int64_t es = 4, step_bytes = 0, sps = 1;
   bool drop_head = false;
   bool direct = false;  // Simple: all-gather half writes into the next rank's receive buffer
+  // Ring of each active channel: entry [n * N + rank] for dense channel n.
+  // Channel id c follows ring c mod nrings [C12 "为什么 channels 会重复":
+  // the base rings are duplicated onto the following channels].
   std::vector<int> index, prev, next;
   std::vector<Conn> conn;  // conn[rank * C + n]: FIFO that `rank` receives on, channel n
   const void* const* sendbufs = nullptr;
@@ -311,7 +314,8 @@ struct Sim {
         direct && (u.op == ORC_OP_RECV_REDUCE_COPY_SEND || u.op == ORC_OP_RECV_COPY_SEND);
     const bool direct_recv = direct && (u.op == ORC_OP_RECV_COPY_SEND || u.op == ORC_OP_RECV);
     Conn& rc = conn[(size_t)ag.rank * C + ag.n];
-    Conn& sc = conn[(size_t)next[ag.rank] * C + ag.n];
+    const int nxt = next[(size_t)ag.n * N + ag.rank];
+    Conn& sc = conn[(size_t)nxt * C + ag.n];
     const uint64_t adv = (uint64_t)sps;
     // sender wait: head + NCCL_STEPS >= step + StepPerSlice
     if (send && !direct_send && !(sc.head + (uint64_t)slots >= ag.send_step + adv)) return false;
@@ -326,7 +330,7 @@ struct Sim {
     const uint8_t* src =
         (const uint8_t*)sendbufs[(size_t)u.work * N + ag.rank] + u.offset * es;
     uint8_t* dst = (uint8_t*)recvbufs[(size_t)u.work * N + ag.rank] + u.offset * es;
-    uint8_t* next_dst = (uint8_t*)recvbufs[(size_t)u.work * N + next[ag.rank]] + u.offset * es;
+    uint8_t* next_dst = (uint8_t*)recvbufs[(size_t)u.work * N + nxt] + u.offset * es;
     std::vector<uint8_t> got;
     if (recv && direct_recv) got.assign(dst, dst + u.nelem * es);
     else if (recv) read_payload(rc, ag.recv_step, u.nelem, got);
@@ -397,7 +401,7 @@ struct Sim {
 void build_program(Agent& ag, const Sim& sim, const std::vector<orc_piece>& pieces) {
   const int N = sim.N;
   std::vector<int> ops(2 * N - 1), chunks(2 * N - 1);
-  orc_ring_schedule(N, sim.index[ag.rank], ops.data(), chunks.data());
+  orc_ring_schedule(N, sim.index[(size_t)ag.n * N + ag.rank], ops.data(), chunks.data());
   const int64_t vec = 16 / sim.es;
   const int64_t step_elems = sim.step_bytes / sim.es;
   for (const orc_piece& p : pieces) {
@@ -514,6 +518,16 @@ int orc_allreduce(int nranks, const int* ring_order, uint64_t channel_mask, int 
                   const void* const* sendbufs, void* const* recvbufs, int slots, int sched,
                   uint64_t seed, int options, orc_stats* stats, orc_call* call_log,
                   int64_t call_log_cap) {
+  return orc_allreduce_rings(nranks, 1, ring_order, channel_mask, proto, buff_size, chunk_steps,
+                             dtype, nworks, counts, sendbufs, recvbufs, slots, sched, seed, options,
+                             stats, call_log, call_log_cap);
+}
+
+int orc_allreduce_rings(int nranks, int nrings, const int* ring_orders, uint64_t channel_mask,
+                        int proto, size_t buff_size, int chunk_steps, int dtype, int nworks,
+                        const size_t* counts, const void* const* sendbufs, void* const* recvbufs,
+                        int slots, int sched, uint64_t seed, int options, orc_stats* stats,
+                        orc_call* call_log, int64_t call_log_cap) {
   if (!valid_params(nranks, channel_mask, proto, buff_size, chunk_steps, dtype, slots))
     return ORC_INVALID;
   if (nworks < 1 || !counts || !sendbufs || !recvbufs) return ORC_INVALID;
@@ -534,15 +548,19 @@ int orc_allreduce(int nranks, const int* ring_order, uint64_t channel_mask, int 
   sim.stats = stats;
   sim.log = call_log;
   sim.log_cap = call_log ? call_log_cap : 0;
-  sim.index.assign(nranks, 0);
-  sim.prev.assign(nranks, 0);
-  sim.next.assign(nranks, 0);
-  if (orc_ring_setup(nranks, ring_order, sim.index.data(), sim.prev.data(), sim.next.data()) !=
-      ORC_OK)
-    return ORC_INVALID;
+  if (nrings < 1 || !ring_orders) return ORC_INVALID;
   for (int b = 0; b < 64; ++b)
     if (channel_mask & (1ull << b)) sim.channel_ids.push_back(b);
   sim.C = (int)sim.channel_ids.size();
+  sim.index.assign((size_t)sim.C * nranks, 0);
+  sim.prev.assign((size_t)sim.C * nranks, 0);
+  sim.next.assign((size_t)sim.C * nranks, 0);
+  for (int n = 0; n < sim.C; ++n) {
+    const int* order = ring_orders + (size_t)(sim.channel_ids[n] % nrings) * nranks;
+    const size_t at = (size_t)n * nranks;
+    if (orc_ring_setup(nranks, order, &sim.index[at], &sim.prev[at], &sim.next[at]) != ORC_OK)
+      return ORC_INVALID;
+  }
   if (stats) {
     std::memset(stats, 0, sizeof(*stats));
     stats->deadlock_rank = -1;

@@ -111,6 +111,15 @@ int orc_allreduce(int nranks, const int* ring_order, uint64_t channel_mask, int 
                   uint64_t seed, int options, orc_stats* stats, orc_call* call_log,
                   int64_t call_log_cap);
 
+/* Same, with one ring per channel [C12 "GRAPH 重建", "为什么 channels 会重复"]:
+ * ring_orders holds nrings rings of nranks ranks each; channel id c runs ring
+ * c mod nrings (the base rings duplicated onto the following channels). */
+int orc_allreduce_rings(int nranks, int nrings, const int* ring_orders, uint64_t channel_mask,
+                        int proto, size_t buff_size, int chunk_steps, int dtype, int nworks,
+                        const size_t* counts, const void* const* sendbufs, void* const* recvbufs,
+                        int slots, int sched, uint64_t seed, int options, orc_stats* stats,
+                        orc_call* call_log, int64_t call_log_cap);
+
 /* Single-connector fault model [C23 "状态机故障注入"]: a producer streams
  * `nsteps` tagged steps through one connector of `slots` slots while a
  * consumer drains it.  Faults:

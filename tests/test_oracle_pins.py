@@ -591,3 +591,49 @@ def test_direct_variant_bytes():
     M = count * 4
     for r in range(N):
         assert st.payload_sent[r] == 2 * (N - 1) * M // N
+
+
+# ------------------------------------------------- per-channel rings (f2)
+def test_per_channel_rings_graph_layout():
+    """Course 12 "GRAPH 重建：N=4" and "为什么 channels 会重复": 12 channels
+    over six base rings, channels 6-11 repeating 0-5.  In the simulator every
+    channel's rank 0 follows its own ring's schedule (first send = chunk
+    index-1 of that ring), and channel c and c+6 behave identically."""
+    g = gold("graph_rings.json")["n4"]
+    rings = g["base"]
+    x = np.ones((4, 12 * 4 * 64), dtype=np.int32)
+    rc, out, _, calls = oracle.allreduce([x], rings, (1 << g["channels"]) - 1, "SIMPLE",
+                                         SMALL_BUFF["SIMPLE"], 4, "int32", log_calls=True)
+    assert rc == oracle.OK and (out[0] == 4).all()
+    for c in range(g["channels"]):
+        ring = rings[c % len(rings)]
+        idx, _, _ = oracle.ring_setup(ring)
+        for rank in range(4):
+            mine = [k for k in calls if k["channel_id"] == c and k["rank"] == rank]
+            assert [(k["op"], k["chunk"]) for k in mine[:7]] == oracle.ring_schedule(4, idx[rank])
+
+
+@pytest.mark.parametrize("key", ["n4", "n3", "n2"])
+def test_per_channel_rings_match_closed_form(key):
+    g = gold("graph_rings.json")[key]
+    N = len(g["base"][0])
+    x = _draw("float32", (N, 40009), N)
+    rc, out, _, _ = oracle.allreduce([x], g["base"], (1 << g["channels"]) - 1, "SIMPLE",
+                                     SMALL_BUFF["SIMPLE"], 4, "float32")
+    assert rc == oracle.OK
+    want = cf.allreduce([x], g["base"], (1 << g["channels"]) - 1, "SIMPLE",
+                        SMALL_BUFF["SIMPLE"], 4, "float32")[0]
+    for r in range(N):
+        np.testing.assert_array_equal(out[0][r], want)
+    # rings change the fold order of each channel, so the bits differ from one ring
+    one = cf.allreduce([x], g["base"][0], (1 << g["channels"]) - 1, "SIMPLE",
+                       SMALL_BUFF["SIMPLE"], 4, "float32")[0]
+    if len(g["base"]) > 1:
+        assert not np.array_equal(one, want)
+    for proto in ("LL", "LL128"):
+        rc, out, _, _ = oracle.allreduce([x], g["base"], (1 << g["channels"]) - 1, proto,
+                                         SMALL_BUFF[proto], 4, "float32", sched=1, seed=7)
+        assert rc == oracle.OK
+        np.testing.assert_array_equal(
+            out[0][0], cf.allreduce([x], g["base"], (1 << g["channels"]) - 1, proto,
+                                    SMALL_BUFF[proto], 4, "float32")[0])
