@@ -131,6 +131,22 @@ rar_result_t rar_comm_create(rar_comm_t* comm, int nranks, const int* ring_order
                              uint64_t channel_mask, rar_proto_t proto, size_t buff_size,
                              int chunk_steps, const rar_tuning_t* tuning);
 
+/* As rar_comm_create, with one ring per channel [C12 "GRAPH 重建：N=2 / N=3 /
+ * N=4", "为什么 channels 会重复"]: ring_orders holds `nrings` rings of
+ * `nranks` ranks each, one after the other, every one a permutation.
+ * Channel id c runs ring (c mod nrings), so the base rings repeat over the
+ * channels that follow them (with the six rings of four ranks and 12
+ * channels, channels 6-11 run the rings of channels 0-5).  A channel's ring
+ * sets both its neighbours and the order its elements are summed in, so the
+ * result bits depend on it.  rar_comm_create(..., ring_order, ...) is
+ * nrings = 1.
+ * Errors: as rar_comm_create; RAR_INVALID_ARGUMENT if nrings is outside
+ * [1, 64] or any ring is not a permutation (the message names the ring). */
+rar_result_t rar_comm_create_rings(rar_comm_t* comm, int nranks, int nrings,
+                                   const int* ring_orders, uint64_t channel_mask,
+                                   rar_proto_t proto, size_t buff_size, int chunk_steps,
+                                   const rar_tuning_t* tuning);
+
 /* AllReduce of `count` elements over all virtual ranks [C12; C23 "Ring
  * AllReduce 到 Primitive"]: afterwards every recvbufs[r][i] holds the sum over
  * ranks of sendbufs[r][i], folded in ring order (the rank after the chunk's

@@ -54,25 +54,32 @@ def _stream_handle(stream):
 
 
 class Comm:
-    """A communicator: N virtual ranks on the current device, one ring, a
-    channel mask and a protocol; owns the FIFOs between ring neighbours."""
+    """A communicator: N virtual ranks on the current device, a ring (or one
+    ring per channel: ``ring_order`` a list of rings, channel id c running
+    ring c mod len(rings)), a channel mask and a protocol; owns the FIFOs
+    between ring neighbours."""
 
     def __init__(self, nranks, ring_order, mask, proto="SIMPLE", buff_size=0, chunk_steps=0,
                  lanes=0, waves=0, timeout_us=0, debug_flags=0, launch_mode=0, placement=0,
                  slices_per_chunk=0, direct=0):
         lib = _lib.load()
-        if len(ring_order) != nranks:
-            raise ValueError("ring_order must list every rank once")
+        rings = [list(r) for r in ring_order] if len(ring_order) and \
+            isinstance(ring_order[0], (list, tuple)) else [list(ring_order)]
+        if any(len(r) != nranks for r in rings):
+            raise ValueError("every ring must list every rank once")
         self.nranks = nranks
-        self.ring_order = list(ring_order)
+        self.rings = rings
+        self.ring_order = rings[0]
         self.mask = mask
         self.proto = proto
-        order = (ctypes.c_int * nranks)(*self.ring_order)
+        flat = [r for ring in rings for r in ring]
+        order = (ctypes.c_int * len(flat))(*flat)
         tune = _lib.Tuning(lanes, waves, timeout_us, debug_flags, launch_mode, placement,
                            slices_per_chunk, direct)
         h = ctypes.c_void_p()
-        _lib.check(lib.rar_comm_create(ctypes.byref(h), nranks, order, mask, _lib.PROTO[proto],
-                                       buff_size, chunk_steps, ctypes.byref(tune)))
+        _lib.check(lib.rar_comm_create_rings(ctypes.byref(h), nranks, len(rings), order, mask,
+                                             _lib.PROTO[proto], buff_size, chunk_steps,
+                                             ctypes.byref(tune)))
         self._h = h
 
     @property

@@ -52,6 +52,9 @@ _ip = _c.POINTER(_c.c_int)
 SIGNATURES = [
     ("rar_comm_create", _c.c_int, [_c.POINTER(_c.c_void_p), _c.c_int, _ip, _c.c_uint64, _c.c_int,
                                    _c.c_size_t, _c.c_int, _c.POINTER(Tuning)]),
+    ("rar_comm_create_rings", _c.c_int, [_c.POINTER(_c.c_void_p), _c.c_int, _c.c_int, _ip,
+                                         _c.c_uint64, _c.c_int, _c.c_size_t, _c.c_int,
+                                         _c.POINTER(Tuning)]),
     ("rar_allreduce", _c.c_int, [_c.c_void_p, _vpp, _vpp, _c.c_size_t, _c.c_int, _c.c_int,
                                  _c.c_void_p]),
     ("rar_group_start", _c.c_int, [_c.c_void_p]),

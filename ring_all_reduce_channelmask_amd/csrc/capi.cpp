@@ -8,6 +8,7 @@
 
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -49,8 +50,8 @@ size_t align_to(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct rar_comm {
   int device = 0;
   int nranks = 0;
-  std::vector<int> order;
-  rar::RingInfo ring;
+  std::vector<int> order;             // nrings * nranks, ring after ring
+  int nrings = 1;
   uint64_t mask = 0;
   int C = 0, P = 0, W = 0, grid = 0;
   int proto = 0;
@@ -262,6 +263,13 @@ rar_result_t rar_plan_pieces(int nranks, uint64_t channel_mask, rar_proto_t prot
 rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order, uint64_t channel_mask,
                              rar_proto_t proto, size_t buff_size, int chunk_steps,
                              const rar_tuning_t* tuning) {
+  return rar_comm_create_rings(out, nranks, 1, ring_order, channel_mask, proto, buff_size, chunk_steps,
+                               tuning);
+}
+
+rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, const int* ring_orders,
+                                   uint64_t channel_mask, rar_proto_t proto, size_t buff_size,
+                                   int chunk_steps, const rar_tuning_t* tuning) {
   g_last_error.clear();
   if (!out) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
   *out = nullptr;
@@ -270,8 +278,13 @@ rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order,
   std::string err;
   if (!rar::check_shape(nranks, channel_mask, proto, buff_size, chunk_steps, &err))
     return fail(RAR_INVALID_ARGUMENT, err);
-  rar::RingInfo ring;
-  if (!rar::build_ring(nranks, ring_order, &ring, &err)) return fail(RAR_INVALID_ARGUMENT, err);
+  if (nrings < 1 || nrings > rar::kMaxChannels)
+    return fail(RAR_INVALID_ARGUMENT, "nrings must be in [1, 64]");
+  if (!ring_orders) return fail(RAR_INVALID_ARGUMENT, "ring_order is NULL");
+  std::vector<rar::RingInfo> rings(nrings);
+  for (int k = 0; k < nrings; ++k)
+    if (!rar::build_ring(nranks, ring_orders + (size_t)k * nranks, &rings[k], &err))
+      return fail(RAR_INVALID_ARGUMENT, "ring " + std::to_string(k) + ": " + err);
   rar_tuning_t tune{0, 0, 0, 0, 0, 0, 0, 0};
   if (tuning) tune = *tuning;
   if (tune.lanes_per_channel < 0 || tune.lanes_per_channel > rar::kMaxLanes)
@@ -302,8 +315,8 @@ rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order,
   rar_comm* c = new rar_comm();
   c->device = dev;
   c->nranks = nranks;
-  c->order.assign(ring_order, ring_order + nranks);
-  c->ring = ring;
+  c->order.assign(ring_orders, ring_orders + (size_t)nrings * nranks);
+  c->nrings = nrings;
   c->mask = channel_mask;
   c->C = __builtin_popcountll(channel_mask);
   c->proto = proto;
@@ -387,7 +400,9 @@ rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order,
   if ((r = guard(hipMemcpy(c->d_wgmap, wg.data(), wg.size() * sizeof(uint32_t), hipMemcpyHostToDevice),
                  "hipMemcpy(wgmap)")))
     return r;
-  rar::DevComm hc;
+  // 64 KiB of ring tables: built on the heap, not the stack
+  std::unique_ptr<rar::DevComm> hcp(new rar::DevComm());
+  rar::DevComm& hc = *hcp;
   std::memset(&hc, 0, sizeof(hc));
   hc.hot.n_ranks = nranks;
   hc.hot.n_channels = c->C;
@@ -414,10 +429,14 @@ rar_result_t rar_comm_create(rar_comm_t* out, int nranks, const int* ring_order,
   hc.hot.trace_count = c->d_trace_count;
   hc.hot.placement = c->d_placement;
   hc.hot.wg_of = c->d_wg_of;
-  for (int i = 0; i < nranks; ++i) {
-    hc.ranks[i].index = ring.index[i];
-    hc.ranks[i].prev = ring.prev[i];
-    hc.ranks[i].next = ring.next[i];
+  for (int id = 0; id < rar::kMaxChannels; ++id) {
+    if (!((channel_mask >> id) & 1)) continue;
+    const rar::RingInfo& ring = rings[id % nrings];
+    for (int i = 0; i < nranks; ++i) {
+      hc.ranks[id][i].index = ring.index[i];
+      hc.ranks[id][i].prev = ring.prev[i];
+      hc.ranks[id][i].next = ring.next[i];
+    }
   }
   if ((r = guard(hipMemcpy(c->d_comm, &hc, sizeof(hc), hipMemcpyHostToDevice), "hipMemcpy(comm)")))
     return r;

@@ -106,9 +106,12 @@ struct alignas(16) DevCommHot {
 };
 static_assert(sizeof(DevCommHot) % 16 == 0, "hot fields are copied in 16-byte packs");
 
+// ranks[c][r]: rank r's place on the ring that channel id c runs.  With
+// several base rings, channel id c runs ring c mod nrings, so the rings repeat
+// over the channels that follow them.
 struct alignas(16) DevComm {
   DevCommHot hot;
-  DevRank ranks[kMaxRanks];
+  DevRank ranks[kMaxChannels][kMaxRanks];
 };
 
 // Kernel arguments (by value).

@@ -315,7 +315,6 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
   // into the next rank's receive buffer (no FIFO slot: no credit wait), and
   // the all-gather receivers find their data in their own receive buffer.
   const bool direct_send = cx.direct && (OP == kOpRecvReduceCopySend || OP == kOpRecvCopySend);
-  const bool direct_recv = cx.direct && (OP == kOpRecvCopySend || OP == kOpRecv);
   constexpr int kVec = 16 / sizeof(S);
   const int sps = cx.sps;
   const int64_t step_elems = cx.step_bytes / (int64_t)sizeof(S);
@@ -761,7 +760,7 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.workers = nthreads;
   cx.rank = rank;
   cx.nranks = sh.comm.n_ranks;
-  const DevRank me = comm->ranks[rank];
+  const DevRank me = comm->ranks[sh.channel_id][rank];
   cx.ring_index = me.index;
   cx.next = me.next;
   cx.direct = sh.comm.direct != 0;

@@ -36,7 +36,7 @@ def _rand(dtype, shape, seed, scale=1.0):
 
 def _check_vs_sim(comm, inputs, dtype, buff, cs, in_place=False, sched=0):
     got = run_hip(comm, inputs, dtype, in_place=in_place)
-    rc, want, _, _ = oracle.allreduce(inputs, comm.ring_order, comm.mask, comm.proto, buff, cs,
+    rc, want, _, _ = oracle.allreduce(inputs, comm.rings, comm.mask, comm.proto, buff, cs,
                                       dtype, sched=sched)
     assert rc == oracle.OK
     for w in range(len(inputs)):
@@ -331,3 +331,67 @@ def test_direct_variant_rejected_for_ll():
         with pytest.raises(rar.RarError) as e:
             _comm(nranks=4, ring_order=[0, 1, 2, 3], mask=1, proto=proto, direct=1)
         assert e.value.code == _lib.UNSUPPORTED
+
+
+# ------------------------------------------------- per-channel rings
+def _graph(key):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "graph_rings.json")) as f:
+        return json.load(f)[key]
+
+
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128"])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+@pytest.mark.parametrize("key", ["n4", "n3"])
+def test_per_channel_rings_vs_simulator(proto, dtype, key):
+    """The graph layouts of the course page: every channel id runs its own
+    ring, the base rings repeat over the later channels; the per-channel fold
+    order must match the simulator bit for bit."""
+    g = _graph(key)
+    N = len(g["base"][0])
+    buff = SMALL_BUFF[proto]
+    comm = _comm(nranks=N, ring_order=g["base"], mask=(1 << g["channels"]) - 1, proto=proto,
+                 buff_size=buff, chunk_steps=4 if proto == "SIMPLE" else 0, lanes=2, waves=4)
+    x = _rand(dtype, (N, 90017), 51 + N)
+    _check_vs_sim(comm, [x], dtype, buff, 4)
+    comm.close()
+
+
+def test_per_channel_rings_follow_channel_id_not_dense_index():
+    """With a sparse mask, channel id c (not the c-th active channel) picks
+    ring c mod nrings; mask 0b1010_1010 under three rings runs rings
+    1, 0, 2, 1 on channels 1, 3, 5, 7."""
+    rings = [[0, 1, 2, 3], [0, 3, 2, 1], [0, 2, 1, 3]]
+    buff = SMALL_BUFF["SIMPLE"]
+    comm = _comm(nranks=4, ring_order=rings, mask=0xAA, proto="SIMPLE", buff_size=buff,
+                 lanes=2, waves=4)
+    x = _rand("float32", (4, 70001), 61)
+    got = run_hip(comm, [x], "float32")[0]
+    comm.close()
+    want = cf.allreduce([x], rings, 0xAA, "SIMPLE", buff, 4, "float32")[0]
+    for r in range(4):
+        assert_bits_equal(got[r], want, f"rank {r}")
+    dense = cf.allreduce([x], [rings[(1 + 2 * n) % 3] for n in range(4)] * 16, 0xF, "SIMPLE",
+                         buff, 4, "float32")[0]
+    assert not np.array_equal(dense, cf.allreduce([x], [rings[n % 3] for n in range(4)] * 16,
+                                                  0xF, "SIMPLE", buff, 4, "float32")[0])
+    assert_bits_equal(got[0], dense, "channel ids 1,3,5,7 = rings 1,0,2,1")
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_per_channel_rings_full_size_direct_and_spread(dtype):
+    """The six four-rank rings over 12 channels at the benchmark's 64 MiB
+    size, with the direct all-gather and with the ranks spread over XCDs,
+    every element against the closed form."""
+    g = _graph("n4")
+    count = 16 << 20 if dtype == "float32" else 32 << 20
+    x = _rand(dtype, (4, count), 71)
+    want = cf.allreduce([x], g["base"], 0xFFF, "SIMPLE", 4 << 20, 4, dtype)[0]
+    for kw in (dict(direct=1), dict(placement=1)):
+        comm = _comm(nranks=4, ring_order=g["base"], mask=0xFFF, proto="SIMPLE",
+                     buff_size=4 << 20, chunk_steps=4, lanes=5, waves=8, launch_mode=1, **kw)
+        got = run_hip(comm, [x], dtype)[0]
+        comm.close()
+        for r in range(4):
+            assert_bits_equal(got[r], want, f"{kw} rank {r}")
