@@ -35,11 +35,19 @@ TUNING = {
     "fused_ll": dict(lanes=1, waves=4, launch_mode=1),
     "simple_4k": dict(lanes=1, waves=4, launch_mode=1),
 }
-KERNEL_SRC = os.path.join(ROOT, "ring_all_reduce_channelmask_amd", "csrc", "ring_kernel.hip")
+# Launch shape of the one-shot kernel per workload (performance only).
+ONESHOT_TUNING = {
+    "simple_64m": dict(waves=4, unroll=4),
+    "bf16_n8": dict(waves=4, unroll=4),
+    "int32_n8": dict(waves=8, unroll=2),
+}
+CSRC = os.path.join(ROOT, "ring_all_reduce_channelmask_amd", "csrc")
+KERNEL_SRC = {"ring": os.path.join(CSRC, "ring_kernel.hip"),
+              "oneshot": os.path.join(CSRC, "oneshot_kernel.hip")}
 
 
-def kernel_fingerprint() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_fingerprint(algo="ring") -> str:
+    with open(KERNEL_SRC[algo], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -56,31 +64,38 @@ def cpu_info():
     return model, os.cpu_count()
 
 
-def measured_traffic(key, lanes, waves, alg_bytes):
+def measured_traffic(key, shape, algo="ring"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when there is none for this kernel source and launch shape."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{key}.json")
+    name = f"traffic_{key}.json" if algo == "ring" else f"traffic_{algo}_{key}.json"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_sha") != kernel_fingerprint() or t.get("lanes") != lanes or \
-            t.get("waves") != waves:
+    if t.get("kernel_sha") != kernel_fingerprint(algo):
+        return None
+    if any(t.get(k) != v for k, v in shape.items()):
         return None
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, xs, budget_s=12.0, max_runs=5):
-    """The oracle simulator, as it stands, on the same workload."""
+def cpu_baseline(w, xs, algo="ring", budget_s=12.0, max_runs=5):
+    """The oracle, as it stands, on the same workload: the state-machine
+    simulator for the ring, the written-out fold for the one-shot."""
     import oracle
+    from oracle import oneshot
     times = []
     t_all = time.perf_counter()
     while len(times) < max_runs and (time.perf_counter() - t_all) < budget_s:
         t0 = time.perf_counter()
-        rc, _, _, _ = oracle.allreduce(xs, list(w.ring_order), w.mask, w.proto, w.buff_size,
-                                       w.chunk_steps, w.dtype)
+        if algo == "ring":
+            rc, _, _, _ = oracle.allreduce(xs, list(w.ring_order), w.mask, w.proto, w.buff_size,
+                                           w.chunk_steps, w.dtype)
+            assert rc == oracle.OK
+        else:
+            oneshot.allreduce(xs[0], w.dtype)
         times.append(time.perf_counter() - t0)
-        assert rc == oracle.OK
     return statistics.median(times), len(times)
 
 
@@ -90,6 +105,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="simple_64m")
+    ap.add_argument("--algo", default="ring", choices=["ring", "oneshot"],
+                    help="ring: the ring AllReduce kernel; oneshot: every output folded "
+                         "from all inputs in one hop, on the same workload")
+    ap.add_argument("--workgroups", type=int, default=None, help="oneshot launch shape")
+    ap.add_argument("--unroll", type=int, default=None, help="oneshot launch shape")
     ap.add_argument("--lanes", type=int, default=None)
     ap.add_argument("--waves", type=int, default=None)
     ap.add_argument("--launch-mode", type=int, default=None, choices=[0, 1])
@@ -135,6 +155,9 @@ def main():
         return
 
     w = workloads.WORKLOADS[args.workload]
+    if args.algo == "oneshot":
+        run_oneshot(args, w)
+        return
     tune = dict(TUNING.get(args.workload, {}))
     if args.lanes is not None:
         tune["lanes"] = args.lanes
@@ -213,7 +236,7 @@ def main():
     busbw = metrics.busbw_gbps(M, t_step, N)
     alg_bytes = metrics.algorithmic_bytes(M, N, w.proto, direct=bool(tune.get("direct", 0)))
     achieved = alg_bytes / t_kernel / 1e9
-    traffic = measured_traffic(args.workload, shape["lanes"], shape["waves"], alg_bytes)
+    traffic = measured_traffic(args.workload, {"lanes": shape["lanes"], "waves": shape["waves"]})
     out = {
         "metric": "algBW/busBW GB/s, N-virtual-rank ring AllReduce, 1 MI355X; % HBM peak",
         "value": round(busbw, 3),
@@ -266,6 +289,114 @@ def main():
         }
     print(json.dumps(out), flush=True)
     comm.close()
+
+
+def run_oneshot(args, w):
+    """Time the one-shot AllReduce on workload ``w`` (its first collective)."""
+    import numpy as np
+    import torch
+
+    import ring_all_reduce_channelmask_amd as rar
+    from ring_all_reduce_channelmask_amd import metrics, workloads
+
+    if len(w.counts) != 1:
+        raise SystemExit("the one-shot path runs single collectives; pick another workload")
+    tune = dict(ONESHOT_TUNING.get(w.key, {}))
+    if args.workgroups is not None:
+        tune["workgroups"] = args.workgroups
+    if args.waves is not None:
+        tune["waves"] = args.waves
+    if args.unroll is not None:
+        tune["unroll"] = args.unroll
+    torch.cuda.set_device(0)
+    xs = workloads.inputs_for(w)
+    x = xs[0]
+    N = w.nranks
+
+    def dev(a):
+        if w.dtype == "bfloat16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    sends = [dev(x[r]) for r in range(N)]
+    recvs = [torch.empty_like(t) for t in sends]
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        rar.oneshot_allreduce(sends, recvs, stream=stream, **tune)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        rar.oneshot_allreduce(sends, recvs, stream=stream, **tune)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    t_step = ev[0][0].elapsed_time(ev[-1][1]) * 1e-3 / args.steps
+    t_kernel = statistics.mean(per)
+    ref = recvs[0].view(torch.int16) if w.dtype == "bfloat16" else recvs[0]
+    for t in recvs[1:]:
+        if not torch.equal(t.view(torch.int16) if w.dtype == "bfloat16" else t, ref):
+            raise RuntimeError("ranks disagree")
+    M = w.message_bytes
+    alg_bytes = metrics.oneshot_algorithmic_bytes(M, N)
+    achieved = alg_bytes / t_kernel / 1e9
+    count = w.counts[0]
+    es = 2 if w.dtype == "bfloat16" else 4
+    threads = 64 * (tune.get("waves") or 4)
+    unroll = tune.get("unroll") or 2
+    nvec = count * es // 16
+    shape = {"workgroups": tune.get("workgroups") or min(-(-nvec // (threads * unroll)), 2048),
+             "waves": threads // 64, "unroll": unroll}
+    busbw = metrics.busbw_gbps(M, t_step, N)
+    out = {
+        "metric": "algBW/busBW GB/s, N-virtual-rank one-shot AllReduce, 1 MI355X; % HBM peak",
+        "value": round(busbw, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"float32": "f32", "bfloat16": "bf16", "int32": "int32"}[w.dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.key} one-shot: {N} ranks, {w.dtype}, {M >> 20} MiB/rank",
+            "nranks": N, "elems_per_rank": count, "algorithm": "one-shot",
+            "parallelism": f"{N} virtual ranks on 1 GPU", **shape,
+        },
+        "algbw_GBps": round(metrics.algbw_gbps(M, t_step), 3),
+        "busbw_GBps": round(busbw, 3),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": metrics.HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / metrics.HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(w.key, shape, "oneshot"),
+            "alg_bytes_per_launch": alg_bytes,
+            "kernel_ms": round(t_kernel * 1e3, 4),
+        },
+        "kernel_sha": kernel_fingerprint("oneshot"),
+    }
+    if not args.no_cpu_baseline:
+        t_cpu, runs = cpu_baseline(w, xs, algo="oneshot")
+        model, ncpu = cpu_info()
+        out["cpu_baseline"] = {
+            "value": round(metrics.busbw_gbps(M, t_cpu, N), 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole {w.key} one-shot ({N} ranks x {M >> 20} MiB) in the numpy "
+                      f"oracle, median of {runs} runs, {t_cpu:.3f} s each; host {model}, "
+                      f"{ncpu} CPUs visible",
+        }
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -6,11 +6,13 @@
  * of NCCL_STEPS (8) slots that the library owns.  One call launches one HIP
  * kernel that runs every (rank, channel) of the collective.
  *
- * Sources for the semantics (two public course pages on NCCL):
+ * Sources for the semantics (two public course pages on NCCL, and notes):
  *   [C12] "NCCL 专家课程 12：Ring AllReduce 逐步推导、真实 Ring 与 Channel 并行"
  *         (ring AllReduce step by step, real rings and channel parallelism)
  *   [C23] "NCCL 专家课程 23：Device Kernel、Primitives、Step/Credit 与 LL Flag"
  *         (device kernel, primitives, step/credit and the LL flag)
+ *   [C2]  NCCL notes at cishoon.github.io/posts/ai-infra/nccl (symmetric
+ *         memory, the LSA device API, the one-shot AllReduce)
  *
  * General rules
  *   - All entry points are plain C; nothing throws across the boundary.
@@ -183,6 +185,38 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
                             size_t count, rar_dtype_t dtype, rar_redop_t op,
                             const int* ring_order, rar_proto_t proto, int nchannels,
                             size_t buff_size, int chunk_steps, void* stream);
+
+/* One-shot AllReduce [C2 "5 Symmetric Memory", "6.1 LSA": with every rank's
+ * buffer reachable by plain loads, one kernel finishes the reduction in one
+ * hop instead of the ring's 2(N-1)].  Afterwards every recvbufs[r][i] holds
+ * the fold of sendbufs[0..N-1][i] in user-rank order (rank 0 first): fp32
+ * rounded per add, bf16 accumulated in fp32 and rounded to nearest-even bf16
+ * once, int32 wrapping; identical on every rank.  Each element is folded once
+ * and stored to all N receive buffers, so the launch reads N*count and writes
+ * N*count elements.  Needs no communicator and allocates nothing; one kernel
+ * launch on `stream`, stream-ordered.
+ *   sendbufs, recvbufs  host arrays of `nranks` (2..64) device pointers, each
+ *                       16-byte aligned, copied at call time.  recvbufs[r] ==
+ *                       sendbufs[r] runs in place; no other two buffers may
+ *                       overlap (checked).
+ *   count               elements per rank; 0 launches nothing and does not
+ *                       look at the pointers.
+ *   tuning              NULL for defaults; launch shape only, no result bit
+ *                       depends on it.
+ * Errors: RAR_INVALID_ARGUMENT for a bad count of ranks, dtype, tuning, NULL
+ * or misaligned or overlapping buffers; RAR_UNSUPPORTED for an op other than
+ * RAR_SUM; RAR_HIP_ERROR if the launch fails. */
+typedef struct {
+  int32_t workgroups; /* 0 = auto (enough for one pass, at most 2048)            */
+  int32_t waves;      /* waves per workgroup, 0 = auto (4), at most 8            */
+  int32_t unroll;     /* 16-byte vectors in flight per thread and input:
+                         0 = auto (2), 1, 2 or 4                               */
+  int32_t pad;
+} rar_oneshot_tuning_t;
+
+rar_result_t rar_oneshot_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                   size_t count, rar_dtype_t dtype, rar_redop_t op,
+                                   const rar_oneshot_tuning_t* tuning, void* stream);
 
 /* Watchdog status: RAR_ABORTED if a launch on this communicator timed out in
  * a wait, else RAR_SUCCESS.  Does not synchronize; reflects launches the

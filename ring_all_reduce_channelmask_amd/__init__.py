@@ -16,7 +16,7 @@ import ctypes
 from . import _lib
 from ._lib import RarError  # noqa: F401
 
-__all__ = ["Comm", "ring_allreduce", "ring_info", "plan_pieces", "RarError"]
+__all__ = ["Comm", "ring_allreduce", "oneshot_allreduce", "ring_info", "plan_pieces", "RarError"]
 
 
 def _dtype_name(t):
@@ -153,6 +153,19 @@ def ring_allreduce(sends, recvs, ring_order, proto="SIMPLE", nchannels=1, buff_s
     _lib.check(lib.ring_allreduce(_ptr_array(sends), _ptr_array(recvs), nranks, n,
                                   _lib.DTYPE[dt], _lib.SUM, order, _lib.PROTO[proto], nchannels,
                                   buff_size, chunk_steps, _stream_handle(stream)))
+
+
+def oneshot_allreduce(sends, recvs=None, workgroups=0, waves=0, unroll=0, stream=None):
+    """One-shot AllReduce of N equally sized device tensors (one per virtual
+    rank): every output gets the fold of all inputs in rank order.
+    ``recvs=None`` runs in place."""
+    recvs = sends if recvs is None else recvs
+    nranks = len(sends)
+    n, dt = _check_tensors(sends, recvs, nranks)
+    tune = _lib.OneshotTuning(workgroups, waves, unroll, 0)
+    _lib.check(_lib.load().rar_oneshot_allreduce(_ptr_array(sends), _ptr_array(recvs), nranks, n,
+                                                 _lib.DTYPE[dt], _lib.SUM, ctypes.byref(tune),
+                                                 _stream_handle(stream)))
 
 
 def ring_info(ring_order):

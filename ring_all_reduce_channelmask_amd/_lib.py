@@ -22,6 +22,11 @@ class Tuning(ctypes.Structure):
                 ("slices_per_chunk", ctypes.c_int), ("direct", ctypes.c_int)]
 
 
+class OneshotTuning(ctypes.Structure):
+    _fields_ = [("workgroups", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("unroll", ctypes.c_int32), ("pad", ctypes.c_int32)]
+
+
 class TraceRec(ctypes.Structure):
     _fields_ = [("rank", ctypes.c_int32), ("channel_id", ctypes.c_int32),
                 ("lane", ctypes.c_int32), ("op", ctypes.c_int32), ("chunk", ctypes.c_int32),
@@ -62,6 +67,8 @@ SIGNATURES = [
     ("rar_comm_destroy", _c.c_int, [_c.c_void_p]),
     ("ring_allreduce", _c.c_int, [_vpp, _vpp, _c.c_int, _c.c_size_t, _c.c_int, _c.c_int, _ip,
                                   _c.c_int, _c.c_int, _c.c_size_t, _c.c_int, _c.c_void_p]),
+    ("rar_oneshot_allreduce", _c.c_int, [_vpp, _vpp, _c.c_int, _c.c_size_t, _c.c_int, _c.c_int,
+                                         _c.POINTER(OneshotTuning), _c.c_void_p]),
     ("rar_comm_get_async_error", _c.c_int, [_c.c_void_p]),
     ("rar_comm_query_state", _c.c_int, [_c.c_void_p, _c.POINTER(_c.c_int64), _c.c_size_t,
                                         _c.POINTER(_c.c_size_t)]),

@@ -9,7 +9,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "librar.so")
-SOURCES = ["csrc/ring_kernel.hip", "csrc/plan.cpp", "csrc/capi.cpp"]
+SOURCES = ["csrc/ring_kernel.hip", "csrc/oneshot_kernel.hip", "csrc/plan.cpp", "csrc/capi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -6,6 +6,8 @@
 // works and buffer pointers are copied before the kernel runs.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cstdint>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -19,6 +21,7 @@
 
 namespace rar {
 const void* get_kernel(int dtype, int proto);
+const void* get_oneshot_kernel(int dtype, int unroll);
 }
 
 namespace {
@@ -533,6 +536,67 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
     g_cache[key] = c;
   }
   return rar_allreduce(c, sendbufs, recvbufs, count, dtype, op, stream);
+}
+
+rar_result_t rar_oneshot_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                   size_t count, rar_dtype_t dtype, rar_redop_t op,
+                                   const rar_oneshot_tuning_t* tuning, void* stream) {
+  g_last_error.clear();
+  if (nranks < 2 || nranks > rar::kMaxRanks) return fail(RAR_INVALID_ARGUMENT, "nranks must be in [2, 64]");
+  if (rar_result_t r = check_dtype(dtype)) return r;
+  if (op != RAR_SUM) return fail(RAR_UNSUPPORTED, "only RAR_SUM is implemented");
+  rar_oneshot_tuning_t tune{0, 0, 0, 0};
+  if (tuning) tune = *tuning;
+  if (tune.workgroups < 0 || tune.workgroups > 65536)
+    return fail(RAR_INVALID_ARGUMENT, "workgroups must be in [0, 65536]");
+  if (tune.waves < 0 || tune.waves > 8) return fail(RAR_INVALID_ARGUMENT, "waves must be in [0, 8]");
+  if (tune.unroll != 0 && tune.unroll != 1 && tune.unroll != 2 && tune.unroll != 4)
+    return fail(RAR_INVALID_ARGUMENT, "unroll must be 0, 1, 2 or 4");
+  if (count == 0) return RAR_SUCCESS;  // nothing to move: no launch, pointers not inspected
+  if (!sendbufs || !recvbufs) return fail(RAR_INVALID_ARGUMENT, "sendbufs/recvbufs is NULL");
+  const size_t es = (size_t)rar::elem_size(dtype);
+  if (count > (SIZE_MAX / 2) / es) return fail(RAR_INVALID_ARGUMENT, "count too large");
+  const uintptr_t bytes = count * es;
+  // [lo, hi) of every buffer; a receive buffer may be its own rank's send
+  // buffer (in place) and must not overlap anything else
+  std::vector<std::pair<uintptr_t, int>> ranges;
+  for (int r = 0; r < nranks; ++r) {
+    if (!sendbufs[r] || !recvbufs[r])
+      return fail(RAR_INVALID_ARGUMENT, "buffer of rank " + std::to_string(r) + " is NULL");
+    const uintptr_t s = reinterpret_cast<uintptr_t>(sendbufs[r]);
+    const uintptr_t d = reinterpret_cast<uintptr_t>(recvbufs[r]);
+    if ((s | d) & 15)
+      return fail(RAR_INVALID_ARGUMENT, "buffer of rank " + std::to_string(r) + " is not 16-byte aligned");
+    ranges.push_back({s, r});
+    if (d != s) ranges.push_back({d, r});
+  }
+  std::sort(ranges.begin(), ranges.end());
+  for (size_t i = 1; i < ranges.size(); ++i)
+    if (ranges[i].first - ranges[i - 1].first < bytes)
+      return fail(RAR_INVALID_ARGUMENT, "buffers of ranks " + std::to_string(ranges[i - 1].second) + " and " +
+                                            std::to_string(ranges[i].second) + " overlap");
+
+  rar::OneshotArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int r = 0; r < nranks; ++r) {
+    a.src[r] = sendbufs[r];
+    a.dst[r] = recvbufs[r];
+  }
+  const int64_t vec = 16 / (int64_t)es;
+  a.nranks = nranks;
+  a.nvec = (int64_t)(count / vec);
+  a.tail = (int32_t)(count % vec);
+  const int threads = 64 * (tune.waves ? tune.waves : 4);
+  const int unroll = tune.unroll ? tune.unroll : 2;
+  const int64_t per_pass = (int64_t)threads * unroll;
+  int64_t blocks = tune.workgroups ? tune.workgroups : std::min<int64_t>((a.nvec + per_pass - 1) / per_pass, 2048);
+  if (blocks < 1) blocks = 1;
+  a.vec_per_block = std::max<int64_t>(1, (a.nvec + blocks - 1) / blocks);
+  blocks = std::max<int64_t>(1, (a.nvec + a.vec_per_block - 1) / a.vec_per_block);
+  void* params[] = {&a};
+  RAR_HIP(hipLaunchKernel(rar::get_oneshot_kernel(dtype, unroll), dim3((unsigned)blocks), dim3(threads),
+                          params, 0, reinterpret_cast<hipStream_t>(stream)));
+  return RAR_SUCCESS;
 }
 
 rar_result_t rar_comm_get_async_error(rar_comm_t c) {

@@ -1,0 +1,185 @@
+// oneshot_kernel.hip -- the one-shot AllReduce for gfx950 (MI355X, wave64).
+//
+// With every rank's buffer reachable by plain loads, the reduction finishes
+// in one hop: each element is loaded from all N inputs, folded in registers
+// and stored [C2 "5 Symmetric Memory", "6.1 LSA"; the notes list the one-shot
+// AllReduce among the abilities symmetric memory unlocks].  All N virtual
+// ranks live in this GPU's HBM, so the N identical folds of an element are
+// done once and the result is stored to all N receive buffers: each input is
+// read once and each output written once, 2*N*M bytes in all, the least any
+// AllReduce can move.
+//
+// Fold order is fixed so every rank holds the same bits: user rank 0 first,
+// then ranks 1 .. N-1 in turn.  fp32 adds round per add; bf16 is widened to
+// fp32, accumulated, and rounded to nearest-even bf16 once; int32 wraps.
+//
+//   [C2] "cishoon.github.io/posts/ai-infra/nccl" (NCCL notes)
+#include <hip/hip_runtime.h>
+
+#include "rar_device.h"
+
+namespace rar {
+namespace {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4u ld_nt(const v4u* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_nt(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
+
+__device__ __forceinline__ uint32_t bf16_round(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;  // quiet NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Accumulator of one 16-byte vector: fp32 and int32 fold the words as they
+// are; bf16 widens each of the 8 elements to fp32.
+struct AccF32 {
+  v4f a;
+  __device__ __forceinline__ void init(v4u x) { a = __builtin_bit_cast(v4f, x); }
+  __device__ __forceinline__ void add(v4u x) {
+    const v4f f = __builtin_bit_cast(v4f, x);
+    a.x = a.x + f.x;
+    a.y = a.y + f.y;
+    a.z = a.z + f.z;
+    a.w = a.w + f.w;
+  }
+  __device__ __forceinline__ v4u out() const { return __builtin_bit_cast(v4u, a); }
+  static __device__ __forceinline__ uint32_t elem_init(uint32_t x) { return x; }
+  static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint32_t x) {
+    return __float_as_uint(__uint_as_float(acc) + __uint_as_float(x));
+  }
+  static __device__ __forceinline__ uint32_t elem_out(uint32_t acc) { return acc; }
+  using S = uint32_t;
+};
+struct AccI32 {
+  v4u a;
+  __device__ __forceinline__ void init(v4u x) { a = x; }
+  __device__ __forceinline__ void add(v4u x) { a = a + x; }
+  __device__ __forceinline__ v4u out() const { return a; }
+  static __device__ __forceinline__ uint32_t elem_init(uint32_t x) { return x; }
+  static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint32_t x) { return acc + x; }
+  static __device__ __forceinline__ uint32_t elem_out(uint32_t acc) { return acc; }
+  using S = uint32_t;
+};
+struct AccBF16 {
+  float lo[4], hi[4];  // element 2i in the low half of word i, 2i+1 in the high half
+  __device__ __forceinline__ void init(v4u x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = __uint_as_float(x[i] << 16);
+      hi[i] = __uint_as_float(x[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ void add(v4u x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = lo[i] + __uint_as_float(x[i] << 16);
+      hi[i] = hi[i] + __uint_as_float(x[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ v4u out() const {
+    v4u r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = bf16_round(lo[i]) | (bf16_round(hi[i]) << 16);
+    return r;
+  }
+  static __device__ __forceinline__ uint32_t elem_init(uint16_t x) {
+    return __float_as_uint(__uint_as_float((uint32_t)x << 16));
+  }
+  static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint16_t x) {
+    return __float_as_uint(__uint_as_float(acc) + __uint_as_float((uint32_t)x << 16));
+  }
+  static __device__ __forceinline__ uint16_t elem_out(uint32_t acc) {
+    return (uint16_t)bf16_round(__uint_as_float(acc));
+  }
+  using S = uint16_t;
+};
+
+// Inputs whose loads are issued together: 8 x U 16-byte vectors in flight
+// per thread up to U = 2, 4 x 4 at U = 4 (no register spills at any U).
+template <int U> constexpr int rank_batch() { return U >= 4 ? 4 : 8; }
+
+// Workgroup b folds the contiguous vectors [b*per, (b+1)*per); inside it,
+// consecutive threads take consecutive 16-byte vectors, U of them in flight
+// per thread and input.  The ragged tail (< one vector per rank) is done
+// element by element by the first workgroup.
+template <class Acc, int U>
+__global__ void __launch_bounds__(512) oneshot_kernel(OneshotArgs args) {
+  constexpr int kRankBatch = rank_batch<U>();
+  const int N = args.nranks;
+  const int64_t per = args.vec_per_block;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < args.nvec ? lo + per : args.nvec;
+  const int nthreads = blockDim.x;
+  for (int64_t base = lo + threadIdx.x; base < hi; base += (int64_t)nthreads * U) {
+    Acc acc[U];
+    bool live[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) live[u] = base + (int64_t)u * nthreads < hi;
+    for (int k0 = 0; k0 < N; k0 += kRankBatch) {
+      v4u x[kRankBatch][U];
+#pragma unroll
+      for (int j = 0; j < kRankBatch; ++j) {
+        if (k0 + j < N) {
+          const v4u* src = reinterpret_cast<const v4u*>(args.src[k0 + j]);
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (live[u]) x[j][u] = ld_nt(src + base + (int64_t)u * nthreads);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kRankBatch; ++j) {
+        if (k0 + j < N) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (!live[u]) continue;
+            if (k0 + j == 0) acc[u].init(x[j][u]);
+            else acc[u].add(x[j][u]);
+          }
+        }
+      }
+    }
+    v4u r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (live[u]) r[u] = acc[u].out();
+    for (int k = 0; k < N; ++k) {
+      v4u* dst = reinterpret_cast<v4u*>(args.dst[k]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (live[u]) st_nt(dst + base + (int64_t)u * nthreads, r[u]);
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x < args.tail) {
+    using S = typename Acc::S;
+    const int64_t e = args.nvec * (16 / (int64_t)sizeof(S)) + threadIdx.x;
+    uint32_t a = Acc::elem_init(reinterpret_cast<const S*>(args.src[0])[e]);
+    for (int k = 1; k < N; ++k) a = Acc::elem_add(a, reinterpret_cast<const S*>(args.src[k])[e]);
+    const S v = (S)Acc::elem_out(a);
+    for (int k = 0; k < N; ++k) reinterpret_cast<S*>(args.dst[k])[e] = v;
+  }
+}
+
+template <class Acc>
+const void* pick(int unroll) {
+  switch (unroll) {
+    case 1: return reinterpret_cast<const void*>(&oneshot_kernel<Acc, 1>);
+    case 4: return reinterpret_cast<const void*>(&oneshot_kernel<Acc, 4>);
+    default: return reinterpret_cast<const void*>(&oneshot_kernel<Acc, 2>);
+  }
+}
+
+}  // namespace
+
+const void* get_oneshot_kernel(int dtype, int unroll) {
+  switch (dtype) {
+    case kInt32: return pick<AccI32>(unroll);
+    case kFloat32: return pick<AccF32>(unroll);
+    case kBFloat16: return pick<AccBF16>(unroll);
+  }
+  return nullptr;
+}
+
+}  // namespace rar

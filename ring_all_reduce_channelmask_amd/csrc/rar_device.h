@@ -20,6 +20,17 @@ constexpr int kBatchWorks = 16;      // 16 works x 64 B = a 1024-byte batch
 constexpr uint32_t kIdleWg = 0xFFFFFFFFu;
 
 enum Proto : int32_t { kLL = 0, kLL128 = 1, kSimple = 2 };
+enum Dtype : int32_t { kInt32 = 0, kFloat32 = 1, kBFloat16 = 2 };
+
+// Arguments of the one-shot kernel (by value: at most 64 ranks' pointers).
+struct OneshotArgs {
+  const void* src[kMaxRanks];  // send buffer of every rank
+  void* dst[kMaxRanks];        // receive buffer of every rank
+  int64_t nvec;                // whole 16-byte vectors per rank
+  int64_t vec_per_block;       // contiguous vectors folded by one workgroup
+  int32_t nranks;
+  int32_t tail;                // elements after the last whole vector
+};
 
 // One (collective, channel) piece: what ncclDevWorkColl carries for runRing.
 struct alignas(16) DevWork {

@@ -42,3 +42,9 @@ def algorithmic_bytes(message_bytes: int, nranks: int, proto: str, direct: bool 
     else:
         per_m = 4 + 4 * f + 2 * (nranks - 2) * (2 * f + 1)
     return float(per_m * message_bytes)
+
+
+def oneshot_algorithmic_bytes(message_bytes: int, nranks: int) -> float:
+    """HBM bytes of the one-shot AllReduce with all ranks in one memory: every
+    input read once and every output written once, 2 N M."""
+    return float(2 * nranks * message_bytes)

@@ -1,6 +1,7 @@
 """Host-side checks of the C ABI library: it loads, exports every entry point
 that include/rar.h declares, and its host planner agrees with the oracle and
 with the pages' tables.  No GPU needed (no compute call is made)."""
+import ctypes
 import itertools
 import json
 import os
@@ -128,3 +129,36 @@ def test_package_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "librar.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def _oneshot_raw(send, recv, count, dtype="float32", op=0, tune=None, nranks=None):
+    lib = _lib.load()
+    n = len(send) if nranks is None else nranks
+    s = (ctypes.c_void_p * len(send))(*send)
+    r = (ctypes.c_void_p * len(recv))(*recv)
+    t = _lib.OneshotTuning(*(tune or (0, 0, 0, 0)))
+    return lib.rar_oneshot_allreduce(s, r, n, count, _lib.DTYPE[dtype], op, ctypes.byref(t), None)
+
+
+def test_oneshot_validates_on_the_host():
+    """Bad arguments are rejected before any HIP call; nothing here is ever
+    dereferenced (the addresses are made up and no launch happens)."""
+    A = 1 << 40
+    ok_s, ok_r = [A, A + 4096], [A + 8192, A + 12288]
+    assert _oneshot_raw(ok_s, ok_r, 0) == _lib.SUCCESS                  # count 0: no launch
+    assert _oneshot_raw([0, 0], [0, 0], 0) == _lib.SUCCESS              # pointers not looked at
+    bad = [
+        (dict(send=ok_s, recv=ok_r, count=16, nranks=1), "one rank"),
+        (dict(send=ok_s, recv=ok_r, count=16, nranks=65), "65 ranks"),
+        (dict(send=[A, A + 4], recv=ok_r, count=16), "misaligned"),
+        (dict(send=[A, 0], recv=ok_r, count=16), "NULL"),
+        (dict(send=[A, A + 64], recv=ok_r, count=17), "send buffers overlap (17 fp32 > 64 B)"),
+        (dict(send=ok_s, recv=[A + 8192, A + 8192], count=16), "two ranks share a receive buffer"),
+        (dict(send=ok_s, recv=[A + 4096, A + 12288], count=16), "rank 0 receives into rank 1's input"),
+        (dict(send=ok_s, recv=ok_r, count=16, tune=(0, 9, 0, 0)), "waves"),
+        (dict(send=ok_s, recv=ok_r, count=16, tune=(0, 0, 3, 0)), "unroll"),
+        (dict(send=ok_s, recv=ok_r, count=16, tune=(-1, 0, 0, 0)), "workgroups"),
+    ]
+    for kw, why in bad:
+        assert _oneshot_raw(**kw) == _lib.INVALID_ARGUMENT, why
+    assert _oneshot_raw(ok_s, ok_r, 16, op=1) in (_lib.UNSUPPORTED, _lib.INVALID_ARGUMENT)
