@@ -32,6 +32,7 @@ DTYPE = {"int32": 0, "float32": 1, "bfloat16": 2}
 OPS = {0: "send", 1: "recvReduceSend", 2: "directRecvReduceCopySend",
        3: "directRecvCopySend", 4: "directRecv"}
 OK, DEADLOCK, INVALID, CORRUPT = 0, 1, 2, 3
+RED = {"sum": 0, "prod": 1, "max": 2, "min": 3, "avg": 4}
 FAULTS = {"none": 0, "drop_recv_head": 1, "tail_before_payload": 2, "ll_flag2_missing": 3,
           "ll_constant_flag": 4, "ll128_flag_missing": 5, "ll128_flag_before_data": 6}
 
@@ -144,7 +145,7 @@ def geometry(nranks, mask, proto, buff_size, chunk_steps, dtype, counts):
 
 def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
               in_place=False, slots=8, sched=0, seed=0, drop_recv_head=False,
-              direct=False, log_calls=False):
+              direct=False, log_calls=False, op="sum"):
     """Run the simulator.
 
     ``inputs`` is a list over works of arrays shaped [N, count] holding the raw
@@ -180,7 +181,7 @@ def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
     if log_calls:
         cap = 1 << 20
         log = (Call * cap)()
-    options = (1 if drop_recv_head else 0) | (2 if direct else 0)
+    options = (1 if drop_recv_head else 0) | (2 if direct else 0) | (RED[op] << 8)
     flat = [r for ring in rings for r in ring]
     assert all(len(ring) == N for ring in rings)
     rc = lib().orc_allreduce_rings(N, len(rings), _ints(flat), mask, PROTO[proto], buff_size,

@@ -107,19 +107,43 @@ def _to_f64(x, dtype):
     return x.astype(np.float64)
 
 
-def _hop(acc, x, dtype):
-    """One addition of the ring, rounded to the payload type."""
+def _hop(acc, x, dtype, op="sum"):
+    """One reduction of the ring (the partial ``acc`` with a rank's input
+    ``x``), rounded to the payload type.  max / min keep ``acc`` unless ``x``
+    is strictly larger / smaller; avg adds (its division is the post-op)."""
+    if op in ("max", "min"):
+        a, b = _to_f64(acc, dtype), _to_f64(x, dtype)
+        if dtype == "int32":
+            a, b = acc.astype(np.int64), x.astype(np.int64)
+        take = b > a if op == "max" else b < a
+        return np.where(take, x, acc).astype(acc.dtype)
     if dtype == "int32":
-        # two's-complement wrap modulo 2^32
-        return (acc.astype(np.int32).view(np.uint32) + x.astype(np.int32).view(np.uint32)) \
-            .view(np.int32)
-    s = _to_f64(acc, dtype) + _to_f64(x, dtype)
+        au, xu = acc.astype(np.int32).view(np.uint32), x.astype(np.int32).view(np.uint32)
+        if op == "prod":
+            # low 32 bits of the product
+            return ((au.astype(np.uint64) * xu.astype(np.uint64)) & 0xFFFFFFFF) \
+                .astype(np.uint32).view(np.int32)
+        return (au + xu).view(np.int32)  # two's-complement wrap modulo 2^32
+    a, b = _to_f64(acc, dtype), _to_f64(x, dtype)
+    s = a * b if op == "prod" else a + b  # exact in binary64 for fp32 / bf16 operands
     if dtype == "float32":
         return s.astype(np.float32)
     return _round_bf16(s)
 
 
-def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype):
+def _post_div(v, nranks, dtype):
+    """avg's post-op: the owner's final sum divided by N, rounded once
+    (int32: truncated toward zero)."""
+    if dtype == "int32":
+        q = np.abs(v.astype(np.int64)) // nranks
+        return np.where(v < 0, -q, q).astype(np.int32)
+    q = _to_f64(v, dtype) / nranks
+    if dtype == "float32":
+        return q.astype(np.float32)
+    return _round_bf16(q)
+
+
+def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, op="sum"):
     """Expected output of every rank.
 
     ``inputs``: list over collectives of arrays [N, count] (int32 / float32 /
@@ -149,6 +173,8 @@ def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype):
         cols = np.arange(x.shape[1])
         acc = x[rank_at[ch, (own + 1) % N], cols]
         for k in range(2, N + 1):
-            acc = _hop(acc, x[rank_at[ch, (own + k) % N], cols], dtype)
+            acc = _hop(acc, x[rank_at[ch, (own + k) % N], cols], dtype, op)
+        if op == "avg":
+            acc = _post_div(acc, N, dtype)
         results.append(acc)
     return results

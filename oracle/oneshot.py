@@ -17,6 +17,10 @@ are widened to fp32, accumulated in fp32 exactly as above, and rounded to
 bfloat16 (nearest-even) once at the end -- no FIFO sits between the adds, so
 nothing forces a rounding per hop; int32 wraps modulo 2^32.
 
+Operators: sum; prod (rounded like the sum, low 32 bits for int32); max / min
+(the accumulator is replaced only by a strictly larger / smaller input); avg
+(the sum, then divided by N and rounded once; int32 truncates toward zero).
+
 [C2] "cishoon.github.io/posts/ai-infra/nccl" (NCCL notes: symmetric memory,
 LSA device API, one-shot AllReduce).
 """
@@ -36,26 +40,52 @@ def _add_f32(a, b):
     return (a.astype(np.float64) + b.astype(np.float64)).astype(np.float32)
 
 
-def allreduce(x, dtype):
+def _mul_f32(a, b):
+    """IEEE fp32 product: exact in binary64 (at most 48 significant bits),
+    then rounded once."""
+    return (a.astype(np.float64) * b.astype(np.float64)).astype(np.float32)
+
+
+def _step(acc, v, op, wide):
+    """acc <- acc (op) v.  ``wide`` is the accumulator's numpy type."""
+    if op in ("max", "min"):
+        take = v > acc if op == "max" else v < acc
+        return np.where(take, v, acc)
+    if wide == "int":
+        au, vu = acc.view(np.uint32), v.view(np.uint32)
+        if op == "prod":
+            return ((au.astype(np.uint64) * vu.astype(np.uint64)) & 0xFFFFFFFF) \
+                .astype(np.uint32).view(np.int32)
+        return (au + vu).view(np.int32)  # wraps modulo 2^32
+    return _mul_f32(acc, v) if op == "prod" else _add_f32(acc, v)
+
+
+def allreduce(x, dtype, op="sum"):
     """x: [N, count] array of raw elements (int32 / float32 / uint16 bf16
     bits).  Returns the [count] array every rank must hold."""
     x = np.asarray(x)
     N = x.shape[0]
     if dtype == "int32":
-        acc = x[0].astype(np.int32).view(np.uint32)
+        acc = x[0].astype(np.int32)
         for k in range(1, N):
-            acc = acc + x[k].astype(np.int32).view(np.uint32)  # wraps modulo 2^32
-        return acc.view(np.int32)
+            acc = _step(acc, x[k].astype(np.int32), op, "int")
+        if op == "avg":
+            q = np.abs(acc.astype(np.int64)) // N
+            acc = np.where(acc < 0, -q, q).astype(np.int32)
+        return acc
     if dtype == "float32":
         acc = x[0].astype(np.float32)
         for k in range(1, N):
-            acc = _add_f32(acc, x[k].astype(np.float32))
+            acc = _step(acc, x[k].astype(np.float32), op, "f32")
+        if op == "avg":
+            acc = (acc.astype(np.float64) / N).astype(np.float32)  # 53 >= 2*24+2: one rounding
         return acc
     if dtype == "bfloat16":
         acc = _bf16_to_f32(x[0])
         for k in range(1, N):
-            acc = _add_f32(acc, _bf16_to_f32(x[k]))
-        return _round_bf16(acc.astype(np.float64))
+            acc = _step(acc, _bf16_to_f32(x[k]), op, "f32")
+        a64 = acc.astype(np.float64)
+        return _round_bf16(a64 / N if op == "avg" else a64)
     raise ValueError(dtype)
 
 

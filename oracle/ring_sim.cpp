@@ -59,26 +59,70 @@ uint16_t bf16_round(double v) {
   return (uint16_t)(sign | (uint16_t)(bits >> 16));
 }
 
-void reduce_elem(int dtype, const uint8_t* a, const uint8_t* b, uint8_t* out) {
+/* One reduction of the partial `a` with the own input `b`.  Floating
+ * operands are taken exactly as binary64; a product of two fp32 (48
+ * significant bits) or two bf16 values is exact there, so every result below
+ * is rounded to the payload type once (or, for the sum, with an innocuous
+ * second rounding, as above). */
+double combine(int red, double acc, double x) {
+  switch (red) {
+    case ORC_RED_PROD: return acc * x;
+    case ORC_RED_MAX: return x > acc ? x : acc;
+    case ORC_RED_MIN: return x < acc ? x : acc;
+    default: return acc + x;  // SUM, AVG
+  }
+}
+
+void reduce_elem(int dtype, int red, const uint8_t* a, const uint8_t* b, uint8_t* out) {
   if (dtype == ORC_INT32) {
-    uint32_t x, y;
+    int32_t x, y;
     std::memcpy(&x, a, 4);
     std::memcpy(&y, b, 4);
-    const uint32_t s = x + y;
-    std::memcpy(out, &s, 4);
+    uint32_t r;
+    if (red == ORC_RED_PROD) r = (uint32_t)x * (uint32_t)y;  // low 32 bits
+    else if (red == ORC_RED_MAX) r = (uint32_t)(y > x ? y : x);
+    else if (red == ORC_RED_MIN) r = (uint32_t)(y < x ? y : x);
+    else r = (uint32_t)x + (uint32_t)y;
+    std::memcpy(out, &r, 4);
   } else if (dtype == ORC_FLOAT32) {
     float x, y;
     std::memcpy(&x, a, 4);
     std::memcpy(&y, b, 4);
-    const double s = (double)x + (double)y;
-    const float r = (float)s;
+    const float r = (float)combine(red, (double)x, (double)y);
     std::memcpy(out, &r, 4);
   } else {
     uint16_t x, y;
     std::memcpy(&x, a, 2);
     std::memcpy(&y, b, 2);
-    const uint16_t r = bf16_round(bf16_to_double(x) + bf16_to_double(y));
+    const double dx = bf16_to_double(x), dy = bf16_to_double(y);
+    uint16_t r;
+    if (red == ORC_RED_MAX) r = dy > dx ? y : x;  // max / min pick an operand's bits
+    else if (red == ORC_RED_MIN) r = dy < dx ? y : x;
+    else r = bf16_round(combine(red, dx, dy));
     std::memcpy(out, &r, 2);
+  }
+}
+
+/* The AVG post-op: the owner's final sum divided by N, rounded once to the
+ * payload type (int32: the wrapped sum, truncated toward zero).  binary64
+ * holds the quotient to 53 bits, and 53 >= 2*24 + 2, so rounding it again to
+ * fp32 or bf16 equals rounding the exact quotient. */
+void post_div(int dtype, int nranks, uint8_t* v) {
+  if (dtype == ORC_INT32) {
+    int32_t x;
+    std::memcpy(&x, v, 4);
+    const int32_t q = (int32_t)((int64_t)x / nranks);  // C division truncates toward zero
+    std::memcpy(v, &q, 4);
+  } else if (dtype == ORC_FLOAT32) {
+    float x;
+    std::memcpy(&x, v, 4);
+    const float q = (float)((double)x / (double)nranks);
+    std::memcpy(v, &q, 4);
+  } else {
+    uint16_t x;
+    std::memcpy(&x, v, 2);
+    const uint16_t q = bf16_round(bf16_to_double(x) / (double)nranks);
+    std::memcpy(v, &q, 2);
   }
 }
 
@@ -201,6 +245,7 @@ struct Sim {
   int N = 0, C = 0, proto = 0, dtype = 0, slots = 8, chunk_steps = 4;
   int64_t es = 4, step_bytes = 0, sps = 1;
   bool drop_head = false;
+  int red = ORC_RED_SUM;
   bool direct = false;  // Simple: all-gather half writes into the next rank's receive buffer
   // Ring of each active channel: entry [n * N + rank] for dense channel n.
   // Channel id c follows ring c mod nrings [C12 "为什么 channels 会重复":
@@ -343,7 +388,8 @@ struct Sim {
           break;
         case ORC_OP_RECV_REDUCE_SEND:
         case ORC_OP_RECV_REDUCE_COPY_SEND:
-          reduce_elem(dtype, got.data() + i * es, src + i * es, v);
+          reduce_elem(dtype, red, got.data() + i * es, src + i * es, v);
+          if (u.op == ORC_OP_RECV_REDUCE_COPY_SEND && red == ORC_RED_AVG) post_div(dtype, N, v);
           break;
         default:
           std::memcpy(v, got.data() + i * es, (size_t)es);
@@ -543,6 +589,8 @@ int orc_allreduce_rings(int nranks, int nrings, const int* ring_orders, uint64_t
   sim.drop_head = (options & ORC_OPT_DROP_RECV_HEAD) != 0;
   sim.direct = (options & ORC_OPT_DIRECT) != 0;
   if (sim.direct && proto != ORC_PROTO_SIMPLE) return ORC_INVALID;
+  sim.red = (options >> ORC_OPT_RED_SHIFT) & 15;
+  if (sim.red > ORC_RED_AVG) return ORC_INVALID;
   sim.sendbufs = sendbufs;
   sim.recvbufs = recvbufs;
   sim.stats = stats;

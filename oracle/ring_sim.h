@@ -42,10 +42,23 @@ enum {
 /* Options of orc_allreduce (bit flags). */
 enum {
   ORC_OPT_DROP_RECV_HEAD = 1, /* fault hook: receivers never publish head           */
-  ORC_OPT_DIRECT = 2          /* Simple only: the all-gather half writes straight into
+  ORC_OPT_DIRECT = 2,         /* Simple only: the all-gather half writes straight into
                                  the next rank's receive buffer instead of its FIFO
                                  [C23 "发布顺序与 Fence", direct read/write]        */
+  ORC_OPT_RED_SHIFT = 8       /* bits 8..11: the reduction operator, ORC_RED_*     */
 };
+
+/* Reduction operators [C23 "RunWorkColl 与 Template Dispatch": the kernel is
+ * specialised on a RedOp; C12 "源码步骤三": the fused final step applies the
+ * post-op].  acc is the partial received from the previous rank, x the
+ * rank's own input:
+ *   SUM  acc + x                  PROD  acc * x
+ *   MAX  x if x > acc, else acc   MIN   x if x < acc, else acc
+ *   AVG  acc + x at every hop; the owner's final value is divided by N
+ *        (the post-op) before it is written and forwarded.
+ * Floating results round to the payload type after every operation; int32
+ * wraps modulo 2^32 and AVG divides the wrapped signed sum, truncating. */
+enum { ORC_RED_SUM = 0, ORC_RED_PROD = 1, ORC_RED_MAX = 2, ORC_RED_MIN = 3, ORC_RED_AVG = 4 };
 
 /* Return codes. */
 enum { ORC_OK = 0, ORC_DEADLOCK = 1, ORC_INVALID = 2, ORC_CORRUPT = 3 };

@@ -108,3 +108,58 @@ def test_error_bound(N):
 
 def test_algorithmic_bytes():
     assert oneshot.algorithmic_bytes(64 << 20, 4) == 8 * (64 << 20)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+def test_max_min_equal_numpy(dtype):
+    rng = np.random.default_rng(21)
+    if dtype == "int32":
+        x = rng.integers(-2 ** 31, 2 ** 31, size=(6, 5000)).astype(np.int32)
+        vals = x.astype(np.int64)
+    else:
+        v = rng.standard_normal((6, 5000)).astype(np.float32)
+        x = v if dtype == "float32" else workloads._bf16_bits(v.ravel()).reshape(v.shape)
+        vals = v if dtype == "float32" else (x.astype(np.uint32) << 16).view(np.float32)
+    for op, fn in (("max", np.argmax), ("min", np.argmin)):
+        np.testing.assert_array_equal(oneshot.allreduce(x, dtype, op),
+                                      x[fn(vals, axis=0), np.arange(5000)])
+
+
+def test_prod_hand_values_and_int32_wrap():
+    """fp32: 2 * 0.5 * 4 * 8 = 32 exactly; (1 + 2^-12) * (1 + 2^-12) = 1 + 2^-11
+    + 2^-24 ties to even at 1 + 2^-11.  int32: the low 32 bits of the exact
+    product."""
+    x = np.array([[2.0, 1 + 2 ** -12], [0.5, 1 + 2 ** -12], [4.0, 1.0], [8.0, 1.0]],
+                 dtype=np.float32)
+    got = oneshot.allreduce(x, "float32", "prod")
+    assert got[0] == 32.0 and got[1] == np.float32(1 + 2 ** -11)
+    rng = np.random.default_rng(22)
+    xi = rng.integers(-2 ** 31, 2 ** 31, size=(5, 300)).astype(np.int32)
+    gi = oneshot.allreduce(xi, "int32", "prod")
+    for j in range(300):
+        p = 1
+        for r in range(5):
+            p *= int(xi[r, j])
+        p %= 2 ** 32
+        assert int(gi[j]) == (p - 2 ** 32 if p >= 2 ** 31 else p)
+
+
+def test_bf16_prod_accumulates_in_fp32():
+    """bf16 (1 + 2^-7) squared is 1 + 2^-6 + 2^-14: kept in the fp32
+    accumulator, times 1 it still rounds to 1 + 2^-6 (0x3F82) once at the end;
+    and (1 + 2^-7)^2 * (1 + 2^-7) = 1 + 3*2^-7 + ... rounds to 0x3F83."""
+    one_p = 1 + 2 ** -7
+    x = workloads._bf16_bits(np.array([[one_p, one_p], [one_p, one_p], [1.0, one_p]],
+                                      dtype=np.float32).ravel()).reshape(3, 2)
+    got = oneshot.allreduce(x, "bfloat16", "prod")
+    assert int(got[0]) == 0x3F82 and int(got[1]) == 0x3F83
+
+
+def test_avg_hand_values():
+    xi = np.array([[7, -7], [0, 0], [0, 0], [0, 0]], dtype=np.int32)
+    assert oneshot.allreduce(xi, "int32", "avg").tolist() == [1, -1]
+    xf = np.array([[1.0, 1.0], [2.0, 0.0], [3.0, 0.0]], dtype=np.float32)
+    got = oneshot.allreduce(xf, "float32", "avg")
+    assert got[0] == 2.0 and got.view(np.uint32)[1] == 0x3EAAAAAB
+    xb = workloads._bf16_bits(xf.ravel()).reshape(3, 2)
+    assert oneshot.allreduce(xb, "bfloat16", "avg").tolist() == [0x4000, 0x3EAB]
