@@ -42,7 +42,7 @@ ONESHOT_TUNING = {
     "int32_n8": dict(waves=8, unroll=2),
 }
 CSRC = os.path.join(ROOT, "ring_all_reduce_channelmask_amd", "csrc")
-KERNEL_SRC = {"ring": os.path.join(CSRC, "ring_kernel.hip"),
+KERNEL_SRC = {"ring": os.path.join(CSRC, "ring_kernel.h"),
               "oneshot": os.path.join(CSRC, "oneshot_kernel.hip")}
 
 

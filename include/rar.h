@@ -54,7 +54,16 @@ typedef enum { RAR_PROTO_LL = 0, RAR_PROTO_LL128 = 1, RAR_PROTO_SIMPLE = 2 } rar
  * ties to even) after every ring hop; int32 wraps modulo 2^32. */
 typedef enum { RAR_INT32 = 0, RAR_FLOAT32 = 1, RAR_BFLOAT16 = 2 } rar_dtype_t;
 
-typedef enum { RAR_SUM = 0 } rar_redop_t;
+/* Reduction operators [C23 "RunWorkColl 与 Template Dispatch": the kernel is
+ * specialised on its RedOp; C12 "源码步骤三": the owner's fused final step
+ * applies the post-op].  With acc the partial from the previous rank and x
+ * the rank's own input, one hop computes
+ *   RAR_SUM   acc + x           RAR_PROD  acc * x (int32: low 32 bits)
+ *   RAR_MAX   x if x > acc      RAR_MIN   x if x < acc   (else acc, bits kept)
+ *   RAR_AVG   acc + x; the owner divides its final sum by N (int32:
+ *             truncating toward zero) before writing and forwarding it.
+ * Floating results round to the payload type after every hop. */
+typedef enum { RAR_SUM = 0, RAR_PROD = 1, RAR_MAX = 2, RAR_MIN = 3, RAR_AVG = 4 } rar_redop_t;
 
 typedef struct rar_comm* rar_comm_t;
 
@@ -150,9 +159,10 @@ rar_result_t rar_comm_create_rings(rar_comm_t* comm, int nranks, int nrings,
                                    const rar_tuning_t* tuning);
 
 /* AllReduce of `count` elements over all virtual ranks [C12; C23 "Ring
- * AllReduce 到 Primitive"]: afterwards every recvbufs[r][i] holds the sum over
- * ranks of sendbufs[r][i], folded in ring order (the rank after the chunk's
- * owner starts, the owner adds last), identical on every rank.
+ * AllReduce 到 Primitive"]: afterwards every recvbufs[r][i] holds the
+ * reduction `op` over ranks of sendbufs[r][i], folded in ring order (the rank
+ * after the chunk's owner starts, the owner combines last), identical on
+ * every rank.
  *   sendbufs, recvbufs  host arrays of `nranks` device pointers, each 16-byte
  *                       aligned.  recvbufs[r] == sendbufs[r] runs in place;
  *                       other overlap is not allowed.
@@ -160,7 +170,8 @@ rar_result_t rar_comm_create_rings(rar_comm_t* comm, int nranks, int nrings,
  *                       FIFO steps untouched and does not look at the pointers.
  * Inside rar_group_start/rar_group_end the call is queued instead of launched.
  * Errors: RAR_INVALID_ARGUMENT (NULL or misaligned pointer, bad enum),
- * RAR_UNSUPPORTED (op other than sum), RAR_ABORTED (poisoned communicator),
+ * RAR_UNSUPPORTED (a group mixing dtypes or operators), RAR_ABORTED
+ * (poisoned communicator),
  * RAR_HIP_ERROR (launch failed). */
 rar_result_t rar_allreduce(rar_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                            size_t count, rar_dtype_t dtype, rar_redop_t op, void* stream);
@@ -189,9 +200,10 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
 /* One-shot AllReduce [C2 "5 Symmetric Memory", "6.1 LSA": with every rank's
  * buffer reachable by plain loads, one kernel finishes the reduction in one
  * hop instead of the ring's 2(N-1)].  Afterwards every recvbufs[r][i] holds
- * the fold of sendbufs[0..N-1][i] in user-rank order (rank 0 first): fp32
- * rounded per add, bf16 accumulated in fp32 and rounded to nearest-even bf16
- * once, int32 wrapping; identical on every rank.  Each element is folded once
+ * the fold of sendbufs[0..N-1][i] with `op` in user-rank order (rank 0
+ * first): fp32 rounded per operation, bf16 accumulated in fp32 and rounded to
+ * nearest-even bf16 once, int32 wrapping; RAR_AVG divides the sum by N at the
+ * end; identical on every rank.  Each element is folded once
  * and stored to all N receive buffers, so the launch reads N*count and writes
  * N*count elements.  Needs no communicator and allocates nothing; one kernel
  * launch on `stream`, stream-ordered.
@@ -204,8 +216,8 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
  *   tuning              NULL for defaults; launch shape only, no result bit
  *                       depends on it.
  * Errors: RAR_INVALID_ARGUMENT for a bad count of ranks, dtype, tuning, NULL
- * or misaligned or overlapping buffers; RAR_UNSUPPORTED for an op other than
- * RAR_SUM; RAR_HIP_ERROR if the launch fails. */
+ * or misaligned or overlapping buffers, an unknown op; RAR_HIP_ERROR if the
+ * launch fails. */
 typedef struct {
   int32_t workgroups; /* 0 = auto (enough for one pass, at most 2048)            */
   int32_t waves;      /* waves per workgroup, 0 = auto (4), at most 8            */

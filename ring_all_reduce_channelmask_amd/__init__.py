@@ -86,13 +86,14 @@ class Comm:
     def handle(self):
         return self._h
 
-    def allreduce(self, sends, recvs=None, stream=None):
-        """Sum over ranks; ``recvs=None`` runs in place."""
+    def allreduce(self, sends, recvs=None, stream=None, op="sum"):
+        """Reduce over ranks with ``op`` (sum, prod, max, min, avg);
+        ``recvs=None`` runs in place."""
         recvs = sends if recvs is None else recvs
         n, dt = _check_tensors(sends, recvs, self.nranks)
         lib = _lib.load()
         _lib.check(lib.rar_allreduce(self._h, _ptr_array(sends), _ptr_array(recvs), n,
-                                     _lib.DTYPE[dt], _lib.SUM, _stream_handle(stream)))
+                                     _lib.DTYPE[dt], _lib.RED[op], _stream_handle(stream)))
 
     @contextlib.contextmanager
     def group(self, stream=None):
@@ -144,18 +145,18 @@ class Comm:
 
 
 def ring_allreduce(sends, recvs, ring_order, proto="SIMPLE", nchannels=1, buff_size=0,
-                   chunk_steps=0, stream=None):
+                   chunk_steps=0, stream=None, op="sum"):
     """The pages' problem statement as one call (communicator cached inside)."""
     nranks = len(sends)
     n, dt = _check_tensors(sends, recvs, nranks)
     lib = _lib.load()
     order = (ctypes.c_int * nranks)(*ring_order)
     _lib.check(lib.ring_allreduce(_ptr_array(sends), _ptr_array(recvs), nranks, n,
-                                  _lib.DTYPE[dt], _lib.SUM, order, _lib.PROTO[proto], nchannels,
+                                  _lib.DTYPE[dt], _lib.RED[op], order, _lib.PROTO[proto], nchannels,
                                   buff_size, chunk_steps, _stream_handle(stream)))
 
 
-def oneshot_allreduce(sends, recvs=None, workgroups=0, waves=0, unroll=0, stream=None):
+def oneshot_allreduce(sends, recvs=None, workgroups=0, waves=0, unroll=0, stream=None, op="sum"):
     """One-shot AllReduce of N equally sized device tensors (one per virtual
     rank): every output gets the fold of all inputs in rank order.
     ``recvs=None`` runs in place."""
@@ -164,7 +165,7 @@ def oneshot_allreduce(sends, recvs=None, workgroups=0, waves=0, unroll=0, stream
     n, dt = _check_tensors(sends, recvs, nranks)
     tune = _lib.OneshotTuning(workgroups, waves, unroll, 0)
     _lib.check(_lib.load().rar_oneshot_allreduce(_ptr_array(sends), _ptr_array(recvs), nranks, n,
-                                                 _lib.DTYPE[dt], _lib.SUM, ctypes.byref(tune),
+                                                 _lib.DTYPE[dt], _lib.RED[op], ctypes.byref(tune),
                                                  _stream_handle(stream)))
 
 

@@ -13,6 +13,7 @@ SUCCESS, INVALID_ARGUMENT, UNSUPPORTED, HIP_ERROR, INTERNAL_ERROR, ABORTED = ran
 PROTO = {"LL": 0, "LL128": 1, "SIMPLE": 2}
 DTYPE = {"int32": 0, "float32": 1, "bfloat16": 2}
 SUM = 0
+RED = {"sum": 0, "prod": 1, "max": 2, "min": 3, "avg": 4}
 
 
 class Tuning(ctypes.Structure):

@@ -20,9 +20,21 @@
 #include "rar_device.h"
 
 namespace rar {
-const void* get_kernel(int dtype, int proto);
-const void* get_oneshot_kernel(int dtype, int unroll);
+const void* get_ring_kernel_i32(int proto, int red);
+const void* get_ring_kernel_f32(int proto, int red);
+const void* get_ring_kernel_bf16(int proto, int red);
+const void* get_oneshot_kernel(int dtype, int red, int unroll);
+
+// The ring kernel for (payload type, protocol, reduction operator).
+const void* get_kernel(int dtype, int proto, int red) {
+  switch (dtype) {
+    case kInt32: return get_ring_kernel_i32(proto, red);
+    case kFloat32: return get_ring_kernel_f32(proto, red);
+    case kBFloat16: return get_ring_kernel_bf16(proto, red);
+  }
+  return nullptr;
 }
+}  // namespace rar
 
 namespace {
 
@@ -44,6 +56,7 @@ struct QueuedCall {
   std::vector<void*> send, recv;
   size_t count;
   int dtype;
+  int red;
 };
 
 size_t align_to(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -110,6 +123,11 @@ void release(rar_comm* c) {
 rar_result_t check_dtype(int dtype) {
   if (dtype != RAR_INT32 && dtype != RAR_FLOAT32 && dtype != RAR_BFLOAT16)
     return fail(RAR_INVALID_ARGUMENT, "unknown dtype");
+  return RAR_SUCCESS;
+}
+
+rar_result_t check_op(int op) {
+  if (op < RAR_SUM || op > RAR_AVG) return fail(RAR_INVALID_ARGUMENT, "unknown reduction operator");
   return RAR_SUCCESS;
 }
 
@@ -192,8 +210,8 @@ rar_result_t launch(rar_comm* c, const std::vector<QueuedCall>& calls, hipStream
   args.wg_map = c->d_wgmap;
   args.epoch = ++c->epoch;
   void* params[] = {&args};
-  const void* fn = rar::get_kernel(dtype, c->proto);
-  if (!fn) return fail(RAR_INTERNAL_ERROR, "no kernel for this dtype/protocol");
+  const void* fn = rar::get_kernel(dtype, c->proto, calls.front().red);
+  if (!fn) return fail(RAR_INTERNAL_ERROR, "no kernel for this dtype/protocol/operator");
   if (c->launch_mode == 0)
     RAR_HIP(hipLaunchCooperativeKernel(fn, dim3(c->grid), dim3(c->W * rar::kWaveSize), params, 0, stream));
   else
@@ -336,9 +354,10 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
   c->debug_flags = tune.debug_flags;
 
   // every workgroup must be resident at once: the ranks wait on each other
-  for (int dt = 0; dt < 3; ++dt) {
+  for (int k = 0; k < 3 * rar::kNumRed; ++k) {
+    const int dt = k / rar::kNumRed, red = k % rar::kNumRed;
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rar::get_kernel(dt, proto),
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rar::get_kernel(dt, proto, red),
                                                                 c->W * rar::kWaveSize, 0);
     if (e != hipSuccess) {
       release(c);
@@ -468,9 +487,9 @@ rar_result_t rar_allreduce(rar_comm_t c, const void* const* sendbufs, void* cons
   g_last_error.clear();
   if (!c) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
   if (rar_result_t r = check_dtype(dtype)) return r;
-  if (op != RAR_SUM) return fail(RAR_UNSUPPORTED, "only RAR_SUM is implemented");
-  if (c->in_group && !c->queue.empty() && c->queue.front().dtype != dtype)
-    return fail(RAR_UNSUPPORTED, "all AllReduces of a group must share one dtype");
+  if (rar_result_t r = check_op(op)) return r;
+  if (c->in_group && !c->queue.empty() && (c->queue.front().dtype != dtype || c->queue.front().red != op))
+    return fail(RAR_UNSUPPORTED, "all AllReduces of a group must share one dtype and operator");
   // nothing to move: no launch, no step advance, pointers are not looked at
   if (count == 0) return RAR_SUCCESS;
   if (rar_result_t r = check_buffers(c, sendbufs, recvbufs)) return r;
@@ -480,6 +499,7 @@ rar_result_t rar_allreduce(rar_comm_t c, const void* const* sendbufs, void* cons
   q.recv.assign(recvbufs, recvbufs + c->nranks);
   q.count = count;
   q.dtype = dtype;
+  q.red = op;
   if (c->in_group) {
     c->queue.push_back(std::move(q));
     return RAR_SUCCESS;
@@ -544,7 +564,7 @@ rar_result_t rar_oneshot_allreduce(const void* const* sendbufs, void* const* rec
   g_last_error.clear();
   if (nranks < 2 || nranks > rar::kMaxRanks) return fail(RAR_INVALID_ARGUMENT, "nranks must be in [2, 64]");
   if (rar_result_t r = check_dtype(dtype)) return r;
-  if (op != RAR_SUM) return fail(RAR_UNSUPPORTED, "only RAR_SUM is implemented");
+  if (rar_result_t r = check_op(op)) return r;
   rar_oneshot_tuning_t tune{0, 0, 0, 0};
   if (tuning) tune = *tuning;
   if (tune.workgroups < 0 || tune.workgroups > 65536)
@@ -594,7 +614,7 @@ rar_result_t rar_oneshot_allreduce(const void* const* sendbufs, void* const* rec
   a.vec_per_block = std::max<int64_t>(1, (a.nvec + blocks - 1) / blocks);
   blocks = std::max<int64_t>(1, (a.nvec + a.vec_per_block - 1) / a.vec_per_block);
   void* params[] = {&a};
-  RAR_HIP(hipLaunchKernel(rar::get_oneshot_kernel(dtype, unroll), dim3((unsigned)blocks), dim3(threads),
+  RAR_HIP(hipLaunchKernel(rar::get_oneshot_kernel(dtype, op, unroll), dim3((unsigned)blocks), dim3(threads),
                           params, 0, reinterpret_cast<hipStream_t>(stream)));
   return RAR_SUCCESS;
 }

@@ -10,7 +10,7 @@
 // AllReduce can move.
 //
 // Fold order is fixed so every rank holds the same bits: user rank 0 first,
-// then ranks 1 .. N-1 in turn.  fp32 adds round per add; bf16 is widened to
+// then ranks 1 .. N-1 in turn.  fp32 rounds per operation; bf16 is widened to
 // fp32, accumulated, and rounded to nearest-even bf16 once; int32 wraps.
 //
 //   [C2] "cishoon.github.io/posts/ai-infra/nccl" (NCCL notes)
@@ -22,7 +22,6 @@ namespace rar {
 namespace {
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4u ld_nt(const v4u* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_nt(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
@@ -33,37 +32,77 @@ __device__ __forceinline__ uint32_t bf16_round(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// One step of the fold, acc <- acc (op) x, in fp32 [prod and sum round per
+// operation; max / min keep acc unless x is strictly larger / smaller].
+template <int R>
+__device__ __forceinline__ float red_f(float a, float b) {
+  if constexpr (R == kRedProd) return a * b;
+  else if constexpr (R == kRedMax) return b > a ? b : a;
+  else if constexpr (R == kRedMin) return b < a ? b : a;
+  else return a + b;
+}
+template <int R>
+__device__ __forceinline__ uint32_t red_i(uint32_t a, uint32_t b) {
+  if constexpr (R == kRedProd) return a * b;  // low 32 bits
+  else if constexpr (R == kRedMax) return (int32_t)b > (int32_t)a ? b : a;
+  else if constexpr (R == kRedMin) return (int32_t)b < (int32_t)a ? b : a;
+  else return a + b;  // wraps
+}
+
 // Accumulator of one 16-byte vector: fp32 and int32 fold the words as they
-// are; bf16 widens each of the 8 elements to fp32.
+// are; bf16 widens each of the 8 elements to fp32 (exact) and rounds once in
+// out().  avg divides the final sum by N there (int32: truncating).
+template <int R>
 struct AccF32 {
-  v4f a;
-  __device__ __forceinline__ void init(v4u x) { a = __builtin_bit_cast(v4f, x); }
-  __device__ __forceinline__ void add(v4u x) {
-    const v4f f = __builtin_bit_cast(v4f, x);
-    a.x = a.x + f.x;
-    a.y = a.y + f.y;
-    a.z = a.z + f.z;
-    a.w = a.w + f.w;
+  using S = uint32_t;
+  float a[4];
+  __device__ __forceinline__ void init(v4u x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = __uint_as_float(x[i]);
   }
-  __device__ __forceinline__ v4u out() const { return __builtin_bit_cast(v4u, a); }
+  __device__ __forceinline__ void add(v4u x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = red_f<R>(a[i], __uint_as_float(x[i]));
+  }
+  __device__ __forceinline__ v4u out(int n) const {
+    v4u r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(R == kRedAvg ? a[i] / (float)n : a[i]);
+    return r;
+  }
   static __device__ __forceinline__ uint32_t elem_init(uint32_t x) { return x; }
   static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint32_t x) {
-    return __float_as_uint(__uint_as_float(acc) + __uint_as_float(x));
+    return __float_as_uint(red_f<R>(__uint_as_float(acc), __uint_as_float(x)));
   }
-  static __device__ __forceinline__ uint32_t elem_out(uint32_t acc) { return acc; }
-  using S = uint32_t;
+  static __device__ __forceinline__ uint32_t elem_out(uint32_t acc, int n) {
+    return R == kRedAvg ? __float_as_uint(__uint_as_float(acc) / (float)n) : acc;
+  }
 };
+template <int R>
 struct AccI32 {
+  using S = uint32_t;
   v4u a;
   __device__ __forceinline__ void init(v4u x) { a = x; }
-  __device__ __forceinline__ void add(v4u x) { a = a + x; }
-  __device__ __forceinline__ v4u out() const { return a; }
+  __device__ __forceinline__ void add(v4u x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = red_i<R>(a[i], x[i]);
+  }
+  __device__ __forceinline__ v4u out(int n) const {
+    if constexpr (R != kRedAvg) return a;
+    v4u r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)((int32_t)a[i] / n);
+    return r;
+  }
   static __device__ __forceinline__ uint32_t elem_init(uint32_t x) { return x; }
-  static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint32_t x) { return acc + x; }
-  static __device__ __forceinline__ uint32_t elem_out(uint32_t acc) { return acc; }
-  using S = uint32_t;
+  static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint32_t x) { return red_i<R>(acc, x); }
+  static __device__ __forceinline__ uint32_t elem_out(uint32_t acc, int n) {
+    return R == kRedAvg ? (uint32_t)((int32_t)acc / n) : acc;
+  }
 };
+template <int R>
 struct AccBF16 {
+  using S = uint16_t;
   float lo[4], hi[4];  // element 2i in the low half of word i, 2i+1 in the high half
   __device__ __forceinline__ void init(v4u x) {
 #pragma unroll
@@ -75,26 +114,30 @@ struct AccBF16 {
   __device__ __forceinline__ void add(v4u x) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lo[i] = lo[i] + __uint_as_float(x[i] << 16);
-      hi[i] = hi[i] + __uint_as_float(x[i] & 0xffff0000u);
+      lo[i] = red_f<R>(lo[i], __uint_as_float(x[i] << 16));
+      hi[i] = red_f<R>(hi[i], __uint_as_float(x[i] & 0xffff0000u));
     }
   }
-  __device__ __forceinline__ v4u out() const {
+  __device__ __forceinline__ v4u out(int n) const {
     v4u r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = bf16_round(lo[i]) | (bf16_round(hi[i]) << 16);
+    for (int i = 0; i < 4; ++i) {
+      const float l = R == kRedAvg ? lo[i] / (float)n : lo[i];
+      const float h = R == kRedAvg ? hi[i] / (float)n : hi[i];
+      r[i] = bf16_round(l) | (bf16_round(h) << 16);
+    }
     return r;
   }
   static __device__ __forceinline__ uint32_t elem_init(uint16_t x) {
     return __float_as_uint(__uint_as_float((uint32_t)x << 16));
   }
   static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint16_t x) {
-    return __float_as_uint(__uint_as_float(acc) + __uint_as_float((uint32_t)x << 16));
+    return __float_as_uint(red_f<R>(__uint_as_float(acc), __uint_as_float((uint32_t)x << 16)));
   }
-  static __device__ __forceinline__ uint16_t elem_out(uint32_t acc) {
-    return (uint16_t)bf16_round(__uint_as_float(acc));
+  static __device__ __forceinline__ uint16_t elem_out(uint32_t acc, int n) {
+    const float f = __uint_as_float(acc);
+    return (uint16_t)bf16_round(R == kRedAvg ? f / (float)n : f);
   }
-  using S = uint16_t;
 };
 
 // Inputs whose loads are issued together: 8 x U 16-byte vectors in flight
@@ -144,7 +187,7 @@ __global__ void __launch_bounds__(512) oneshot_kernel(OneshotArgs args) {
     v4u r[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (live[u]) r[u] = acc[u].out();
+      if (live[u]) r[u] = acc[u].out(N);
     for (int k = 0; k < N; ++k) {
       v4u* dst = reinterpret_cast<v4u*>(args.dst[k]);
 #pragma unroll
@@ -157,13 +200,13 @@ __global__ void __launch_bounds__(512) oneshot_kernel(OneshotArgs args) {
     const int64_t e = args.nvec * (16 / (int64_t)sizeof(S)) + threadIdx.x;
     uint32_t a = Acc::elem_init(reinterpret_cast<const S*>(args.src[0])[e]);
     for (int k = 1; k < N; ++k) a = Acc::elem_add(a, reinterpret_cast<const S*>(args.src[k])[e]);
-    const S v = (S)Acc::elem_out(a);
+    const S v = (S)Acc::elem_out(a, N);
     for (int k = 0; k < N; ++k) reinterpret_cast<S*>(args.dst[k])[e] = v;
   }
 }
 
 template <class Acc>
-const void* pick(int unroll) {
+const void* pick_unroll(int unroll) {
   switch (unroll) {
     case 1: return reinterpret_cast<const void*>(&oneshot_kernel<Acc, 1>);
     case 4: return reinterpret_cast<const void*>(&oneshot_kernel<Acc, 4>);
@@ -171,13 +214,25 @@ const void* pick(int unroll) {
   }
 }
 
+template <template <int> class Acc>
+const void* pick(int red, int unroll) {
+  switch (red) {
+    case kRedSum: return pick_unroll<Acc<kRedSum>>(unroll);
+    case kRedProd: return pick_unroll<Acc<kRedProd>>(unroll);
+    case kRedMax: return pick_unroll<Acc<kRedMax>>(unroll);
+    case kRedMin: return pick_unroll<Acc<kRedMin>>(unroll);
+    case kRedAvg: return pick_unroll<Acc<kRedAvg>>(unroll);
+  }
+  return nullptr;
+}
+
 }  // namespace
 
-const void* get_oneshot_kernel(int dtype, int unroll) {
+const void* get_oneshot_kernel(int dtype, int red, int unroll) {
   switch (dtype) {
-    case kInt32: return pick<AccI32>(unroll);
-    case kFloat32: return pick<AccF32>(unroll);
-    case kBFloat16: return pick<AccBF16>(unroll);
+    case kInt32: return pick<AccI32>(red, unroll);
+    case kFloat32: return pick<AccF32>(red, unroll);
+    case kBFloat16: return pick<AccBF16>(red, unroll);
   }
   return nullptr;
 }

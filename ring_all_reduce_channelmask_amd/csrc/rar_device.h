@@ -21,6 +21,8 @@ constexpr uint32_t kIdleWg = 0xFFFFFFFFu;
 
 enum Proto : int32_t { kLL = 0, kLL128 = 1, kSimple = 2 };
 enum Dtype : int32_t { kInt32 = 0, kFloat32 = 1, kBFloat16 = 2 };
+enum Red : int32_t { kRedSum = 0, kRedProd = 1, kRedMax = 2, kRedMin = 3, kRedAvg = 4 };
+constexpr int kNumRed = 5;
 
 // Arguments of the one-shot kernel (by value: at most 64 ranks' pointers).
 struct OneshotArgs {

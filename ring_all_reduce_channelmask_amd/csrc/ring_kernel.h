@@ -1,4 +1,6 @@
-// ring_kernel.hip -- the ring AllReduce device path for gfx950 (MI355X, wave64).
+// ring_kernel.h -- the ring AllReduce device path for gfx950 (MI355X, wave64).
+//
+// Device templates only; ring_kernel_{i32,f32,bf16}.hip instantiate them.
 //
 // One cooperative launch runs every virtual rank.  Workgroup = (rank r, dense
 // channel n, lane p).  The lanes of a channel split every slice (Simple) or
@@ -10,6 +12,8 @@
 //   [C12] "NCCL 专家课程 12：Ring AllReduce 逐步推导、真实 Ring 与 Channel 并行"
 // Memory ordering uses HIP's scoped atomics: agent scope (all XCDs of this
 // GPU) is the widest observer set, since every rank lives on this device.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include "rar_device.h"
@@ -46,47 +50,95 @@ __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)"
 
 // ---------------------------------------------------------------- arithmetic
 // A 16-byte vector is four 32-bit words; each word holds one fp32 / int32 or
-// two bf16.  bf16 sums are formed in fp32 (exact for the operands' product
-// of two bf16 values' alignment) and rounded to nearest-even bf16 per hop.
+// two bf16.  The kernel is specialised on the payload type and the reduction
+// operator [C23 "RunWorkColl 与 Template Dispatch"].  red(acc, x) combines
+// the partial from the previous rank with the own input:
+//   sum / avg  acc + x          prod  acc * x
+//   max        x if x > acc     min   x if x < acc   (else acc, bits kept)
+// bf16 sums and products are formed in fp32 (exact for two bf16 operands)
+// and rounded to nearest-even bf16 per hop; int32 wraps.  avg's post-op
+// divides the owner's final sum by N, rounded once [C12 "源码步骤三"].
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;  // quiet NaN
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+template <int R>
+__device__ __forceinline__ float red_f(float a, float b) {
+  if constexpr (R == kRedProd) return a * b;
+  else if constexpr (R == kRedMax) return b > a ? b : a;
+  else if constexpr (R == kRedMin) return b < a ? b : a;
+  else return a + b;
+}
+
+template <int R>
 struct TyF32 {
   using S = uint32_t;
-  static __device__ __forceinline__ uint32_t add_word(uint32_t a, uint32_t b) {
-    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  static constexpr bool kPost = R == kRedAvg;
+  static __device__ __forceinline__ uint32_t red_word(uint32_t a, uint32_t b) {
+    return __float_as_uint(red_f<R>(__uint_as_float(a), __uint_as_float(b)));
   }
-  static __device__ __forceinline__ S add_elem(S a, S b) { return add_word(a, b); }
+  static __device__ __forceinline__ S red_elem(S a, S b) { return red_word(a, b); }
+  static __device__ __forceinline__ uint32_t post_word(uint32_t a, int n) {
+    return __float_as_uint(__uint_as_float(a) / (float)n);  // IEEE division, nearest-even
+  }
+  static __device__ __forceinline__ S post_elem(S a, int n) { return post_word(a, n); }
 };
+template <int R>
 struct TyI32 {
   using S = uint32_t;
-  static __device__ __forceinline__ uint32_t add_word(uint32_t a, uint32_t b) { return a + b; }
-  static __device__ __forceinline__ S add_elem(S a, S b) { return a + b; }
+  static constexpr bool kPost = R == kRedAvg;
+  static __device__ __forceinline__ uint32_t red_word(uint32_t a, uint32_t b) {
+    if constexpr (R == kRedProd) return a * b;  // low 32 bits
+    else if constexpr (R == kRedMax) return (int32_t)b > (int32_t)a ? b : a;
+    else if constexpr (R == kRedMin) return (int32_t)b < (int32_t)a ? b : a;
+    else return a + b;
+  }
+  static __device__ __forceinline__ S red_elem(S a, S b) { return red_word(a, b); }
+  static __device__ __forceinline__ uint32_t post_word(uint32_t a, int n) {
+    return (uint32_t)((int32_t)a / n);  // truncates toward zero
+  }
+  static __device__ __forceinline__ S post_elem(S a, int n) { return post_word(a, n); }
 };
+template <int R>
 struct TyBF16 {
   using S = uint16_t;
-  static __device__ __forceinline__ uint16_t add_elem(uint16_t a, uint16_t b) {
-    return (uint16_t)bf16_rne(__uint_as_float((uint32_t)a << 16) + __uint_as_float((uint32_t)b << 16));
+  static constexpr bool kPost = R == kRedAvg;
+  static __device__ __forceinline__ uint32_t red_half(uint32_t a, uint32_t b) {  // bf16 in the low 16 bits
+    const float fa = __uint_as_float(a << 16), fb = __uint_as_float(b << 16);
+    if constexpr (R == kRedMax) return fb > fa ? b : a;
+    else if constexpr (R == kRedMin) return fb < fa ? b : a;
+    else return bf16_rne(red_f<R>(fa, fb));
   }
-  static __device__ __forceinline__ uint32_t add_word(uint32_t a, uint32_t b) {
-    const uint32_t lo = bf16_rne(__uint_as_float(a << 16) + __uint_as_float(b << 16));
-    const uint32_t hi = bf16_rne(__uint_as_float(a & 0xffff0000u) + __uint_as_float(b & 0xffff0000u));
-    return lo | (hi << 16);
+  static __device__ __forceinline__ uint16_t red_elem(uint16_t a, uint16_t b) {
+    return (uint16_t)red_half(a, b);
+  }
+  static __device__ __forceinline__ uint32_t red_word(uint32_t a, uint32_t b) {
+    if constexpr (R == kRedSum || R == kRedAvg) {
+      const uint32_t lo = bf16_rne(__uint_as_float(a << 16) + __uint_as_float(b << 16));
+      const uint32_t hi = bf16_rne(__uint_as_float(a & 0xffff0000u) + __uint_as_float(b & 0xffff0000u));
+      return lo | (hi << 16);
+    } else {
+      return (red_half(a & 0xffffu, b & 0xffffu) & 0xffffu) | (red_half(a >> 16, b >> 16) << 16);
+    }
+  }
+  static __device__ __forceinline__ uint16_t post_elem(uint16_t a, int n) {
+    return (uint16_t)bf16_rne(__uint_as_float((uint32_t)a << 16) / (float)n);
+  }
+  static __device__ __forceinline__ uint32_t post_word(uint32_t a, int n) {
+    return (uint32_t)post_elem((uint16_t)(a & 0xffffu), n) | ((uint32_t)post_elem((uint16_t)(a >> 16), n) << 16);
   }
 };
 
 template <class Ty>
-__device__ __forceinline__ uint4 add16(uint4 a, uint4 b) {
-  return make_uint4(Ty::add_word(a.x, b.x), Ty::add_word(a.y, b.y), Ty::add_word(a.z, b.z),
-                    Ty::add_word(a.w, b.w));
+__device__ __forceinline__ uint64_t red8(uint64_t a, uint64_t b) {
+  return (uint64_t)Ty::red_word((uint32_t)a, (uint32_t)b) |
+         ((uint64_t)Ty::red_word((uint32_t)(a >> 32), (uint32_t)(b >> 32)) << 32);
 }
 template <class Ty>
-__device__ __forceinline__ uint64_t add8(uint64_t a, uint64_t b) {
-  return (uint64_t)Ty::add_word((uint32_t)a, (uint32_t)b) |
-         ((uint64_t)Ty::add_word((uint32_t)(a >> 32), (uint32_t)(b >> 32)) << 32);
+__device__ __forceinline__ uint64_t post8(uint64_t a, int n) {
+  return (uint64_t)Ty::post_word((uint32_t)a, n) | ((uint64_t)Ty::post_word((uint32_t)(a >> 32), n) << 32);
 }
 
 template <int OP> struct OpTraits {
@@ -230,12 +282,21 @@ __device__ __forceinline__ bool wait_credit(Ctx& cx, uint64_t n) {
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 template <class Ty>
-__device__ __forceinline__ v4u add16v(v4u a, v4u b) {
+__device__ __forceinline__ v4u red16(v4u a, v4u b) {
   v4u r;
-  r.x = Ty::add_word(a.x, b.x);
-  r.y = Ty::add_word(a.y, b.y);
-  r.z = Ty::add_word(a.z, b.z);
-  r.w = Ty::add_word(a.w, b.w);
+  r.x = Ty::red_word(a.x, b.x);
+  r.y = Ty::red_word(a.y, b.y);
+  r.z = Ty::red_word(a.z, b.z);
+  r.w = Ty::red_word(a.w, b.w);
+  return r;
+}
+template <class Ty>
+__device__ __forceinline__ v4u post16(v4u a, int n) {
+  v4u r;
+  r.x = Ty::post_word(a.x, n);
+  r.y = Ty::post_word(a.y, n);
+  r.z = Ty::post_word(a.z, n);
+  r.w = Ty::post_word(a.w, n);
   return r;
 }
 template <bool kNt>
@@ -251,14 +312,17 @@ __device__ __forceinline__ void st16(v4u* p, v4u v) {
 
 // reduceCopy over n elements with 16-byte vectors, RAR_UNROLL in flight per
 // thread and source; consecutive threads touch consecutive 16-byte vectors.
+// The call that combines a partial with the own input and writes the output
+// is the owner's final step, which also applies the post-op (divisor n_post).
 // `fin` / `fout` are FIFO slots, or user buffers in the direct variants
 // (kUserIn / kUserOut), which then take the user-buffer access hint.
 template <class Ty, bool kRecv, bool kSrc, bool kDst, bool kSend, bool kUserIn = false,
           bool kUserOut = false>
 __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typename Ty::S* src,
                                             typename Ty::S* dst, typename Ty::S* fout, int64_t n,
-                                            int tid, int nthr) {
+                                            int tid, int nthr, int n_post) {
   using S = typename Ty::S;
+  constexpr bool kPost = kRecv && kSrc && kDst && Ty::kPost;
   constexpr int kVec = 16 / sizeof(S);
   constexpr int kUnroll = RAR_UNROLL;
   constexpr bool kNu = RAR_NT_USER != 0;
@@ -279,7 +343,8 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const v4u r = (kRecv && kSrc) ? add16v<Ty>(a[u], b[u]) : (kRecv ? a[u] : b[u]);
+      v4u r = (kRecv && kSrc) ? red16<Ty>(a[u], b[u]) : (kRecv ? a[u] : b[u]);
+      if constexpr (kPost) r = post16<Ty>(r, n_post);
       if (kDst) st16<kNu>(vdst + i + (int64_t)u * nthr, r);
       if (kSend) st16<kNo>(vout + i + (int64_t)u * nthr, r);
     }
@@ -288,7 +353,8 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
     v4u a = {0, 0, 0, 0}, b = a;
     if (kRecv) a = ld16<kNi>(vin + i);
     if (kSrc) b = ld16<kNu>(vsrc + i);
-    const v4u r = (kRecv && kSrc) ? add16v<Ty>(a, b) : (kRecv ? a : b);
+    v4u r = (kRecv && kSrc) ? red16<Ty>(a, b) : (kRecv ? a : b);
+    if constexpr (kPost) r = post16<Ty>(r, n_post);
     if (kDst) st16<kNu>(vdst + i, r);
     if (kSend) st16<kNo>(vout + i, r);
   }
@@ -296,7 +362,8 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
     S a = 0, b = 0;
     if (kRecv) a = fin[e];
     if (kSrc) b = src[e];
-    const S r = (kRecv && kSrc) ? Ty::add_elem(a, b) : (kRecv ? a : b);
+    S r = (kRecv && kSrc) ? Ty::red_elem(a, b) : (kRecv ? a : b);
+    if constexpr (kPost) r = Ty::post_elem(r, n_post);
     if (kDst) dst[e] = r;
     if (kSend) fout[e] = r;
   }
@@ -352,16 +419,16 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
       const int64_t e0 = s_off + lo;
       if (!cx.direct || OP == kOpSend || OP == kOpRecvReduceSend) {
         reduce_copy<Ty, O::kRecv, O::kSrc, O::kDst, O::kSend>(fin, src + e0, dst + e0, fout, hi - lo,
-                                                               cx.tid, cx.workers);
+                                                               cx.tid, cx.workers, cx.nranks);
       } else if (OP == kOpRecvReduceCopySend) {
         // FIFO partial + own input -> own output and the next rank's output
         reduce_copy<Ty, true, true, true, true, false, true>(fin, src + e0, dst + e0, next_dst + e0,
-                                                             hi - lo, cx.tid, cx.workers);
+                                                             hi - lo, cx.tid, cx.workers, cx.nranks);
       } else if (OP == kOpRecvCopySend) {
         // already in the own output (written by prev) -> the next rank's output
         reduce_copy<Ty, true, false, false, true, true, true>(dst + e0, src + e0, dst + e0,
                                                               next_dst + e0, hi - lo, cx.tid,
-                                                              cx.workers);
+                                                              cx.workers, cx.nranks);
       }
       // direct recv: the data is already in place
     }
@@ -473,7 +540,8 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
         const int64_t j = j0 + (int64_t)u * stride;
         if (j >= hi) continue;
         const uint64_t in = (a[u] & 0xffffffffull) | (b[u] << 32);
-        const uint64_t v = (O::kRecv && O::kSrc) ? add8<Ty>(in, own[u]) : (O::kRecv ? in : own[u]);
+        uint64_t v = (O::kRecv && O::kSrc) ? red8<Ty>(in, own[u]) : (O::kRecv ? in : own[u]);
+        if constexpr (OP == kOpRecvReduceCopySend && Ty::kPost) v = post8<Ty>(v, cx.nranks);
         if (O::kDst) store_bytes8<S>(db + 8 * j, v, nbytes - 8 * j);
         if (O::kSend) {
           store_relaxed(sl + 2 * j, (v & 0xffffffffull) | ((uint64_t)sflag << 32));
@@ -595,7 +663,8 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
         for (int u = 0; u < U; ++u) {
           const int64_t j = g0 + (int64_t)u * stride + sub;
           if (j >= hi) continue;
-          const v4u v = (O::kRecv && O::kSrc) ? add16v<Ty>(in[u], own[u]) : (O::kRecv ? in[u] : own[u]);
+          v4u v = (O::kRecv && O::kSrc) ? red16<Ty>(in[u], own[u]) : (O::kRecv ? in[u] : own[u]);
+          if constexpr (OP == kOpRecvReduceCopySend && Ty::kPost) v = post16<Ty>(v, cx.nranks);
           const int64_t b0 = 120 * j + 16 * k;
           if (O::kDst) store_bytes16<S>(db + b0, v, nbytes - b0, cap);
           if (O::kSend) {
@@ -833,20 +902,26 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   if (cx.trace && tid == 0) sh.comm.trace_count[blockIdx.x] = cx.trace_n;
 }
 
-using KernelFn = void (*)(KernelArgs);
-
-// Kernel table by (dtype, protocol): dtype 0 int32, 1 float32, 2 bfloat16.
-const void* get_kernel(int dtype, int proto) {
-  static const KernelFn table[3][3] = {
-      {ring_allreduce_kernel<TyI32, kLL>, ring_allreduce_kernel<TyI32, kLL128>,
-       ring_allreduce_kernel<TyI32, kSimple>},
-      {ring_allreduce_kernel<TyF32, kLL>, ring_allreduce_kernel<TyF32, kLL128>,
-       ring_allreduce_kernel<TyF32, kSimple>},
-      {ring_allreduce_kernel<TyBF16, kLL>, ring_allreduce_kernel<TyBF16, kLL128>,
-       ring_allreduce_kernel<TyBF16, kSimple>},
+// Kernel table of one payload type: [operator][protocol].  Each payload type
+// is instantiated in its own translation unit so the library builds in
+// parallel.
+template <template <int> class Ty>
+const void* ring_kernel_table(int proto, int red) {
+  using KernelFn = void (*)(KernelArgs);
+  static const KernelFn table[kNumRed][3] = {
+      {ring_allreduce_kernel<Ty<kRedSum>, kLL>, ring_allreduce_kernel<Ty<kRedSum>, kLL128>,
+       ring_allreduce_kernel<Ty<kRedSum>, kSimple>},
+      {ring_allreduce_kernel<Ty<kRedProd>, kLL>, ring_allreduce_kernel<Ty<kRedProd>, kLL128>,
+       ring_allreduce_kernel<Ty<kRedProd>, kSimple>},
+      {ring_allreduce_kernel<Ty<kRedMax>, kLL>, ring_allreduce_kernel<Ty<kRedMax>, kLL128>,
+       ring_allreduce_kernel<Ty<kRedMax>, kSimple>},
+      {ring_allreduce_kernel<Ty<kRedMin>, kLL>, ring_allreduce_kernel<Ty<kRedMin>, kLL128>,
+       ring_allreduce_kernel<Ty<kRedMin>, kSimple>},
+      {ring_allreduce_kernel<Ty<kRedAvg>, kLL>, ring_allreduce_kernel<Ty<kRedAvg>, kLL128>,
+       ring_allreduce_kernel<Ty<kRedAvg>, kSimple>},
   };
-  if (dtype < 0 || dtype > 2 || proto < 0 || proto > 2) return nullptr;
-  return reinterpret_cast<const void*>(table[dtype][proto]);
+  if (proto < 0 || proto > 2 || red < 0 || red >= kNumRed) return nullptr;
+  return reinterpret_cast<const void*>(table[red][proto]);
 }
 
 }  // namespace rar

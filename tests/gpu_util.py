@@ -17,7 +17,7 @@ def to_host(t, dtype):
     return t.cpu().numpy()
 
 
-def run_hip(comm, inputs, dtype, in_place=False):
+def run_hip(comm, inputs, dtype, in_place=False, op="sum"):
     """inputs: list over collectives of [N, count] arrays.  Returns a list of
     [N, count] arrays (what every rank's receive buffer holds)."""
     import torch
@@ -30,11 +30,11 @@ def run_hip(comm, inputs, dtype, in_place=False):
         sends.append(s)
         recvs.append(r_)
     if len(inputs) == 1:
-        comm.allreduce(sends[0], recvs[0])
+        comm.allreduce(sends[0], recvs[0], op=op)
     else:
         with comm.group():
             for s, r_ in zip(sends, recvs):
-                comm.allreduce(s, r_)
+                comm.allreduce(s, r_, op=op)
     torch.cuda.synchronize()
     assert comm.async_error() == 0, "watchdog fired"
     return [np.stack([to_host(t, dtype) for t in r_]) for r_ in recvs]
