@@ -96,6 +96,8 @@ def lib():
                                        ctypes.POINTER(ctypes.c_int64),
                                        ctypes.POINTER(ctypes.c_int64),
                                        ctypes.POINTER(ctypes.c_int64)]
+        L.orc_ll_wrap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, i32p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
         L.orc_bf16_round.argtypes = [ctypes.c_double]
         L.orc_bf16_round.restype = ctypes.c_uint16
         _lib = L
@@ -145,7 +147,7 @@ def geometry(nranks, mask, proto, buff_size, chunk_steps, dtype, counts):
 
 def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
               in_place=False, slots=8, sched=0, seed=0, drop_recv_head=False,
-              direct=False, log_calls=False, op="sum"):
+              direct=False, log_calls=False, op="sum", ll_wrap8=False):
     """Run the simulator.
 
     ``inputs`` is a list over works of arrays shaped [N, count] holding the raw
@@ -181,7 +183,8 @@ def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
     if log_calls:
         cap = 1 << 20
         log = (Call * cap)()
-    options = (1 if drop_recv_head else 0) | (2 if direct else 0) | (RED[op] << 8)
+    options = (1 if drop_recv_head else 0) | (2 if direct else 0) | (4 if ll_wrap8 else 0) | \
+        (RED[op] << 8)
     flat = [r for ring in rings for r in ring]
     assert all(len(ring) == N for ring in rings)
     rc = lib().orc_allreduce_rings(N, len(rings), _ints(flat), mask, PROTO[proto], buff_size,
@@ -204,6 +207,15 @@ def stream_fault(proto, fault, slots, nsteps=64):
                                 ctypes.byref(cons), ctypes.byref(bad))
     name = {OK: "complete", DEADLOCK: "deadlock", CORRUPT: "corrupt", INVALID: "invalid"}[rc]
     return name, done.value, cons.value, bad.value
+
+
+def ll_wrap(flag_bits, cleanup, slots, cap, lines_of, nsteps):
+    """LL flag-generation model of one connector; returns (outcome, bad_step)."""
+    bad = ctypes.c_int64()
+    rc = lib().orc_ll_wrap(flag_bits, int(cleanup), slots, cap, len(lines_of), _ints(lines_of),
+                           nsteps, ctypes.byref(bad))
+    name = {OK: "complete", DEADLOCK: "deadlock", CORRUPT: "corrupt", INVALID: "invalid"}[rc]
+    return name, bad.value
 
 
 def bf16_round(v: float) -> int:

@@ -245,6 +245,7 @@ struct Sim {
   int N = 0, C = 0, proto = 0, dtype = 0, slots = 8, chunk_steps = 4;
   int64_t es = 4, step_bytes = 0, sps = 1;
   bool drop_head = false;
+  uint64_t ll_period = 1ull << 32;
   int red = ORC_RED_SUM;
   bool direct = false;  // Simple: all-gather half writes into the next rank's receive buffer
   // Ring of each active channel: entry [n * N + rank] for dense channel n.
@@ -265,6 +266,14 @@ struct Sim {
     if (proto == ORC_PROTO_LL128) return div_up(bytes, 120);
     return 0;
   }
+  // LL line flag of a step: step+1 modulo the flag period (2^32, or 2^8 in
+  // the wrap test mode) [C23 "LL：Data 与 Flag 同 Line"].
+  uint32_t ll_flag(uint64_t step) const { return (uint32_t)((step + 1) % ll_period); }
+  bool ll_cleanup(uint64_t step) const {
+    const uint64_t half = ll_period / 2;
+    return (step + 1) % half >= half - (uint64_t)slots;
+  }
+
   uint8_t* slot(Conn& c, uint64_t step) { return c.fifo.data() + (step % (uint64_t)slots) * step_bytes; }
 
   /* A receiver may consume step `step` of an LL / LL128 connector once every
@@ -277,7 +286,7 @@ struct Sim {
         uint32_t f1, f2;
         std::memcpy(&f1, s + 16 * j + 4, 4);
         std::memcpy(&f2, s + 16 * j + 12, 4);
-        const uint32_t want = (uint32_t)(step + 1);
+        const uint32_t want = ll_flag(step);
         if (f1 != want || f2 != want) return false;
       } else {
         uint64_t f;
@@ -325,7 +334,7 @@ struct Sim {
           const int64_t b = 8 * j + k;
           if (b < bytes) line[k < 4 ? k : 8 + (k - 4)] = val[(size_t)b];
         }
-        const uint32_t flag = (uint32_t)(step + 1);
+        const uint32_t flag = ll_flag(step);
         std::memcpy(line + 4, &flag, 4);
         std::memcpy(line + 12, &flag, 4);
         std::memcpy(s + 16 * j, line, 16);
@@ -339,6 +348,17 @@ struct Sim {
         const uint64_t flag = step + 1;
         std::memcpy(line + 120, &flag, 8);
         std::memcpy(s + 128 * j, line, 128);
+      }
+    }
+    // LL cleanup: in the last NCCL_STEPS steps of each half of the flag period
+    // the rest of the slot takes the current flag, so no line keeps a
+    // generation old enough to come round again.
+    if (proto == ORC_PROTO_LL && ll_cleanup(step)) {
+      const uint32_t flag = ll_flag(step);
+      for (int64_t j = nlines; j < step_bytes / 16; ++j) {
+        std::memset(s + 16 * j, 0, 16);
+        std::memcpy(s + 16 * j + 4, &flag, 4);
+        std::memcpy(s + 16 * j + 12, &flag, 4);
       }
     }
   }
@@ -590,6 +610,8 @@ int orc_allreduce_rings(int nranks, int nrings, const int* ring_orders, uint64_t
   sim.direct = (options & ORC_OPT_DIRECT) != 0;
   if (sim.direct && proto != ORC_PROTO_SIMPLE) return ORC_INVALID;
   sim.red = (options >> ORC_OPT_RED_SHIFT) & 15;
+  if (options & ORC_OPT_LL_WRAP8) sim.ll_period = 256;
+  if ((uint64_t)slots >= sim.ll_period / 2) return ORC_INVALID;
   if (sim.red > ORC_RED_AVG) return ORC_INVALID;
   sim.sendbufs = sendbufs;
   sim.recvbufs = recvbufs;
@@ -811,6 +833,63 @@ int orc_stream_fault(int proto, int fault, int slots, int nsteps, int64_t* steps
   if (consumed) *consumed = c;
   if (bad_step) *bad_step = first_bad;
   return rc;
+}
+
+int orc_ll_wrap(int flag_bits, int cleanup, int slots, int cap, int nsizes, const int* lines_of,
+                int nsteps, int64_t* bad_step) {
+  if ((flag_bits != 8 && flag_bits != 32) || slots < 1 || cap < 1 || nsizes < 1 || !lines_of ||
+      nsteps < 1)
+    return ORC_INVALID;
+  const uint64_t period = 1ull << flag_bits, half = period / 2;
+  if ((uint64_t)slots >= half) return ORC_INVALID;
+  for (int i = 0; i < nsizes; ++i)
+    if (lines_of[i] < 1 || lines_of[i] > cap) return ORC_INVALID;
+  // line = {payload tag, flag}; both halves of an LL line carry the same flag
+  struct Line {
+    uint32_t tag = 0, flag = 0;
+  };
+  std::vector<Line> fifo((size_t)slots * cap);
+  auto flag_of = [&](int64_t k) { return (uint32_t)(((uint64_t)k + 1) % period); };
+  auto tag_of = [&](int64_t k, int j) { return tag32(k, j) | 1u; };  // never 0: zero lines are stale
+  auto lines = [&](int64_t k) { return lines_of[k % nsizes]; };
+  auto is_cleanup = [&](int64_t k) { return ((uint64_t)k + 1) % half >= half - (uint64_t)slots; };
+  int64_t p = 0, c = 0;  // producer step, consumer step
+  int pj = 0, cj = 0;    // next line to write / to take
+  uint64_t head = 0;
+  *bad_step = -1;
+  while (c < nsteps) {
+    // consumer first: take every line that looks ready
+    bool moved = false;
+    while (c < nsteps && cj < lines(c)) {
+      const Line& l = fifo[(size_t)(c % slots) * cap + cj];
+      if (l.flag != flag_of(c)) break;
+      if (l.tag != tag_of(c, cj)) {
+        *bad_step = c;
+        return ORC_CORRUPT;
+      }
+      ++cj;
+      moved = true;
+    }
+    if (c < nsteps && cj == lines(c)) {  // step consumed: hand the slot back
+      ++c;
+      cj = 0;
+      head = (uint64_t)c;
+      continue;
+    }
+    if (moved) continue;
+    // producer: one line (or the whole cleanup tail) per turn
+    if (p >= nsteps || head + (uint64_t)slots < (uint64_t)p + 1) return ORC_DEADLOCK;
+    Line* slot = &fifo[(size_t)(p % slots) * cap];
+    slot[pj].tag = tag_of(p, pj);
+    slot[pj].flag = flag_of(p);
+    if (++pj == lines(p)) {
+      if (cleanup && is_cleanup(p))
+        for (int j = lines(p); j < cap; ++j) slot[j] = Line{0, flag_of(p)};
+      ++p;
+      pj = 0;
+    }
+  }
+  return ORC_OK;
 }
 
 }  // extern "C"

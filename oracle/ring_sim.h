@@ -45,6 +45,7 @@ enum {
   ORC_OPT_DIRECT = 2,         /* Simple only: the all-gather half writes straight into
                                  the next rank's receive buffer instead of its FIFO
                                  [C23 "发布顺序与 Fence", direct read/write]        */
+  ORC_OPT_LL_WRAP8 = 4,       /* LL flags wrap at 0x100 (test mode) instead of 2^32 */
   ORC_OPT_RED_SHIFT = 8       /* bits 8..11: the reduction operator, ORC_RED_*     */
 };
 
@@ -149,6 +150,22 @@ int orc_allreduce_rings(int nranks, int nrings, const int* ring_orders, uint64_t
  * accepted; *bad_step = first corrupted step (or -1). */
 int orc_stream_fault(int proto, int fault, int slots, int nsteps, int64_t* steps_done,
                      int64_t* consumed, int64_t* bad_step);
+
+/* LL flag generations on one connector [C23 "LL：Data 与 Flag 同 Line": a test
+ * mode makes the flag wrap at 0x100; at cleanup steps the sender writes the
+ * rest of the slot with the current generation].  A producer streams `nsteps`
+ * steps; step k carries lines_of[k mod nsizes] lines (1..cap) into slot
+ * k mod slots, which holds `cap` lines and starts zeroed.  Line flags are
+ * (k+1) mod 2^flag_bits (flag_bits 8 or 32).  With `cleanup`, the last
+ * `slots` steps of each half of the flag period also stamp lines [n, cap) of
+ * their slot with their flag.  The consumer is eager: it takes each line of
+ * its step as soon as both flags equal its generation -- possibly before the
+ * producer has written that line -- and checks the payload; the producer
+ * writes one line at a time and waits for head credit per step.
+ * Returns ORC_OK, ORC_CORRUPT (*bad_step = first step that took a stale line)
+ * or ORC_INVALID. */
+int orc_ll_wrap(int flag_bits, int cleanup, int slots, int cap, int nsizes, const int* lines_of,
+                int nsteps, int64_t* bad_step);
 
 /* Round a binary64 value to bfloat16 (round to nearest, ties to even,
  * subnormals kept, overflow to infinity).  Exposed for pinning. */
