@@ -79,7 +79,11 @@ typedef struct {
                             head" fault), so senders stall after exactly
                             NCCL_STEPS slots and the watchdog ends the launch
                             with RAR_ABORTED [C23 "状态机故障注入"].  Bit 1:
-                            record a timeline (rar_comm_read_trace)        */
+                            record a timeline (rar_comm_read_trace).  Bit 2:
+                            LL flags wrap at 0x100 instead of 2^32 [C23 "LL：
+                            Data 与 Flag 同 Line" test mode]; the slot
+                            cleanup that makes a wrap safe then runs every
+                            128 steps instead of every 2^31            */
   int launch_mode;       /* 0: cooperative launch, the runtime guarantees that
                             every workgroup is resident (or fails the launch).
                             1: plain launch, shorter gaps between launches; the
@@ -113,6 +117,7 @@ typedef struct {
 
 #define RAR_DEBUG_DROP_RECV_HEAD 1
 #define RAR_DEBUG_TRACE 2
+#define RAR_DEBUG_LL_FLAG_WRAP8 4
 
 /* Create a communicator: the ring, the active channels, the protocol and the
  * FIFOs for every (rank, channel).  Allocates N * popcount(mask) * buffSize

@@ -10,6 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "librar.so")
 
 SUCCESS, INVALID_ARGUMENT, UNSUPPORTED, HIP_ERROR, INTERNAL_ERROR, ABORTED = range(6)
+DEBUG_DROP_RECV_HEAD, DEBUG_TRACE, DEBUG_LL_FLAG_WRAP8 = 1, 2, 4
 PROTO = {"LL": 0, "LL128": 1, "SIMPLE": 2}
 DTYPE = {"int32": 0, "float32": 1, "bfloat16": 2}
 SUM = 0

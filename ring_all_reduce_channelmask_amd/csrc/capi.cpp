@@ -315,7 +315,7 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
   if (tune.spin_timeout_us < 0) return fail(RAR_INVALID_ARGUMENT, "spin_timeout_us is negative");
   if (tune.launch_mode != 0 && tune.launch_mode != 1)
     return fail(RAR_INVALID_ARGUMENT, "launch_mode must be 0 or 1");
-  if (tune.debug_flags & ~3) return fail(RAR_INVALID_ARGUMENT, "unknown debug_flags bits");
+  if (tune.debug_flags & ~7) return fail(RAR_INVALID_ARGUMENT, "unknown debug_flags bits");
   if (tune.placement != 0 && tune.placement != 1)
     return fail(RAR_INVALID_ARGUMENT, "placement must be 0 or 1");
   if (tune.slices_per_chunk < 0 || tune.slices_per_chunk > 4 || tune.slices_per_chunk == 3)
@@ -451,6 +451,7 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
   hc.hot.trace_count = c->d_trace_count;
   hc.hot.placement = c->d_placement;
   hc.hot.wg_of = c->d_wg_of;
+  hc.hot.ll_flag_mask = (tune.debug_flags & RAR_DEBUG_LL_FLAG_WRAP8) ? 0xFFu : 0xFFFFFFFFu;
   for (int id = 0; id < rar::kMaxChannels; ++id) {
     if (!((channel_mask >> id) & 1)) continue;
     const rar::RingInfo& ring = rings[id % nrings];

@@ -116,6 +116,7 @@ struct alignas(16) DevCommHot {
   uint32_t* trace_count;       // [grid] records written by the last launch
   uint64_t* placement;         // [grid] epoch << 8 | XCC id, written at kernel entry
   const uint32_t* wg_of;       // [(r * C + n) * P + p] -> workgroup index in the grid
+  uint32_t ll_flag_mask;       // LL flag period - 1 (0xFFFFFFFF, or 0xFF in the wrap test mode)
 };
 static_assert(sizeof(DevCommHot) % 16 == 0, "hot fields are copied in 16-byte packs");
 

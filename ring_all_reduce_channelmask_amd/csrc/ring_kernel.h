@@ -183,6 +183,7 @@ struct Ctx {
   uint32_t* abort_host;
   uint64_t timeout;
   bool drop_head;  // fault test: never publish head credit
+  uint32_t ll_mask;  // LL flag period - 1: 2^32 - 1, or 0xFF in the wrap test mode
   bool aborted;
   // The receiving workgroup of the send connector shares this workgroup's L2:
   // payload stores that have completed (vmcnt drained) are already visible to
@@ -457,6 +458,17 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
 // usually without a load) and keeps kLlUnroll lines in flight.
 constexpr int kLlUnroll = 4;
 
+// LL cleanup [C23 "LL：Data 与 Flag 同 Line": when the flag period is about
+// to wrap, the sender stamps the rest of the slot with the current flag].
+// Cleanup steps are the last NCCL_STEPS steps of each half of the flag
+// period, so each slot is restamped at least once per half period and no
+// line keeps a generation that could come round again (nor the zero of a
+// never-written line, which flag 0 would match).
+__device__ __forceinline__ bool ll_cleanup_step(uint64_t step, uint32_t mask) {
+  const uint64_t half = ((uint64_t)mask + 1) >> 1;
+  return ((step + 1) & (half - 1)) >= half - kSteps;
+}
+
 __device__ __forceinline__ bool ll_ready(uint64_t a, uint64_t b, uint32_t flag) {
   return (uint32_t)(a >> 32) == flag && (uint32_t)(b >> 32) == flag;
 }
@@ -504,9 +516,12 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
   const uint64_t step0 = cx.recv_step;
   bool ok = true;
   const bool worker = cx.tid < cx.workers;
-  if (O::kSend && worker && lo < hi) ok = wait_credit(cx, 1);
+  // a cleanup step writes the whole slot, so it needs the credit even with no lines
+  const bool cleanup = O::kSend && ll_cleanup_step(cx.send_step, cx.ll_mask);
+  if (O::kSend && worker && (lo < hi || cleanup)) ok = wait_credit(cx, 1);
   const uint64_t t1 = cx.trace ? now_ticks() : 0;
-  const uint32_t rflag = (uint32_t)(cx.recv_step + 1), sflag = (uint32_t)(cx.send_step + 1);
+  const uint32_t rflag = (uint32_t)(cx.recv_step + 1) & cx.ll_mask;
+  const uint32_t sflag = (uint32_t)(cx.send_step + 1) & cx.ll_mask;
   // line j of the step sits at line j - lo of this lane's slot
   const uint64_t* rl = reinterpret_cast<const uint64_t*>(cx.recv_fifo + (cx.recv_step % kSteps) * cx.lane_step_bytes) - 2 * lo;
   uint64_t* sl = reinterpret_cast<uint64_t*>(cx.send_fifo + (cx.send_step % kSteps) * cx.lane_step_bytes) - 2 * lo;
@@ -549,6 +564,17 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
         }
       }
     }
+  }
+  if (cleanup && worker && ok) {
+    // lines [hi - lo, cap) of this lane's slot take the current flag; they
+    // complete before the barrier, ahead of any later write to the slot
+    const int64_t cap = cx.lane_step_bytes / 16;
+    const uint64_t stamp = (uint64_t)sflag << 32;
+    for (int64_t p = hi - lo + cx.tid; p < cap; p += cx.workers) {
+      store_relaxed(sl + 2 * (lo + p), stamp);
+      store_relaxed(sl + 2 * (lo + p) + 1, stamp);
+    }
+    drain_vmem();
   }
   if (!ok) cx.sh->abort = 1;
   // Every line value was consumed before this barrier, so every line read of
@@ -859,6 +885,7 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.abort_host = sh.comm.abort_host;
   cx.timeout = sh.comm.spin_timeout_ticks;
   cx.drop_head = (sh.comm.debug_flags & 1) != 0;
+  cx.ll_mask = sh.comm.ll_flag_mask;
   cx.aborted = false;
   cx.trace = (sh.comm.debug_flags & 2) ? sh.comm.trace + (int64_t)blockIdx.x * sh.comm.trace_cap : nullptr;
   cx.trace_n = 0;

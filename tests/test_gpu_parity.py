@@ -395,3 +395,25 @@ def test_per_channel_rings_full_size_direct_and_spread(dtype):
         comm.close()
         for r in range(4):
             assert_bits_equal(got[r], want, f"{kw} rank {r}")
+
+
+# ------------------------------------------------- LL flag wrap test mode
+@pytest.mark.parametrize("lanes", [1, 3])
+def test_ll_flag_wrap_mode_over_many_wraps(lanes):
+    """LL with 8-bit flags (debug bit 2): launches of varying size on one
+    communicator carry every connector through several wraps of the flag and
+    several slot cleanups; every launch matches the closed form."""
+    import ring_all_reduce_channelmask_amd as rar
+    buff = SMALL_BUFF["LL"]
+    comm = _comm(nranks=4, ring_order=[0, 2, 3, 1], mask=0x3, proto="LL", buff_size=buff,
+                 lanes=lanes, waves=2, debug_flags=rar._lib.DEBUG_LL_FLAG_WRAP8)
+    rng = np.random.default_rng(lanes)
+    for i, count in enumerate([20011, 7, 40000, 333, 61111, 1, 25000]):
+        x = _rand("float32", (4, count), 100 + i)
+        got = run_hip(comm, [x], "float32")[0]
+        want = cf.allreduce([x], [0, 2, 3, 1], 0x3, "LL", buff, 4, "float32")[0]
+        for r in range(4):
+            assert_bits_equal(got[r], want, f"launch {i} rank {r}")
+    steps = comm.query_state()
+    assert min(steps[1::2]) > 4 * 256, "each connector should have crossed several wraps"
+    comm.close()
