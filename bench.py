@@ -80,6 +80,18 @@ def measured_traffic(key, shape, algo="ring"):
     return t.get("hbm_bytes_per_launch")
 
 
+def place(t, off):
+    """``t``'s contents in a tensor that starts ``off`` elements past a 16-byte
+    boundary (a view into a slightly larger allocation)."""
+    if off == 0:
+        return t
+    import torch
+    big = torch.empty(t.numel() + off + 16, dtype=t.dtype, device=t.device)
+    v = big[off:off + t.numel()]
+    v.copy_(t)
+    return v
+
+
 def cpu_baseline(w, xs, algo="ring", budget_s=12.0, max_runs=5):
     """The oracle, as it stands, on the same workload: the state-machine
     simulator for the ring, the written-out fold for the one-shot."""
@@ -110,6 +122,8 @@ def main():
                          "from all inputs in one hop, on the same workload")
     ap.add_argument("--workgroups", type=int, default=None, help="oneshot launch shape")
     ap.add_argument("--unroll", type=int, default=None, help="oneshot launch shape")
+    ap.add_argument("--misalign", type=int, default=0, metavar="ELEMS",
+                    help="place every user buffer ELEMS elements past a 16-byte boundary")
     ap.add_argument("--lanes", type=int, default=None)
     ap.add_argument("--waves", type=int, default=None)
     ap.add_argument("--launch-mode", type=int, default=None, choices=[0, 1])
@@ -180,8 +194,8 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
-    sends = [[dev(x[r]) for r in range(N)] for x in xs]
-    recvs = [[torch.empty_like(t) for t in s] for s in sends]
+    sends = [[place(dev(x[r]), args.misalign) for r in range(N)] for x in xs]
+    recvs = [[place(torch.empty_like(t), args.misalign) for t in s] for s in sends]
     comm = rar.Comm(N, list(w.ring_order), w.mask, proto=w.proto, buff_size=w.buff_size,
                     chunk_steps=w.chunk_steps if w.proto == "SIMPLE" else 0, **tune)
     shape = comm.shape()
@@ -258,6 +272,7 @@ def main():
             "lanes_per_channel": shape["lanes"], "waves_per_lane": shape["waves"],
             "grid": shape["grid"], "parallelism": f"{N} virtual ranks on 1 GPU",
             "launch": "plain" if tune.get("launch_mode", 0) == 1 else "cooperative",
+            "misalign_elems": args.misalign,
         },
         "algbw_GBps": round(algbw, 3),
         "busbw_GBps": round(busbw, 3),
@@ -318,8 +333,8 @@ def run_oneshot(args, w):
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
-    sends = [dev(x[r]) for r in range(N)]
-    recvs = [torch.empty_like(t) for t in sends]
+    sends = [place(dev(x[r]), args.misalign) for r in range(N)]
+    recvs = [place(torch.empty_like(t), args.misalign) for t in sends]
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         rar.oneshot_allreduce(sends, recvs, stream=stream, **tune)
@@ -368,6 +383,7 @@ def run_oneshot(args, w):
             "workload": f"{w.key} one-shot: {N} ranks, {w.dtype}, {M >> 20} MiB/rank",
             "nranks": N, "elems_per_rank": count, "algorithm": "one-shot",
             "parallelism": f"{N} virtual ranks on 1 GPU", **shape,
+            "misalign_elems": args.misalign,
         },
         "algbw_GBps": round(metrics.algbw_gbps(M, t_step), 3),
         "busbw_GBps": round(busbw, 3),

@@ -168,8 +168,12 @@ rar_result_t rar_comm_create_rings(rar_comm_t* comm, int nranks, int nrings,
  * reduction `op` over ranks of sendbufs[r][i], folded in ring order (the rank
  * after the chunk's owner starts, the owner combines last), identical on
  * every rank.
- *   sendbufs, recvbufs  host arrays of `nranks` device pointers, each 16-byte
- *                       aligned.  recvbufs[r] == sendbufs[r] runs in place;
+ *   sendbufs, recvbufs  host arrays of `nranks` device pointers, each aligned
+ *                       to its element size (4 bytes for int32 and float32, 2
+ *                       for bfloat16); 16-byte alignment is not needed
+ *                       [C23 "LL128：15/16 Payload" stages misaligned user
+ *                       data; here the hardware's unaligned vector accesses
+ *                       serve it].  recvbufs[r] == sendbufs[r] runs in place;
  *                       other overlap is not allowed.
  *   count               elements per rank; 0 launches nothing, leaves the
  *                       FIFO steps untouched and does not look at the pointers.
@@ -213,7 +217,7 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
  * N*count elements.  Needs no communicator and allocates nothing; one kernel
  * launch on `stream`, stream-ordered.
  *   sendbufs, recvbufs  host arrays of `nranks` (2..64) device pointers, each
- *                       16-byte aligned, copied at call time.  recvbufs[r] ==
+ *                       aligned to its element size, copied at call time.  recvbufs[r] ==
  *                       sendbufs[r] runs in place; no other two buffers may
  *                       overlap (checked).
  *   count               elements per rank; 0 launches nothing and does not

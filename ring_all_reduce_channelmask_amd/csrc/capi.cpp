@@ -131,15 +131,16 @@ rar_result_t check_op(int op) {
   return RAR_SUCCESS;
 }
 
-rar_result_t check_buffers(const rar_comm* c, const void* const* sendbufs, void* const* recvbufs) {
+rar_result_t check_buffers(const rar_comm* c, const void* const* sendbufs, void* const* recvbufs,
+                           int dtype) {
   if (!sendbufs || !recvbufs) return fail(RAR_INVALID_ARGUMENT, "sendbufs/recvbufs is NULL");
+  const uintptr_t align = (uintptr_t)rar::elem_size(dtype);
   for (int r = 0; r < c->nranks; ++r) {
     if (!sendbufs[r] || !recvbufs[r])
       return fail(RAR_INVALID_ARGUMENT, "buffer of rank " + std::to_string(r) + " is NULL");
-    if ((reinterpret_cast<uintptr_t>(sendbufs[r]) & 15) ||
-        (reinterpret_cast<uintptr_t>(recvbufs[r]) & 15))
+    if ((reinterpret_cast<uintptr_t>(sendbufs[r]) | reinterpret_cast<uintptr_t>(recvbufs[r])) & (align - 1))
       return fail(RAR_INVALID_ARGUMENT,
-                  "buffer of rank " + std::to_string(r) + " is not 16-byte aligned");
+                  "buffer of rank " + std::to_string(r) + " is not aligned to its element size");
   }
   return RAR_SUCCESS;
 }
@@ -493,7 +494,7 @@ rar_result_t rar_allreduce(rar_comm_t c, const void* const* sendbufs, void* cons
     return fail(RAR_UNSUPPORTED, "all AllReduces of a group must share one dtype and operator");
   // nothing to move: no launch, no step advance, pointers are not looked at
   if (count == 0) return RAR_SUCCESS;
-  if (rar_result_t r = check_buffers(c, sendbufs, recvbufs)) return r;
+  if (rar_result_t r = check_buffers(c, sendbufs, recvbufs, dtype)) return r;
   if (count > (size_t(1) << 40)) return fail(RAR_INVALID_ARGUMENT, "count too large");
   QueuedCall q;
   for (int r = 0; r < c->nranks; ++r) q.send.push_back(const_cast<void*>(sendbufs[r]));
@@ -586,8 +587,8 @@ rar_result_t rar_oneshot_allreduce(const void* const* sendbufs, void* const* rec
       return fail(RAR_INVALID_ARGUMENT, "buffer of rank " + std::to_string(r) + " is NULL");
     const uintptr_t s = reinterpret_cast<uintptr_t>(sendbufs[r]);
     const uintptr_t d = reinterpret_cast<uintptr_t>(recvbufs[r]);
-    if ((s | d) & 15)
-      return fail(RAR_INVALID_ARGUMENT, "buffer of rank " + std::to_string(r) + " is not 16-byte aligned");
+    if ((s | d) & (es - 1))
+      return fail(RAR_INVALID_ARGUMENT, "buffer of rank " + std::to_string(r) + " is not aligned to its element size");
     ranges.push_back({s, r});
     if (d != s) ranges.push_back({d, r});
   }

@@ -22,9 +22,13 @@ namespace rar {
 namespace {
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+// Buffers need only element alignment: gfx950 serves unaligned global
+// loads and stores in hardware, so the under-aligned type compiles to the
+// same dwordx4 accesses as an aligned one.
+typedef uint32_t v4u_user __attribute__((ext_vector_type(4), aligned(2)));
 
-__device__ __forceinline__ v4u ld_nt(const v4u* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ void st_nt(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ v4u ld_nt(const v4u_user* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_nt(v4u_user* p, v4u v) { __builtin_nontemporal_store((v4u_user)v, p); }
 
 __device__ __forceinline__ uint32_t bf16_round(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -166,7 +170,7 @@ __global__ void __launch_bounds__(512) oneshot_kernel(OneshotArgs args) {
 #pragma unroll
       for (int j = 0; j < kRankBatch; ++j) {
         if (k0 + j < N) {
-          const v4u* src = reinterpret_cast<const v4u*>(args.src[k0 + j]);
+          const v4u_user* src = reinterpret_cast<const v4u_user*>(args.src[k0 + j]);
 #pragma unroll
           for (int u = 0; u < U; ++u)
             if (live[u]) x[j][u] = ld_nt(src + base + (int64_t)u * nthreads);
@@ -189,7 +193,7 @@ __global__ void __launch_bounds__(512) oneshot_kernel(OneshotArgs args) {
     for (int u = 0; u < U; ++u)
       if (live[u]) r[u] = acc[u].out(N);
     for (int k = 0; k < N; ++k) {
-      v4u* dst = reinterpret_cast<v4u*>(args.dst[k]);
+      v4u_user* dst = reinterpret_cast<v4u_user*>(args.dst[k]);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (live[u]) st_nt(dst + base + (int64_t)u * nthreads, r[u]);

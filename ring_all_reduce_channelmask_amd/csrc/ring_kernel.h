@@ -300,15 +300,43 @@ __device__ __forceinline__ v4u post16(v4u a, int n) {
   r.w = Ty::post_word(a.w, n);
   return r;
 }
-template <bool kNt>
-__device__ __forceinline__ v4u ld16(const v4u* p) {
-  if constexpr (kNt) return __builtin_nontemporal_load(p);
-  else return *p;
+// User buffers need only element alignment [C23 "LL128：15/16 Payload": a
+// misaligned user buffer takes a staging path there].  gfx950 serves
+// unaligned global loads and stores in hardware (the target runs in
+// unaligned access mode), so user data is read and written through an
+// under-aligned 16-byte type: the same dwordx4 instructions as the aligned
+// case, split by the memory system where they cross a cache line.  FIFO
+// slots stay 16-byte aligned.
+typedef uint32_t v4u_user __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint64_t u64_user __attribute__((aligned(2)));
+
+// Vector i of a buffer: kUser = element-aligned user buffer, else a FIFO
+// slot.  The pointer types are spelled out here (an alignment attribute on a
+// typedef does not survive a template argument).
+template <bool kNt, bool kUser>
+__device__ __forceinline__ v4u ldv(const void* base, int64_t i) {
+  if constexpr (kUser) {
+    const v4u_user* p = reinterpret_cast<const v4u_user*>(base) + i;
+    if constexpr (kNt) return __builtin_nontemporal_load(p);
+    else return *p;
+  } else {
+    const v4u* p = reinterpret_cast<const v4u*>(base) + i;
+    if constexpr (kNt) return __builtin_nontemporal_load(p);
+    else return *p;
+  }
 }
-template <bool kNt>
-__device__ __forceinline__ void st16(v4u* p, v4u v) {
-  if constexpr (kNt) __builtin_nontemporal_store(v, p);
-  else *p = v;
+template <bool kNt, bool kUser>
+__device__ __forceinline__ void stv(void* base, int64_t i, v4u v) {
+  if constexpr (kUser) {
+    v4u_user* p = reinterpret_cast<v4u_user*>(base) + i;
+    const v4u_user w = v;
+    if constexpr (kNt) __builtin_nontemporal_store(w, p);
+    else *p = w;
+  } else {
+    v4u* p = reinterpret_cast<v4u*>(base) + i;
+    if constexpr (kNt) __builtin_nontemporal_store(v, p);
+    else *p = v;
+  }
 }
 
 // reduceCopy over n elements with 16-byte vectors, RAR_UNROLL in flight per
@@ -330,34 +358,30 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
   constexpr bool kNi = kUserIn ? RAR_NT_DIRECT != 0 : RAR_NT_FIFO != 0;
   constexpr bool kNo = kUserOut ? RAR_NT_DIRECT != 0 : RAR_NT_FIFO != 0;
   const int64_t nv = n / kVec;
-  const v4u* vin = reinterpret_cast<const v4u*>(fin);
-  const v4u* vsrc = reinterpret_cast<const v4u*>(src);
-  v4u* vdst = reinterpret_cast<v4u*>(dst);
-  v4u* vout = reinterpret_cast<v4u*>(fout);
   int64_t i = tid;
   for (; i + (int64_t)(kUnroll - 1) * nthr < nv; i += (int64_t)kUnroll * nthr) {
     v4u a[kUnroll], b[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (kRecv) a[u] = ld16<kNi>(vin + i + (int64_t)u * nthr);
-      if (kSrc) b[u] = ld16<kNu>(vsrc + i + (int64_t)u * nthr);
+      if (kRecv) a[u] = ldv<kNi, kUserIn>(fin, i + (int64_t)u * nthr);
+      if (kSrc) b[u] = ldv<kNu, true>(src, i + (int64_t)u * nthr);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       v4u r = (kRecv && kSrc) ? red16<Ty>(a[u], b[u]) : (kRecv ? a[u] : b[u]);
       if constexpr (kPost) r = post16<Ty>(r, n_post);
-      if (kDst) st16<kNu>(vdst + i + (int64_t)u * nthr, r);
-      if (kSend) st16<kNo>(vout + i + (int64_t)u * nthr, r);
+      if (kDst) stv<kNu, true>(dst, i + (int64_t)u * nthr, r);
+      if (kSend) stv<kNo, kUserOut>(fout, i + (int64_t)u * nthr, r);
     }
   }
   for (; i < nv; i += nthr) {
     v4u a = {0, 0, 0, 0}, b = a;
-    if (kRecv) a = ld16<kNi>(vin + i);
-    if (kSrc) b = ld16<kNu>(vsrc + i);
+    if (kRecv) a = ldv<kNi, kUserIn>(fin, i);
+    if (kSrc) b = ldv<kNu, true>(src, i);
     v4u r = (kRecv && kSrc) ? red16<Ty>(a, b) : (kRecv ? a : b);
     if constexpr (kPost) r = post16<Ty>(r, n_post);
-    if (kDst) st16<kNu>(vdst + i, r);
-    if (kSend) st16<kNo>(vout + i, r);
+    if (kDst) stv<kNu, true>(dst, i, r);
+    if (kSend) stv<kNo, kUserOut>(fout, i, r);
   }
   for (int64_t e = nv * kVec + tid; e < n; e += nthr) {
     S a = 0, b = 0;
@@ -486,7 +510,7 @@ __device__ bool ll_wait_line(const uint64_t* line, uint32_t flag, uint64_t& a, u
 
 template <class S>
 __device__ __forceinline__ uint64_t load_bytes8(const uint8_t* p, int64_t valid) {
-  if (valid >= 8) return *reinterpret_cast<const uint64_t*>(p);
+  if (valid >= 8) return *reinterpret_cast<const u64_user*>(p);
   uint64_t v = 0;
   for (int64_t b = 0; b < valid; b += sizeof(S))
     v |= (uint64_t)(*reinterpret_cast<const S*>(p + b)) << (8 * b);
@@ -495,7 +519,7 @@ __device__ __forceinline__ uint64_t load_bytes8(const uint8_t* p, int64_t valid)
 template <class S>
 __device__ __forceinline__ void store_bytes8(uint8_t* p, uint64_t v, int64_t valid) {
   if (valid >= 8) {
-    *reinterpret_cast<uint64_t*>(p) = v;
+    *reinterpret_cast<u64_user*>(p) = v;
     return;
   }
   for (int64_t b = 0; b < valid; b += sizeof(S)) *reinterpret_cast<S*>(p + b) = (S)(v >> (8 * b));

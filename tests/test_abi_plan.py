@@ -150,7 +150,7 @@ def test_oneshot_validates_on_the_host():
     bad = [
         (dict(send=ok_s, recv=ok_r, count=16, nranks=1), "one rank"),
         (dict(send=ok_s, recv=ok_r, count=16, nranks=65), "65 ranks"),
-        (dict(send=[A, A + 4], recv=ok_r, count=16), "misaligned"),
+        (dict(send=[A, A + 4098], recv=ok_r, count=16), "not element-aligned (fp32 at 2 mod 4)"),
         (dict(send=[A, 0], recv=ok_r, count=16), "NULL"),
         (dict(send=[A, A + 64], recv=ok_r, count=17), "send buffers overlap (17 fp32 > 64 B)"),
         (dict(send=ok_s, recv=[A + 8192, A + 8192], count=16), "two ranks share a receive buffer"),
