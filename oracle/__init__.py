@@ -147,7 +147,7 @@ def geometry(nranks, mask, proto, buff_size, chunk_steps, dtype, counts):
 
 def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
               in_place=False, slots=8, sched=0, seed=0, drop_recv_head=False,
-              direct=False, log_calls=False, op="sum", ll_wrap8=False):
+              direct=False, log_calls=False, op="sum", ll_wrap8=False, direct_read=False):
     """Run the simulator.
 
     ``inputs`` is a list over works of arrays shaped [N, count] holding the raw
@@ -184,7 +184,7 @@ def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
         cap = 1 << 20
         log = (Call * cap)()
     options = (1 if drop_recv_head else 0) | (2 if direct else 0) | (4 if ll_wrap8 else 0) | \
-        (RED[op] << 8)
+        (16 if direct_read else 0) | (RED[op] << 8)
     flat = [r for ring in rings for r in ring]
     assert all(len(ring) == N for ring in rings)
     rc = lib().orc_allreduce_rings(N, len(rings), _ints(flat), mask, PROTO[proto], buff_size,

@@ -223,6 +223,7 @@ struct Unit {
   int chunk;
   int loop;
   int first_of_call;  // first slice of a primitive call (counts the call once)
+  int raw_recv;       // the loop's first receive: its data is the previous rank's raw input
   int64_t offset;     // element offset of this unit in the collective's buffers
   int64_t nelem;      // elements moved by this unit (may be 0)
   int64_t call_offset, call_nelem;
@@ -248,6 +249,7 @@ struct Sim {
   uint64_t ll_period = 1ull << 32;
   int red = ORC_RED_SUM;
   bool direct = false;  // Simple: all-gather half writes into the next rank's receive buffer
+  bool direct_read = false;  // Simple: the loop's first receive reads the previous send buffer
   // Ring of each active channel: entry [n * N + rank] for dense channel n.
   // Channel id c follows ring c mod nrings [C12 "为什么 channels 会重复":
   // the base rings are duplicated onto the following channels].
@@ -378,12 +380,17 @@ struct Sim {
     const bool direct_send =
         direct && (u.op == ORC_OP_RECV_REDUCE_COPY_SEND || u.op == ORC_OP_RECV_COPY_SEND);
     const bool direct_recv = direct && (u.op == ORC_OP_RECV_COPY_SEND || u.op == ORC_OP_RECV);
+    // Direct read: the loop's opening send leaves its data where it is, and
+    // the next rank's first receive reads it from this rank's send buffer.
+    const bool skip_send = direct_read && u.op == ORC_OP_SEND;
+    const bool read_prev = direct_read && u.raw_recv;
     Conn& rc = conn[(size_t)ag.rank * C + ag.n];
     const int nxt = next[(size_t)ag.n * N + ag.rank];
     Conn& sc = conn[(size_t)nxt * C + ag.n];
     const uint64_t adv = (uint64_t)sps;
     // sender wait: head + NCCL_STEPS >= step + StepPerSlice
-    if (send && !direct_send && !(sc.head + (uint64_t)slots >= ag.send_step + adv)) return false;
+    if (send && !direct_send && !skip_send && !(sc.head + (uint64_t)slots >= ag.send_step + adv))
+      return false;
     // receiver wait: tail >= step + StepPerSlice (Simple) or line flags (LL, LL128)
     if (recv) {
       if (proto == ORC_PROTO_SIMPLE) {
@@ -397,7 +404,11 @@ struct Sim {
     uint8_t* dst = (uint8_t*)recvbufs[(size_t)u.work * N + ag.rank] + u.offset * es;
     uint8_t* next_dst = (uint8_t*)recvbufs[(size_t)u.work * N + nxt] + u.offset * es;
     std::vector<uint8_t> got;
-    if (recv && direct_recv) got.assign(dst, dst + u.nelem * es);
+    if (recv && read_prev) {
+      const int prv = prev[(size_t)ag.n * N + ag.rank];
+      const uint8_t* prev_src = (const uint8_t*)sendbufs[(size_t)u.work * N + prv] + u.offset * es;
+      got.assign(prev_src, prev_src + u.nelem * es);
+    } else if (recv && direct_recv) got.assign(dst, dst + u.nelem * es);
     else if (recv) read_payload(rc, ag.recv_step, u.nelem, got);
     std::vector<uint8_t> val((size_t)(u.nelem * es));
     for (int64_t i = 0; i < u.nelem; ++i) {
@@ -422,7 +433,7 @@ struct Sim {
     }
     if (send && direct_send) {
       if (u.nelem > 0) std::memcpy(next_dst, val.data(), val.size());
-    } else if (send) {
+    } else if (send && !skip_send) {
       write_payload(sc, ag.send_step, val);
     }
     // publish: receiver frees the slots (head), sender announces data (tail)
@@ -442,7 +453,9 @@ struct Sim {
       }
       if (send) {
         stats->payload_sent[ag.rank] += u.nelem * es;
-        if (proto == ORC_PROTO_SIMPLE) stats->wire_sent[ag.rank] += u.nelem * es;
+        if (proto == ORC_PROTO_SIMPLE) {
+          if (!direct_send && !skip_send) stats->wire_sent[ag.rank] += u.nelem * es;  // FIFO bytes
+        }
         else if (proto == ORC_PROTO_LL) stats->wire_sent[ag.rank] += lines_for(u.nelem) * 16;
         else stats->wire_sent[ag.rank] += lines_for(u.nelem) * 128;
       }
@@ -490,11 +503,11 @@ void build_program(Agent& ag, const Sim& sim, const std::vector<orc_piece>& piec
           for (int s = 0; s < kSlicesPerChunk; ++s) {
             const int64_t soff = (int64_t)s * slice;
             const int64_t sn = std::max<int64_t>(0, std::min<int64_t>(slice, nelem - soff));
-            Unit u{ops[k], p.work, c, loop, s == 0, offset + soff, sn, offset, nelem};
+            Unit u{ops[k], p.work, c, loop, s == 0, k == 1, offset + soff, sn, offset, nelem};
             ag.prog.push_back(u);
           }
         } else {
-          Unit u{ops[k], p.work, c, loop, 1, offset, nelem, offset, nelem};
+          Unit u{ops[k], p.work, c, loop, 1, k == 1, offset, nelem, offset, nelem};
           ag.prog.push_back(u);
         }
       }
@@ -608,7 +621,8 @@ int orc_allreduce_rings(int nranks, int nrings, const int* ring_orders, uint64_t
   sim.sps = proto == ORC_PROTO_SIMPLE ? chunk_steps / 2 : 1;
   sim.drop_head = (options & ORC_OPT_DROP_RECV_HEAD) != 0;
   sim.direct = (options & ORC_OPT_DIRECT) != 0;
-  if (sim.direct && proto != ORC_PROTO_SIMPLE) return ORC_INVALID;
+  sim.direct_read = (options & ORC_OPT_DIRECT_READ) != 0;
+  if ((sim.direct || sim.direct_read) && proto != ORC_PROTO_SIMPLE) return ORC_INVALID;
   sim.red = (options >> ORC_OPT_RED_SHIFT) & 15;
   if (options & ORC_OPT_LL_WRAP8) sim.ll_period = 256;
   if ((uint64_t)slots >= sim.ll_period / 2) return ORC_INVALID;

@@ -46,6 +46,10 @@ enum {
                                  the next rank's receive buffer instead of its FIFO
                                  [C23 "发布顺序与 Fence", direct read/write]        */
   ORC_OPT_LL_WRAP8 = 4,       /* LL flags wrap at 0x100 (test mode) instead of 2^32 */
+  ORC_OPT_DIRECT_READ = 16,   /* Simple only: the first receive of every loop reads the
+                                 previous rank's send buffer in place, and the loop's
+                                 opening send moves no data [C23 "发布顺序与 Fence",
+                                 direct read/write]                                   */
   ORC_OPT_RED_SHIFT = 8       /* bits 8..11: the reduction operator, ORC_RED_*     */
 };
 
@@ -103,7 +107,8 @@ typedef struct {
   int64_t send_ops[64];       /* per user rank: primitive calls that send    */
   int64_t recv_ops[64];       /* per user rank: primitive calls that receive */
   int64_t payload_sent[64];   /* per user rank: payload bytes sent           */
-  int64_t wire_sent[64];      /* per user rank: FIFO bytes written (lines)   */
+  int64_t wire_sent[64];      /* per user rank: FIFO bytes written (lines);
+                                 direct sends write none                    */
   int64_t units_run;          /* slices / steps executed in total            */
   int64_t calls_recorded;     /* entries written to the call log             */
   int32_t deadlock_rank, deadlock_channel;

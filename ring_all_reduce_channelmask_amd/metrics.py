@@ -28,19 +28,24 @@ def busbw_gbps(message_bytes: float, seconds: float, nranks: int) -> float:
     return algbw_gbps(message_bytes, seconds) * 2.0 * (nranks - 1) / nranks
 
 
-def algorithmic_bytes(message_bytes: int, nranks: int, proto: str, direct: bool = False) -> float:
+def algorithmic_bytes(message_bytes: int, nranks: int, proto: str, direct: bool = False,
+                      direct_read: bool = False) -> float:
     """HBM bytes the ring schedule must move for one collective, all ranks.
 
-    The direct variant (Simple) writes the all-gather half straight into the
+    The direct write (Simple) puts the all-gather half straight into the
     next rank's receive buffer: recvReduceCopySend moves f + 3 (FIFO in, own
     input, own output, next output), recvCopySend 2 (own output in, next
     output out), recv 0.  Summed: B = [4 + 2f + (N-2)(3 + 2f)] * M, which is
-    (5N-4) M for Simple."""
+    (5N-4) M for Simple.  The direct read (Simple) drops the loop's opening
+    send (1 + f) and has the next rank read the raw input from the sender's
+    buffer instead of the FIFO (the same f = 1 bytes): 2 M less."""
     f = FIFO_FACTOR[proto]
     if direct:
         per_m = (1 + f) + (f + 3) + (nranks - 2) * ((1 + 2 * f) + 2)
     else:
         per_m = 4 + 4 * f + 2 * (nranks - 2) * (2 * f + 1)
+    if direct_read:
+        per_m -= 1 + f
     return float(per_m * message_bytes)
 
 

@@ -544,6 +544,9 @@ def test_algorithmic_bytes():
     assert abs(metrics.algorithmic_bytes(M, 4, "LL128") - 20.8 * M) < 1
     for N in (2, 3, 4, 8):
         assert metrics.algorithmic_bytes(M, N, "SIMPLE", direct=True) == (5 * N - 4) * M
+        assert metrics.algorithmic_bytes(M, N, "SIMPLE", direct_read=True) == (6 * N - 6) * M
+        assert metrics.algorithmic_bytes(M, N, "SIMPLE", direct=True,
+                                         direct_read=True) == (5 * N - 6) * M
 
 
 # ------------------------------------------------------------- direct variant
@@ -637,3 +640,50 @@ def test_per_channel_rings_match_closed_form(key):
         np.testing.assert_array_equal(
             out[0][0], cf.allreduce([x], g["base"], (1 << g["channels"]) - 1, proto,
                                     SMALL_BUFF[proto], 4, "float32")[0])
+
+
+# ------------------------------------------------- direct read (f1)
+@pytest.mark.parametrize("N", [2, 3, 4, 8])
+def test_direct_read_same_result(N):
+    """Direct read (course 23, "发布顺序与 Fence"): the first receive of every
+    loop takes the previous rank's raw input from its send buffer instead of
+    the FIFO.  The data is the same, so every value matches the FIFO path, in
+    place and out of place, with and without the direct all-gather, under
+    random interleavings.  Reading the wrong rank's buffer or offset would
+    change the fold and fail here."""
+    rng = np.random.default_rng(100 + N)
+    order = [int(v) for v in rng.permutation(N)]
+    x = _draw("float32", (N, 30011), N + 1)
+    base = oracle.allreduce([x], order, 0x5, "SIMPLE", SMALL_BUFF["SIMPLE"], 4, "float32")[1][0]
+    for in_place in (False, True):
+        for direct in (False, True):
+            for sched, seed in ((0, 0), (1, 3)):
+                rc, out, _, _ = oracle.allreduce([x], order, 0x5, "SIMPLE", SMALL_BUFF["SIMPLE"],
+                                                 4, "float32", in_place=in_place, sched=sched,
+                                                 seed=seed, direct=direct, direct_read=True)
+                assert rc == oracle.OK
+                np.testing.assert_array_equal(out[0], base)
+
+
+def test_direct_read_needs_simple():
+    x = np.ones((4, 64), dtype=np.float32)
+    for proto in ("LL", "LL128"):
+        assert oracle.allreduce([x], [0, 1, 2, 3], 1, proto, SMALL_BUFF[proto], 4, "float32",
+                                direct_read=True)[0] == oracle.INVALID
+
+
+def test_fifo_bytes_of_the_direct_variants():
+    """FIFO bytes written per rank, per collective of M bytes: 2(N-1) M/N
+    through the FIFO; (N-1) M/N with the direct all-gather (only the
+    reduce-scatter half uses the FIFO); (N-2) M/N with direct read as well
+    (the loop's opening send moves nothing)."""
+    N, count = 4, 4 * 8192
+    x = np.ones((N, count), dtype=np.float32)
+    M = count * 4
+    for kw, chunks in ((dict(), 2 * (N - 1)), (dict(direct=True), N - 1),
+                       (dict(direct_read=True), 2 * (N - 1) - 1),
+                       (dict(direct=True, direct_read=True), N - 2)):
+        rc, _, st, _ = oracle.allreduce([x], [0, 1, 2, 3], 0x1, "SIMPLE", 65536, 4, "float32", **kw)
+        assert rc == oracle.OK
+        for r in range(N):
+            assert st.wire_sent[r] == chunks * M // N, (kw, r)
