@@ -129,7 +129,8 @@ def main():
     ap.add_argument("--launch-mode", type=int, default=None, choices=[0, 1])
     ap.add_argument("--slices", type=int, default=None, choices=[1, 2, 4])
     ap.add_argument("--placement", type=int, default=None, choices=[0, 1])
-    ap.add_argument("--direct", type=int, default=None, choices=[0, 1])
+    ap.add_argument("--direct", type=int, default=None, choices=[0, 1, 2, 3],
+                    help="Simple direct variants: bit 0 write, bit 1 read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the AllReduce, time a plain device copy of MIB MiB "
@@ -248,7 +249,9 @@ def main():
     M = w.message_bytes
     algbw = metrics.algbw_gbps(M, t_step)
     busbw = metrics.busbw_gbps(M, t_step, N)
-    alg_bytes = metrics.algorithmic_bytes(M, N, w.proto, direct=bool(tune.get("direct", 0)))
+    d = int(tune.get("direct", 0))
+    alg_bytes = metrics.algorithmic_bytes(M, N, w.proto, direct=bool(d & 1),
+                                          direct_read=bool(d & 2))
     achieved = alg_bytes / t_kernel / 1e9
     traffic = measured_traffic(args.workload, {"lanes": shape["lanes"], "waves": shape["waves"]})
     out = {
@@ -273,6 +276,7 @@ def main():
             "grid": shape["grid"], "parallelism": f"{N} virtual ranks on 1 GPU",
             "launch": "plain" if tune.get("launch_mode", 0) == 1 else "cooperative",
             "misalign_elems": args.misalign,
+            "direct": int(tune.get("direct", 0)),
         },
         "algbw_GBps": round(algbw, 3),
         "busbw_GBps": round(busbw, 3),

@@ -103,16 +103,20 @@ typedef struct {
                             and every call still consumes chunk_steps steps;
                             smaller slices keep fewer FIFO bytes in flight.
                             Timing only: results are identical            */
-  int direct;            /* Simple only, 0 or 1: the direct variants of the
-                            all-gather half [C23 "发布顺序与 Fence"].  The
-                            rank that completes a chunk, and every rank that
-                            forwards it, writes it straight into the next
-                            rank's receive buffer instead of the FIFO (no
-                            send credit needed); the final receive has nothing
-                            to copy.  Steps still advance on every connector.
-                            Same results; (5N-4)M instead of (6N-4)M bytes
-                            of traffic.  Receive buffers of different ranks
-                            must not overlap.                             */
+  int direct;            /* Simple only, bit mask of the direct variants
+                            [C23 "发布顺序与 Fence", direct read/write].
+                            Bit 0, direct write: the rank that completes a
+                            chunk, and every rank that forwards it, writes it
+                            straight into the next rank's receive buffer
+                            instead of the FIFO (no send credit needed); the
+                            final receive has nothing to copy.  Bit 1, direct
+                            read: the loop's opening send moves nothing and
+                            the next rank's first receive reads the raw input
+                            from the sender's send buffer.  Steps still
+                            advance on every connector.  Same results; bytes
+                            of traffic (6N-4)M, (5N-4)M with bit 0, (6N-6)M
+                            with bit 1, (5N-6)M with both.  Buffers of
+                            different ranks must not overlap.              */
 } rar_tuning_t;
 
 #define RAR_DEBUG_DROP_RECV_HEAD 1

@@ -323,7 +323,8 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
     return fail(RAR_INVALID_ARGUMENT, "slices_per_chunk must be 0, 1, 2 or 4");
   if (tune.slices_per_chunk == 4 && (int)proto == rar::kSimple && chunk_steps != 4)
     return fail(RAR_INVALID_ARGUMENT, "4 slices per chunk need chunk_steps 4");
-  if (tune.direct != 0 && tune.direct != 1) return fail(RAR_INVALID_ARGUMENT, "direct must be 0 or 1");
+  if (tune.direct < 0 || tune.direct > 3)
+    return fail(RAR_INVALID_ARGUMENT, "direct must be 0..3 (bit 0 write, bit 1 read)");
   if (tune.direct && (int)proto != rar::kSimple)
     return fail(RAR_UNSUPPORTED, "the direct variant exists for the Simple protocol only");
 

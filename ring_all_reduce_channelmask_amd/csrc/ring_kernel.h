@@ -165,8 +165,9 @@ struct Ctx {
   Shmem* sh;
   void* const* ptrs;
   int tid, nthreads, workers;
-  int rank, next, nranks, ring_index, lane, nlanes, sps, spc;
-  bool direct;  // Simple: all-gather half straight into the next rank's receive buffer
+  int rank, next, prev, nranks, ring_index, lane, nlanes, sps, spc;
+  bool direct;       // Simple: all-gather half straight into the next rank's receive buffer
+  bool direct_read;  // Simple: the loop's first receive reads the previous rank's send buffer
   int64_t step_bytes;       // channel slot: sets the slice geometry
   int64_t lane_step_bytes;  // this lane's slot in its own FIFO
   uint8_t* recv_fifo;
@@ -400,13 +401,19 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
 // "发布顺序与 Fence", "Slice Size"].  Empty slices still wait and post.
 template <class Ty, int OP>
 __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
-                            typename Ty::S* next_dst, int64_t nelem, int chunk) {
+                            typename Ty::S* next_dst, const typename Ty::S* prev_src, bool raw,
+                            int64_t nelem, int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
   // Direct variants [C23 "发布顺序与 Fence"]: the final value goes straight
   // into the next rank's receive buffer (no FIFO slot: no credit wait), and
   // the all-gather receivers find their data in their own receive buffer.
+  // With the direct read the loop's opening send moves nothing and the next
+  // rank's first receive (`raw`) reads the raw input from this rank's send
+  // buffer (prev_src on its side).  Steps, waits and posts are unchanged.
   const bool direct_send = cx.direct && (OP == kOpRecvReduceCopySend || OP == kOpRecvCopySend);
+  const bool skip_send = cx.direct_read && OP == kOpSend;
+  const bool read_prev = cx.direct_read && raw;
   constexpr int kVec = 16 / sizeof(S);
   const int sps = cx.sps;
   const int64_t step_elems = cx.step_bytes / (int64_t)sizeof(S);
@@ -428,7 +435,7 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
     if (cx.tid < 2) {
       bool ok = true;
       if (cx.tid == 0 && O::kRecv) ok = wait_cached(cx.recv_tail, cx.recv_step + sps, cx.tail_cache, cx);
-      if (cx.tid == 1 && O::kSend && !direct_send) ok = wait_credit(cx, sps);
+      if (cx.tid == 1 && O::kSend && !direct_send && !skip_send) ok = wait_credit(cx, sps);
       acquire_fence();
       if (!ok) cx.sh->abort = 1;
     }
@@ -438,11 +445,24 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
       return;
     }
     const uint64_t t1 = cx.trace ? now_ticks() : 0;
-    if (cx.tid < cx.workers && hi > lo) {
+    if (cx.tid < cx.workers && hi > lo && !skip_send) {
       const S* fin = reinterpret_cast<const S*>(cx.recv_fifo + (cx.recv_step % kSteps) * cx.lane_step_bytes);
       S* fout = reinterpret_cast<S*>(cx.send_fifo + (cx.send_step % kSteps) * cx.lane_step_bytes);
       const int64_t e0 = s_off + lo;
-      if (!cx.direct || OP == kOpSend || OP == kOpRecvReduceSend) {
+      if (read_prev && OP == kOpRecvReduceSend) {
+        // previous rank's raw input + own input -> FIFO
+        reduce_copy<Ty, true, true, false, true, true, false>(prev_src + e0, src + e0, dst + e0, fout,
+                                                              hi - lo, cx.tid, cx.workers, cx.nranks);
+      } else if (read_prev && OP == kOpRecvReduceCopySend) {
+        // two ranks: previous rank's raw input + own input -> own output, forwarded
+        if (cx.direct)
+          reduce_copy<Ty, true, true, true, true, true, true>(prev_src + e0, src + e0, dst + e0,
+                                                              next_dst + e0, hi - lo, cx.tid,
+                                                              cx.workers, cx.nranks);
+        else
+          reduce_copy<Ty, true, true, true, true, true, false>(prev_src + e0, src + e0, dst + e0, fout,
+                                                               hi - lo, cx.tid, cx.workers, cx.nranks);
+      } else if (!cx.direct || OP == kOpSend || OP == kOpRecvReduceSend) {
         reduce_copy<Ty, O::kRecv, O::kSrc, O::kDst, O::kSend>(fin, src + e0, dst + e0, fout, hi - lo,
                                                                cx.tid, cx.workers, cx.nranks);
       } else if (OP == kOpRecvReduceCopySend) {
@@ -468,7 +488,7 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
     // a receiver on another XCD additionally needs them written back.
     if (cx.tid == cx.nthreads - 2 && O::kRecv && !cx.drop_head) store_relaxed(cx.recv_head, cx.recv_step);
     if (cx.tid == cx.nthreads - 1 && O::kSend) {
-      if (!cx.local_send) release_fence();
+      if (!cx.local_send && !skip_send) release_fence();
       store_relaxed(cx.send_tail, cx.send_step);
     }
   }
@@ -755,13 +775,14 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
 // ---------------------------------------------------------------- runRing
 template <class Ty, int PROTO, int OP>
 __device__ __forceinline__ void prim(Ctx& cx, const typename Ty::S* sendbuf, typename Ty::S* recvbuf,
-                                     typename Ty::S* next_recvbuf, int64_t base, int64_t cc,
-                                     int64_t rem, int chunk) {
+                                     typename Ty::S* next_recvbuf, const typename Ty::S* prev_sendbuf,
+                                     bool raw, int64_t base, int64_t cc, int64_t rem, int chunk) {
   const int64_t chunk_off = (int64_t)chunk * cc;
   const int64_t nelem = clamp64(rem - chunk_off, 0, cc);
   const int64_t off = base + chunk_off;
   if (PROTO == kSimple)
-    simple_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, next_recvbuf + off, nelem, chunk);
+    simple_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, next_recvbuf + off, prev_sendbuf + off, raw,
+                        nelem, chunk);
   else if (PROTO == kLL)
     ll_call<Ty, OP>(cx, sendbuf + off, recvbuf + off, nelem, chunk);
   else
@@ -780,6 +801,7 @@ __device__ void run_ring(Ctx& cx, const DevWork& w) {
   const S* sendbuf = reinterpret_cast<const S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.rank) * 2]);
   S* recvbuf = reinterpret_cast<S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.rank) * 2 + 1]);
   S* next_recvbuf = reinterpret_cast<S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.next) * 2 + 1]);
+  const S* prev_sendbuf = reinterpret_cast<const S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.prev) * 2]);
   int workers = (int)w.n_waves * kWaveSize;
   cx.workers = workers < cx.nthreads ? workers : cx.nthreads;
   const int64_t loop_count = (int64_t)N * w.chunk_count;
@@ -788,17 +810,21 @@ __device__ void run_ring(Ctx& cx, const DevWork& w) {
     const int64_t cc = rem < loop_count ? align_up(div_up(rem, N), kVec) : w.chunk_count;
     const int64_t base = w.grid_offset + eo;
     auto mod = [N](int x) { return ((x % N) + N) % N; };
-    prim<Ty, PROTO, kOpSend>(cx, sendbuf, recvbuf, next_recvbuf, base, cc, rem, mod(ix - 1));
+    // the call right after the opening send receives that send's raw input
+    prim<Ty, PROTO, kOpSend>(cx, sendbuf, recvbuf, next_recvbuf, prev_sendbuf, false, base, cc, rem,
+                             mod(ix - 1));
     for (int j = 2; j < N && !cx.aborted; ++j)
-      prim<Ty, PROTO, kOpRecvReduceSend>(cx, sendbuf, recvbuf, next_recvbuf, base, cc, rem,
-                                         mod(ix - j));
+      prim<Ty, PROTO, kOpRecvReduceSend>(cx, sendbuf, recvbuf, next_recvbuf, prev_sendbuf, j == 2,
+                                         base, cc, rem, mod(ix - j));
     if (cx.aborted) return;
-    prim<Ty, PROTO, kOpRecvReduceCopySend>(cx, sendbuf, recvbuf, next_recvbuf, base, cc, rem, ix);
+    prim<Ty, PROTO, kOpRecvReduceCopySend>(cx, sendbuf, recvbuf, next_recvbuf, prev_sendbuf, N == 2,
+                                           base, cc, rem, ix);
     for (int j = 1; j < N - 1 && !cx.aborted; ++j)
-      prim<Ty, PROTO, kOpRecvCopySend>(cx, sendbuf, recvbuf, next_recvbuf, base, cc, rem,
-                                       mod(ix - j));
+      prim<Ty, PROTO, kOpRecvCopySend>(cx, sendbuf, recvbuf, next_recvbuf, prev_sendbuf, false, base,
+                                       cc, rem, mod(ix - j));
     if (cx.aborted) return;
-    prim<Ty, PROTO, kOpRecv>(cx, sendbuf, recvbuf, next_recvbuf, base, cc, rem, mod(ix + 1));
+    prim<Ty, PROTO, kOpRecv>(cx, sendbuf, recvbuf, next_recvbuf, prev_sendbuf, false, base, cc, rem,
+                             mod(ix + 1));
     if (cx.aborted) return;
   }
 }
@@ -882,7 +908,9 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   const DevRank me = comm->ranks[sh.channel_id][rank];
   cx.ring_index = me.index;
   cx.next = me.next;
-  cx.direct = sh.comm.direct != 0;
+  cx.direct = (sh.comm.direct & 1) != 0;
+  cx.direct_read = (sh.comm.direct & 2) != 0;
+  cx.prev = me.prev;
   cx.lane = lane;
   cx.nlanes = sh.comm.n_lanes;
   cx.sps = sh.comm.step_per_slice;

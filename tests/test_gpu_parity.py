@@ -417,3 +417,52 @@ def test_ll_flag_wrap_mode_over_many_wraps(lanes):
     steps = comm.query_state()
     assert min(steps[1::2]) > 4 * 256, "each connector should have crossed several wraps"
     comm.close()
+
+
+# ------------------------------------------------- direct read
+@pytest.mark.parametrize("direct", [2, 3])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("N", [2, 3, 5])
+def test_direct_read_vs_oracle(direct, dtype, in_place, N):
+    """Direct read (bit 1), alone and with the direct write: the loop's first
+    receive reads the previous rank's send buffer.  N = 2 takes it in the
+    fused final step, N > 2 in the first recvReduceSend.  Same bits as the
+    oracle's direct simulation and its FIFO simulation."""
+    order = [[1, 0], [2, 0, 1], [0, 3, 1, 4, 2]][[2, 3, 5].index(N)]
+    buff = SMALL_BUFF["SIMPLE"] * 2
+    comm = _comm(nranks=N, ring_order=order, mask=0x5, proto="SIMPLE", buff_size=buff,
+                 lanes=3, waves=4, direct=direct)
+    x = _rand(dtype, (N, 150011), 61 + N)
+    got = run_hip(comm, [x], dtype, in_place=in_place)[0]
+    comm.close()
+    for kw in (dict(direct=bool(direct & 1), direct_read=True), dict()):
+        rc, want, _, _ = oracle.allreduce([x], order, 0x5, "SIMPLE", buff, 4, dtype, **kw)
+        assert rc == oracle.OK
+        for r in range(N):
+            assert_bits_equal(got[r], want[0][r], f"{kw} rank {r}")
+
+
+@pytest.mark.parametrize("placement", [0, 1])
+def test_direct_read_write_full_size_and_many_launches(placement):
+    """64 MiB with both direct variants in the benchmark's launch shape, 100
+    launches on one communicator, every element against the closed form."""
+    import torch
+    import ring_all_reduce_channelmask_amd as rar
+    from .gpu_util import to_device, to_host
+    w = wl.WORKLOADS["simple_64m"]
+    x = wl.inputs_for(w)[0]
+    tune = dict(_bench_tuning()["simple_64m"])
+    tune.update(direct=3, placement=placement)
+    comm = _comm(nranks=4, ring_order=list(w.ring_order), mask=w.mask, proto="SIMPLE",
+                 buff_size=w.buff_size, chunk_steps=4, **tune)
+    sends = [to_device(x[r], "float32") for r in range(4)]
+    recvs = [torch.empty_like(t) for t in sends]
+    for _ in range(100):
+        comm.allreduce(sends, recvs)
+    torch.cuda.synchronize()
+    assert comm.async_error() == 0
+    comm.close()
+    want = cf.allreduce([x], list(w.ring_order), w.mask, "SIMPLE", w.buff_size, 4, "float32")[0]
+    for r in range(4):
+        assert_bits_equal(to_host(recvs[r], "float32"), want, f"rank {r}")
