@@ -29,12 +29,25 @@ __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
+// ---------------------------------------------------------------- addressing
+// Every FIFO, counter and user buffer lives in device (or host-mapped)
+// memory.  Their pointers reach the kernel as generic pointers, which would
+// compile to FLAT instructions; FLAT accesses may complete out of order with
+// LDS and scalar traffic, so the compiler must wait for everything
+// outstanding before using any of their results.  Accessing them through
+// the global address space gives GLOBAL instructions whose completions are
+// counted in order: loads stay in flight while earlier results are used.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* G(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 // ---------------------------------------------------------------- ordering
 __device__ __forceinline__ uint64_t load_relaxed(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(G(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void store_relaxed(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(G(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void acquire_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void release_fence() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
@@ -44,9 +57,11 @@ __device__ __forceinline__ uint32_t xcc_id() {
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
   return v & 0xFu;
 }
-// Wait until every vector memory operation this wave issued has completed,
-// so that a barrier that follows also covers this wave's payload stores.
-__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until every memory operation this wave issued has completed, so that
+// a barrier that follows also covers this wave's payload stores.  The FIFO
+// and user pointers are generic, so their accesses are FLAT instructions,
+// which count in both vmcnt and lgkmcnt: wait for both.
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------- arithmetic
 // A 16-byte vector is four 32-bit words; each word holds one fp32 / int32 or
@@ -219,12 +234,12 @@ __device__ __forceinline__ void trace_unit(Ctx& cx, int op, int chunk, int64_t n
 // abort]: after `timeout` ticks of the 100 MHz clock the waiter raises the
 // communicator's abort word and every other waiter leaves on seeing it.
 __device__ void raise_abort(Ctx& cx) {
-  __hip_atomic_store(cx.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(cx.abort_host, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(G(cx.abort_flag), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(G(cx.abort_host), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 __device__ __forceinline__ bool should_stop(Ctx& cx, uint64_t t0) {
-  if (__hip_atomic_load(cx.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return true;
+  if (__hip_atomic_load(G(cx.abort_flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return true;
   if (__builtin_amdgcn_s_memrealtime() - t0 > cx.timeout) {
     raise_abort(cx);
     return true;
@@ -310,6 +325,9 @@ __device__ __forceinline__ v4u post16(v4u a, int n) {
 // slots stay 16-byte aligned.
 typedef uint32_t v4u_user __attribute__((ext_vector_type(4), aligned(2)));
 typedef uint64_t u64_user __attribute__((aligned(2)));
+typedef __attribute__((address_space(1))) v4u_user g_v4u_user;
+typedef __attribute__((address_space(1))) u64_user g_u64_user;
+typedef __attribute__((address_space(1))) v4u g_v4u;
 
 // Vector i of a buffer: kUser = element-aligned user buffer, else a FIFO
 // slot.  The pointer types are spelled out here (an alignment attribute on a
@@ -317,11 +335,11 @@ typedef uint64_t u64_user __attribute__((aligned(2)));
 template <bool kNt, bool kUser>
 __device__ __forceinline__ v4u ldv(const void* base, int64_t i) {
   if constexpr (kUser) {
-    const v4u_user* p = reinterpret_cast<const v4u_user*>(base) + i;
+    const g_v4u_user* p = (const g_v4u_user*)base + i;
     if constexpr (kNt) return __builtin_nontemporal_load(p);
     else return *p;
   } else {
-    const v4u* p = reinterpret_cast<const v4u*>(base) + i;
+    const g_v4u* p = (const g_v4u*)base + i;
     if constexpr (kNt) return __builtin_nontemporal_load(p);
     else return *p;
   }
@@ -329,12 +347,12 @@ __device__ __forceinline__ v4u ldv(const void* base, int64_t i) {
 template <bool kNt, bool kUser>
 __device__ __forceinline__ void stv(void* base, int64_t i, v4u v) {
   if constexpr (kUser) {
-    v4u_user* p = reinterpret_cast<v4u_user*>(base) + i;
+    g_v4u_user* p = (g_v4u_user*)base + i;
     const v4u_user w = v;
     if constexpr (kNt) __builtin_nontemporal_store(w, p);
     else *p = w;
   } else {
-    v4u* p = reinterpret_cast<v4u*>(base) + i;
+    g_v4u* p = (g_v4u*)base + i;
     if constexpr (kNt) __builtin_nontemporal_store(v, p);
     else *p = v;
   }
@@ -386,12 +404,12 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
   }
   for (int64_t e = nv * kVec + tid; e < n; e += nthr) {
     S a = 0, b = 0;
-    if (kRecv) a = fin[e];
-    if (kSrc) b = src[e];
+    if (kRecv) a = G(fin)[e];
+    if (kSrc) b = G(src)[e];
     S r = (kRecv && kSrc) ? Ty::red_elem(a, b) : (kRecv ? a : b);
     if constexpr (kPost) r = Ty::post_elem(r, n_post);
-    if (kDst) dst[e] = r;
-    if (kSend) fout[e] = r;
+    if (kDst) G(dst)[e] = r;
+    if (kSend) G(fout)[e] = r;
   }
 }
 
@@ -530,19 +548,19 @@ __device__ bool ll_wait_line(const uint64_t* line, uint32_t flag, uint64_t& a, u
 
 template <class S>
 __device__ __forceinline__ uint64_t load_bytes8(const uint8_t* p, int64_t valid) {
-  if (valid >= 8) return *reinterpret_cast<const u64_user*>(p);
+  if (valid >= 8) return *(const g_u64_user*)p;
   uint64_t v = 0;
   for (int64_t b = 0; b < valid; b += sizeof(S))
-    v |= (uint64_t)(*reinterpret_cast<const S*>(p + b)) << (8 * b);
+    v |= (uint64_t)(*G(reinterpret_cast<const S*>(p + b))) << (8 * b);
   return v;
 }
 template <class S>
 __device__ __forceinline__ void store_bytes8(uint8_t* p, uint64_t v, int64_t valid) {
   if (valid >= 8) {
-    *reinterpret_cast<u64_user*>(p) = v;
+    *(g_u64_user*)p = v;
     return;
   }
-  for (int64_t b = 0; b < valid; b += sizeof(S)) *reinterpret_cast<S*>(p + b) = (S)(v >> (8 * b));
+  for (int64_t b = 0; b < valid; b += sizeof(S)) *G(reinterpret_cast<S*>(p + b)) = (S)(v >> (8 * b));
 }
 
 template <class Ty, int OP>
@@ -723,7 +741,7 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
           own[u] = zero;
           if (j < hi) {
             if (O::kRecv) {
-              in[u] = *reinterpret_cast<const v4u*>(rl + 16 * j + 2 * k);
+              in[u] = *G(reinterpret_cast<const v4u*>(rl + 16 * j + 2 * k));
               if (k == 7) in[u].z = in[u].w = 0;  // the flag word is not payload
             }
             if (O::kSrc) own[u] = load_bytes16<S>(sb + 120 * j + 16 * k, nbytes - (120 * j + 16 * k), cap);
@@ -740,9 +758,9 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
           if (O::kSend) {
             uint64_t* w = sl + 16 * j + 2 * k;
             if (k < 7) {
-              *reinterpret_cast<v4u*>(w) = v;
+              *G(reinterpret_cast<v4u*>(w)) = v;
             } else {
-              w[0] = (uint64_t)v.x | ((uint64_t)v.y << 32);
+              *G(w) = (uint64_t)v.x | ((uint64_t)v.y << 32);
             }
           }
         }
@@ -798,10 +816,11 @@ __device__ void run_ring(Ctx& cx, const DevWork& w) {
   using S = typename Ty::S;
   constexpr int kVec = 16 / sizeof(S);
   const int N = cx.nranks, ix = cx.ring_index;
-  const S* sendbuf = reinterpret_cast<const S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.rank) * 2]);
-  S* recvbuf = reinterpret_cast<S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.rank) * 2 + 1]);
-  S* next_recvbuf = reinterpret_cast<S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.next) * 2 + 1]);
-  const S* prev_sendbuf = reinterpret_cast<const S*>(cx.ptrs[((int64_t)w.buf_index * N + cx.prev) * 2]);
+  void* const* ptrs = cx.ptrs;
+  const S* sendbuf = reinterpret_cast<const S*>(G(ptrs)[((int64_t)w.buf_index * N + cx.rank) * 2]);
+  S* recvbuf = reinterpret_cast<S*>(G(ptrs)[((int64_t)w.buf_index * N + cx.rank) * 2 + 1]);
+  S* next_recvbuf = reinterpret_cast<S*>(G(ptrs)[((int64_t)w.buf_index * N + cx.next) * 2 + 1]);
+  const S* prev_sendbuf = reinterpret_cast<const S*>(G(ptrs)[((int64_t)w.buf_index * N + cx.prev) * 2]);
   int workers = (int)w.n_waves * kWaveSize;
   cx.workers = workers < cx.nthreads ? workers : cx.nthreads;
   const int64_t loop_count = (int64_t)N * w.chunk_count;
