@@ -204,7 +204,8 @@ std::vector<uint32_t> make_wg_map(int nranks, int n_channels, int n_lanes, bool 
 }
 
 int64_t lane_step_bytes(int proto, size_t buff_size, int lanes) {
-  const int64_t unit = proto == kLL128 ? 128 : 16;
+  // LL128 lanes take an even number of 128-byte lines
+  const int64_t unit = proto == kLL128 ? 256 : 16;
   const int64_t step_units = (int64_t)buff_size / kSteps / unit;
   return unit * div_up(step_units, lanes);
 }

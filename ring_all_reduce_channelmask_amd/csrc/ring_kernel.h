@@ -200,6 +200,7 @@ struct Ctx {
   uint64_t timeout;
   bool drop_head;  // fault test: never publish head credit
   uint32_t ll_mask;  // LL flag period - 1: 2^32 - 1, or 0xFF in the wrap test mode
+  uint8_t* stage;    // LL128: per-wave LDS tiles for the user <-> line layout change
   bool aborted;
   // The receiving workgroup of the send connector shares this workgroup's L2:
   // payload stores that have completed (vmcnt drained) are already visible to
@@ -660,7 +661,14 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
 // receiver is on another XCD), then the flag words.  Receiver: the flag lanes
 // poll every line of the wave, the wave votes until none is missing, then one
 // acquire fence precedes the data loads.
-constexpr int kLl128Unroll = 4;
+constexpr int kLl128Unroll = 2;  // groups of 8 lines in flight per wave
+
+// Orders this wave's LDS accesses around a hand-off between its lanes.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <class S>
 __device__ __forceinline__ v4u load_bytes16(const uint8_t* p, int64_t valid, int64_t cap) {
@@ -685,7 +693,9 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
   constexpr int U = kLl128Unroll;
   const int64_t nbytes = nelem * (int64_t)sizeof(S);
   const int64_t nlines = div_up(nbytes, 120);
-  const int64_t part = div_up(nlines, cx.nlanes);
+  // lanes take an even number of lines, so every group of 8 lines starts
+  // 16-byte aligned in the user buffer (120 x 2 = 15 x 16)
+  const int64_t part = 2 * div_up(nlines, 2 * (int64_t)cx.nlanes);
   const int64_t lo = clamp64((int64_t)cx.lane * part, 0, nlines);
   const int64_t hi = clamp64(lo + part, 0, nlines);
   const uint64_t t0 = cx.trace ? now_ticks() : 0;
@@ -693,7 +703,7 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
   const int wave = cx.tid >> 6, lid = cx.tid & 63, nw = cx.workers >> 6;
   const int sub = lid >> 3;  // line within the wave's group of 8
   const int k = lid & 7;     // 16-byte segment of the line
-  const int64_t cap = k < 7 ? 16 : 8;
+
   const int64_t first = lo + (int64_t)wave * 8, stride = (int64_t)nw * 8;
   const bool active = wave < nw && first < hi;
   bool ok = true;
@@ -705,64 +715,109 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
   uint64_t* sl = reinterpret_cast<uint64_t*>(cx.send_fifo + (cx.send_step % kSteps) * cx.lane_step_bytes) - 16 * lo;
   const uint8_t* sb = reinterpret_cast<const uint8_t*>(src);
   uint8_t* db = reinterpret_cast<uint8_t*>(dst);
-  if (active && ok) {
-    if (O::kRecv) {
+  // Receive: wave 0 polls the flags of every line of this lane's share and
+  // then issues one agent-scope acquire; the barrier hands that ordering to
+  // the other waves, which load data only after it.  One L1 invalidation per
+  // workgroup and step, not one per wave.  Flags to different lines need not
+  // arrive in order, so every line is checked; between rounds the wave
+  // sleeps, leaving the memory system to the data.
+  if (O::kRecv) {
+    if (wave == 0 && lo < hi) {
       const uint64_t tp = __builtin_amdgcn_s_memrealtime();
       for (uint32_t it = 1;; ++it) {
         bool pending = false;
-        if (k == 7) {
-          for (int64_t g0 = first; g0 < hi; g0 += (int64_t)U * stride) {
-            uint64_t f[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-              const int64_t j = g0 + (int64_t)u * stride + sub;
-              f[u] = j < hi ? load_relaxed(rl + 16 * j + 15) : rflag;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) pending = pending || f[u] != rflag;
-          }
-        }
+        for (int64_t j = lo + lid; j < hi; j += 64) pending |= load_relaxed(rl + 16 * j + 15) != rflag;
         if (!__any(pending)) break;
+        __builtin_amdgcn_s_sleep(1);
         if ((it & 15u) == 0 && should_stop(cx, tp)) {
           ok = false;
           break;
         }
       }
       if (ok) acquire_fence();
+      else cx.sh->abort = 1;
     }
+    __syncthreads();
+    if (cx.sh->abort) ok = false;
+  }
+  if (active && ok) {
     if (ok) {
+      // A wave moves groups of 8 lines: 960 payload bytes, 1 KiB of FIFO.
+      // User data goes through an LDS tile [C23 "LL128：15/16 Payload" stages
+      // user data through shared memory]: 60 lanes load or store 16
+      // contiguous user bytes each, and the tile is read or written in
+      // line layout (lane (line, segment), 16 bytes, 8 in the last segment).
+      // Every lane then stores its 16 FIFO bytes with one instruction; the
+      // flag word gets a placeholder 0 that never matches a flag, and the
+      // real flag follows after the drain below.
+      constexpr bool kNu = RAR_NT_USER != 0;
+      uint8_t* stage = cx.stage + (int64_t)wave * U * 1024;
+      const int64_t ub = 16 * (int64_t)lid;  // this lane's 16 bytes of a group, user layout
+      const bool ulane = lid < 60;
+      const v4u zero = {0, 0, 0, 0};
       for (int64_t g0 = first; g0 < hi; g0 += (int64_t)U * stride) {
         v4u in[U], own[U];
+        int64_t gb[U], gvalid[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t j = g0 + (int64_t)u * stride + sub;
-          const v4u zero = {0, 0, 0, 0};
+          const int64_t gs = g0 + (int64_t)u * stride;  // first line of group u
+          const int64_t ge = gs + 8 < hi ? gs + 8 : hi;
+          gb[u] = 120 * gs;
+          const int64_t gend = 120 * ge < nbytes ? 120 * ge : nbytes;
+          gvalid[u] = gs < hi ? gend - gb[u] : 0;  // payload bytes of the group
+          const int64_t j = gs + sub;
           in[u] = zero;
           own[u] = zero;
-          if (j < hi) {
-            if (O::kRecv) {
-              in[u] = *G(reinterpret_cast<const v4u*>(rl + 16 * j + 2 * k));
-              if (k == 7) in[u].z = in[u].w = 0;  // the flag word is not payload
-            }
-            if (O::kSrc) own[u] = load_bytes16<S>(sb + 120 * j + 16 * k, nbytes - (120 * j + 16 * k), cap);
+          if (O::kRecv && j < hi) {
+            in[u] = *G(reinterpret_cast<const v4u*>(rl + 16 * j + 2 * k));
+            if (k == 7) in[u].z = in[u].w = 0;  // the flag word is not payload
+          }
+          if (O::kSrc && ulane) {
+            v4u x = zero;
+            if (ub + 16 <= gvalid[u]) x = ldv<kNu, true>(sb + gb[u] + ub, 0);
+            else if (ub < gvalid[u]) x = load_bytes16<S>(sb + gb[u] + ub, gvalid[u] - ub, 16);
+            *reinterpret_cast<v4u*>(stage + u * 1024 + ub) = x;
           }
         }
+        if (O::kSrc) {
+          wave_sync();
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const uint8_t* q = stage + u * 1024 + 120 * sub + 16 * k;
+            const uint64_t w0 = *reinterpret_cast<const uint64_t*>(q);
+            const uint64_t w1 = k < 7 ? *reinterpret_cast<const uint64_t*>(q + 8) : 0;
+            own[u].x = (uint32_t)w0;
+            own[u].y = (uint32_t)(w0 >> 32);
+            own[u].z = (uint32_t)w1;
+            own[u].w = (uint32_t)(w1 >> 32);
+          }
+          wave_sync();  // the tile is read before it is written again
+        }
+        v4u v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+          v[u] = (O::kRecv && O::kSrc) ? red16<Ty>(in[u], own[u]) : (O::kRecv ? in[u] : own[u]);
+          if constexpr (OP == kOpRecvReduceCopySend && Ty::kPost) v[u] = post16<Ty>(v[u], cx.nranks);
+          if (k == 7) v[u].z = v[u].w = 0;  // flag placeholder
           const int64_t j = g0 + (int64_t)u * stride + sub;
-          if (j >= hi) continue;
-          v4u v = (O::kRecv && O::kSrc) ? red16<Ty>(in[u], own[u]) : (O::kRecv ? in[u] : own[u]);
-          if constexpr (OP == kOpRecvReduceCopySend && Ty::kPost) v = post16<Ty>(v, cx.nranks);
-          const int64_t b0 = 120 * j + 16 * k;
-          if (O::kDst) store_bytes16<S>(db + b0, v, nbytes - b0, cap);
-          if (O::kSend) {
-            uint64_t* w = sl + 16 * j + 2 * k;
-            if (k < 7) {
-              *G(reinterpret_cast<v4u*>(w)) = v;
-            } else {
-              *G(w) = (uint64_t)v.x | ((uint64_t)v.y << 32);
-            }
+          if (O::kSend && j < hi) *G(reinterpret_cast<v4u*>(sl + 16 * j + 2 * k)) = v[u];
+        }
+        if (O::kDst) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            uint8_t* q = stage + u * 1024 + 120 * sub + 16 * k;
+            *reinterpret_cast<uint64_t*>(q) = (uint64_t)v[u].x | ((uint64_t)v[u].y << 32);
+            if (k < 7) *reinterpret_cast<uint64_t*>(q + 8) = (uint64_t)v[u].z | ((uint64_t)v[u].w << 32);
           }
+          wave_sync();
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (!ulane) continue;
+            const v4u x = *reinterpret_cast<const v4u*>(stage + u * 1024 + ub);
+            if (ub + 16 <= gvalid[u]) stv<kNu, true>(db + gb[u] + ub, 0, x);
+            else if (ub < gvalid[u]) store_bytes16<S>(db + gb[u] + ub, x, gvalid[u] - ub, 16);
+          }
+          wave_sync();
         }
       }
       if (O::kSend) {
@@ -883,6 +938,7 @@ __device__ void load_batch(Shmem& sh, const KernelArgs& a, uint32_t b, int lid) 
 template <class Ty, int PROTO>
 __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   __shared__ Shmem sh;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[PROTO == kLL128 ? kMaxWaves * kLl128Unroll * 1024 : 16];
   const uint32_t m = args.wg_map[blockIdx.x];
   if (m == kIdleWg) return;
   const int tid = threadIdx.x, nthreads = blockDim.x;
@@ -957,6 +1013,7 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.timeout = sh.comm.spin_timeout_ticks;
   cx.drop_head = (sh.comm.debug_flags & 1) != 0;
   cx.ll_mask = sh.comm.ll_flag_mask;
+  cx.stage = stage;
   cx.aborted = false;
   cx.trace = (sh.comm.debug_flags & 2) ? sh.comm.trace + (int64_t)blockIdx.x * sh.comm.trace_cap : nullptr;
   cx.trace_n = 0;
