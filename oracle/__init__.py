@@ -32,7 +32,7 @@ DTYPE = {"int32": 0, "float32": 1, "bfloat16": 2}
 OPS = {0: "send", 1: "recvReduceSend", 2: "directRecvReduceCopySend",
        3: "directRecvCopySend", 4: "directRecv"}
 OK, DEADLOCK, INVALID, CORRUPT = 0, 1, 2, 3
-RED = {"sum": 0, "prod": 1, "max": 2, "min": 3, "avg": 4}
+RED = {"sum": 0, "prod": 1, "max": 2, "min": 3, "avg": 4, "premulsum": 5}
 FAULTS = {"none": 0, "drop_recv_head": 1, "tail_before_payload": 2, "ll_flag2_missing": 3,
           "ll_constant_flag": 4, "ll128_flag_missing": 5, "ll128_flag_before_data": 6}
 
@@ -96,6 +96,15 @@ def lib():
                                        ctypes.POINTER(ctypes.c_int64),
                                        ctypes.POINTER(ctypes.c_int64),
                                        ctypes.POINTER(ctypes.c_int64)]
+        L.orc_allreduce_premul.argtypes = [ctypes.c_int, ctypes.c_int, i32p, ctypes.c_uint64,
+                                           ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.POINTER(ctypes.c_void_p),
+                                           ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                           ctypes.c_int, ctypes.POINTER(Stats),
+                                           ctypes.POINTER(Call), ctypes.c_int64]
         L.orc_ll_wrap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, i32p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
         L.orc_bf16_round.argtypes = [ctypes.c_double]
@@ -147,14 +156,17 @@ def geometry(nranks, mask, proto, buff_size, chunk_steps, dtype, counts):
 
 def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
               in_place=False, slots=8, sched=0, seed=0, drop_recv_head=False,
-              direct=False, log_calls=False, op="sum", ll_wrap8=False, direct_read=False):
+              direct=False, log_calls=False, op="sum", ll_wrap8=False, direct_read=False,
+              scalars=None):
     """Run the simulator.
 
     ``inputs`` is a list over works of arrays shaped [N, count] holding the raw
     elements (int32, float32, or uint16 bit patterns for bfloat16).
     ``ring_order`` is one ring, or a list of rings (channel id c runs ring
-    c mod len(rings)).  Returns (rc, outputs, stats, calls): outputs is a list
-    over works of [N, count] arrays in the same representation.
+    c mod len(rings)).  ``op="premulsum"`` needs ``scalars``, an array
+    [works, N] of payload-type elements (rank r's scalar for work w).  Returns
+    (rc, outputs, stats, calls): outputs is a list over works of [N, count]
+    arrays in the same representation.
     """
     rings = [list(r) for r in ring_order] if isinstance(ring_order[0], (list, tuple)) \
         else [list(ring_order)]
@@ -187,10 +199,17 @@ def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
         (16 if direct_read else 0) | (RED[op] << 8)
     flat = [r for ring in rings for r in ring]
     assert all(len(ring) == N for ring in rings)
-    rc = lib().orc_allreduce_rings(N, len(rings), _ints(flat), mask, PROTO[proto], buff_size,
-                                   chunk_steps, DTYPE[dtype], len(works), carr, send_ptrs,
-                                   recv_ptrs, slots, sched, seed, options, ctypes.byref(stats),
-                                   log, cap)
+    if op == "premulsum":
+        sc = np.ascontiguousarray(scalars).reshape(len(works), N)
+        rc = lib().orc_allreduce_premul(N, len(rings), _ints(flat), mask, PROTO[proto], buff_size,
+                                        chunk_steps, DTYPE[dtype], len(works), carr, send_ptrs,
+                                        recv_ptrs, sc.ctypes.data, slots, sched, seed, options,
+                                        ctypes.byref(stats), log, cap)
+    else:
+        rc = lib().orc_allreduce_rings(N, len(rings), _ints(flat), mask, PROTO[proto], buff_size,
+                                       chunk_steps, DTYPE[dtype], len(works), carr, send_ptrs,
+                                       recv_ptrs, slots, sched, seed, options, ctypes.byref(stats),
+                                       log, cap)
     calls = []
     if log_calls:
         for c in log[:stats.calls_recorded]:

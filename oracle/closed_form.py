@@ -131,6 +131,19 @@ def _hop(acc, x, dtype, op="sum"):
     return _round_bf16(s)
 
 
+def _premul(s, x, dtype):
+    """PreMulSum's scaling of a rank's input: s * x rounded once to the
+    payload type (int32: low 32 bits)."""
+    if dtype == "int32":
+        su = np.asarray(s).astype(np.int32).view(np.uint32).astype(np.uint64)
+        xu = x.astype(np.int32).view(np.uint32).astype(np.uint64)
+        return ((su * xu) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+    p = _to_f64(np.asarray(s), dtype) * _to_f64(x, dtype)  # exact in binary64
+    if dtype == "float32":
+        return p.astype(np.float32)
+    return _round_bf16(p)
+
+
 def _post_div(v, nranks, dtype):
     """avg's post-op: the owner's final sum divided by N, rounded once
     (int32: truncated toward zero)."""
@@ -143,7 +156,8 @@ def _post_div(v, nranks, dtype):
     return _round_bf16(q)
 
 
-def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, op="sum"):
+def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, op="sum",
+              scalars=None):
     """Expected output of every rank.
 
     ``inputs``: list over collectives of arrays [N, count] (int32 / float32 /
@@ -152,6 +166,13 @@ def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, op
     """
     if isinstance(inputs, np.ndarray):
         inputs = [inputs]
+    if op == "premulsum":
+        # every rank's input enters the fold already scaled by its scalar;
+        # then the fold is the sum's
+        sc = np.asarray(scalars).reshape(len(inputs), -1)
+        inputs = [np.stack([_premul(sc[w, r], x[r], dtype) for r in range(x.shape[0])])
+                  for w, x in enumerate(inputs)]
+        op = "sum"
     # one ring, or one per channel id (channel c runs ring c mod len(rings))
     rings = [list(r) for r in ring_order] if isinstance(ring_order[0], (list, tuple)) \
         else [list(ring_order)]

@@ -60,11 +60,37 @@ def _step(acc, v, op, wide):
     return _mul_f32(acc, v) if op == "prod" else _add_f32(acc, v)
 
 
-def allreduce(x, dtype, op="sum"):
+def _scale(s, x, dtype):
+    """PreMulSum: rank input times its scalar, in the accumulator's precision
+    (fp32 rounds once; bf16 x bf16 is exact in fp32; int32 keeps the low 32
+    bits)."""
+    if dtype == "int32":
+        su = np.asarray(s).astype(np.int32).view(np.uint32).astype(np.uint64)
+        xu = x.astype(np.int32).view(np.uint32).astype(np.uint64)
+        return ((su * xu) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+    if dtype == "float32":
+        return _mul_f32(np.float32(s) * np.ones_like(x, dtype=np.float32), x.astype(np.float32))
+    return _mul_f32(_bf16_to_f32(np.full(x.shape, s, dtype=np.uint16)), _bf16_to_f32(x))
+
+
+def allreduce(x, dtype, op="sum", scalars=None):
     """x: [N, count] array of raw elements (int32 / float32 / uint16 bf16
-    bits).  Returns the [count] array every rank must hold."""
+    bits).  Returns the [count] array every rank must hold.  PreMulSum
+    (``scalars``: one payload-type element per rank) scales each input in
+    the accumulator's precision, then sums."""
     x = np.asarray(x)
     N = x.shape[0]
+    if op == "premulsum":
+        scaled = [_scale(scalars[r], x[r], dtype) for r in range(N)]
+        if dtype == "int32":
+            acc = scaled[0]
+            for k in range(1, N):
+                acc = _step(acc, scaled[k], "sum", "int")
+            return acc
+        acc = scaled[0]
+        for k in range(1, N):
+            acc = _add_f32(acc, scaled[k])
+        return acc if dtype == "float32" else _round_bf16(acc.astype(np.float64))
     if dtype == "int32":
         acc = x[0].astype(np.int32)
         for k in range(1, N):

@@ -103,6 +103,30 @@ void reduce_elem(int dtype, int red, const uint8_t* a, const uint8_t* b, uint8_t
   }
 }
 
+/* PreMulSum's scaling of one own input: s * x rounded once to the payload
+ * type (the product of two fp32 or two bf16 values is exact in binary64). */
+void premul_elem(int dtype, const uint8_t* s, const uint8_t* x, uint8_t* out) {
+  if (dtype == ORC_INT32) {
+    uint32_t a, b;
+    std::memcpy(&a, s, 4);
+    std::memcpy(&b, x, 4);
+    const uint32_t r = a * b;  // low 32 bits
+    std::memcpy(out, &r, 4);
+  } else if (dtype == ORC_FLOAT32) {
+    float a, b;
+    std::memcpy(&a, s, 4);
+    std::memcpy(&b, x, 4);
+    const float r = (float)((double)a * (double)b);
+    std::memcpy(out, &r, 4);
+  } else {
+    uint16_t a, b;
+    std::memcpy(&a, s, 2);
+    std::memcpy(&b, x, 2);
+    const uint16_t r = bf16_round(bf16_to_double(a) * bf16_to_double(b));
+    std::memcpy(out, &r, 2);
+  }
+}
+
 /* The AVG post-op: the owner's final sum divided by N, rounded once to the
  * payload type (int32: the wrapped sum, truncated toward zero).  binary64
  * holds the quotient to 53 bits, and 53 >= 2*24 + 2, so rounding it again to
@@ -248,6 +272,7 @@ struct Sim {
   bool drop_head = false;
   uint64_t ll_period = 1ull << 32;
   int red = ORC_RED_SUM;
+  const uint8_t* scalars = nullptr;  // PreMulSum: [work * N + rank] payload-type scalars
   bool direct = false;  // Simple: all-gather half writes into the next rank's receive buffer
   bool direct_read = false;  // Simple: the loop's first receive reads the previous send buffer
   // Ring of each active channel: entry [n * N + rank] for dense channel n.
@@ -408,18 +433,27 @@ struct Sim {
       const int prv = prev[(size_t)ag.n * N + ag.rank];
       const uint8_t* prev_src = (const uint8_t*)sendbufs[(size_t)u.work * N + prv] + u.offset * es;
       got.assign(prev_src, prev_src + u.nelem * es);
+      if (red == ORC_RED_PREMULSUM)  // the raw input enters the fold here, with its owner's scalar
+        for (int64_t i = 0; i < u.nelem; ++i)
+          premul_elem(dtype, scalars + ((size_t)u.work * N + prv) * es, got.data() + i * es,
+                      got.data() + i * es);
     } else if (recv && direct_recv) got.assign(dst, dst + u.nelem * es);
     else if (recv) read_payload(rc, ag.recv_step, u.nelem, got);
     std::vector<uint8_t> val((size_t)(u.nelem * es));
+    const uint8_t* my_scalar = scalars ? scalars + ((size_t)u.work * N + ag.rank) * es : nullptr;
     for (int64_t i = 0; i < u.nelem; ++i) {
       uint8_t* v = val.data() + i * es;
+      // the rank's own input as it enters the fold (PreMulSum: scaled)
+      uint8_t own[8];
+      std::memcpy(own, src + i * es, (size_t)es);
+      if (red == ORC_RED_PREMULSUM) premul_elem(dtype, my_scalar, own, own);
       switch (u.op) {
         case ORC_OP_SEND:
-          std::memcpy(v, src + i * es, (size_t)es);
+          std::memcpy(v, own, (size_t)es);
           break;
         case ORC_OP_RECV_REDUCE_SEND:
         case ORC_OP_RECV_REDUCE_COPY_SEND:
-          reduce_elem(dtype, red, got.data() + i * es, src + i * es, v);
+          reduce_elem(dtype, red == ORC_RED_PREMULSUM ? ORC_RED_SUM : red, got.data() + i * es, own, v);
           if (u.op == ORC_OP_RECV_REDUCE_COPY_SEND && red == ORC_RED_AVG) post_div(dtype, N, v);
           break;
         default:
@@ -607,6 +641,17 @@ int orc_allreduce_rings(int nranks, int nrings, const int* ring_orders, uint64_t
                         const size_t* counts, const void* const* sendbufs, void* const* recvbufs,
                         int slots, int sched, uint64_t seed, int options, orc_stats* stats,
                         orc_call* call_log, int64_t call_log_cap) {
+  if (((options >> ORC_OPT_RED_SHIFT) & 15) == ORC_RED_PREMULSUM) return ORC_INVALID;  // needs scalars
+  return orc_allreduce_premul(nranks, nrings, ring_orders, channel_mask, proto, buff_size,
+                              chunk_steps, dtype, nworks, counts, sendbufs, recvbufs, nullptr, slots,
+                              sched, seed, options, stats, call_log, call_log_cap);
+}
+
+int orc_allreduce_premul(int nranks, int nrings, const int* ring_orders, uint64_t channel_mask,
+                         int proto, size_t buff_size, int chunk_steps, int dtype, int nworks,
+                         const size_t* counts, const void* const* sendbufs, void* const* recvbufs,
+                         const void* scalars, int slots, int sched, uint64_t seed, int options,
+                         orc_stats* stats, orc_call* call_log, int64_t call_log_cap) {
   if (!valid_params(nranks, channel_mask, proto, buff_size, chunk_steps, dtype, slots))
     return ORC_INVALID;
   if (nworks < 1 || !counts || !sendbufs || !recvbufs) return ORC_INVALID;
@@ -623,10 +668,11 @@ int orc_allreduce_rings(int nranks, int nrings, const int* ring_orders, uint64_t
   sim.direct = (options & ORC_OPT_DIRECT) != 0;
   sim.direct_read = (options & ORC_OPT_DIRECT_READ) != 0;
   if ((sim.direct || sim.direct_read) && proto != ORC_PROTO_SIMPLE) return ORC_INVALID;
-  sim.red = (options >> ORC_OPT_RED_SHIFT) & 15;
+  sim.red = scalars ? ORC_RED_PREMULSUM : (options >> ORC_OPT_RED_SHIFT) & 15;
+  sim.scalars = (const uint8_t*)scalars;
   if (options & ORC_OPT_LL_WRAP8) sim.ll_period = 256;
   if ((uint64_t)slots >= sim.ll_period / 2) return ORC_INVALID;
-  if (sim.red > ORC_RED_AVG) return ORC_INVALID;
+  if (sim.red > ORC_RED_PREMULSUM) return ORC_INVALID;
   sim.sendbufs = sendbufs;
   sim.recvbufs = recvbufs;
   sim.stats = stats;

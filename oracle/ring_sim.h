@@ -63,7 +63,8 @@ enum {
  *        (the post-op) before it is written and forwarded.
  * Floating results round to the payload type after every operation; int32
  * wraps modulo 2^32 and AVG divides the wrapped signed sum, truncating. */
-enum { ORC_RED_SUM = 0, ORC_RED_PROD = 1, ORC_RED_MAX = 2, ORC_RED_MIN = 3, ORC_RED_AVG = 4 };
+enum { ORC_RED_SUM = 0, ORC_RED_PROD = 1, ORC_RED_MAX = 2, ORC_RED_MIN = 3, ORC_RED_AVG = 4,
+       ORC_RED_PREMULSUM = 5 };
 
 /* Return codes. */
 enum { ORC_OK = 0, ORC_DEADLOCK = 1, ORC_INVALID = 2, ORC_CORRUPT = 3 };
@@ -155,6 +156,21 @@ int orc_allreduce_rings(int nranks, int nrings, const int* ring_orders, uint64_t
  * accepted; *bad_step = first corrupted step (or -1). */
 int orc_stream_fault(int proto, int fault, int slots, int nsteps, int64_t* steps_done,
                      int64_t* consumed, int64_t* bad_step);
+
+/* PreMulSum (READING: the pages do not describe it): as orc_allreduce_rings
+ * with the sum, where every rank's own input is first multiplied by that
+ * rank's scalar and rounded to the payload type (int32: low 32 bits) at the
+ * point it enters the fold -- the loop's opening send, recvReduceSend, the
+ * fused final step, and (direct read) the raw input read from the previous
+ * rank's send buffer, which takes the previous rank's scalar.
+ *   scalars  [nworks * nranks] elements of the payload type (raw bytes), index
+ *            work*nranks + rank.
+ * The options' operator bits are ignored. */
+int orc_allreduce_premul(int nranks, int nrings, const int* ring_orders, uint64_t channel_mask,
+                         int proto, size_t buff_size, int chunk_steps, int dtype, int nworks,
+                         const size_t* counts, const void* const* sendbufs, void* const* recvbufs,
+                         const void* scalars, int slots, int sched, uint64_t seed, int options,
+                         orc_stats* stats, orc_call* call_log, int64_t call_log_cap);
 
 /* LL flag generations on one connector [C23 "LL：Data 与 Flag 同 Line": a test
  * mode makes the flag wrap at 0x100; at cleanup steps the sender writes the

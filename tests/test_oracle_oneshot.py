@@ -163,3 +163,24 @@ def test_avg_hand_values():
     assert got[0] == 2.0 and got.view(np.uint32)[1] == 0x3EAAAAAB
     xb = workloads._bf16_bits(xf.ravel()).reshape(3, 2)
     assert oneshot.allreduce(xb, "bfloat16", "avg").tolist() == [0x4000, 0x3EAB]
+
+
+def test_premulsum_pins():
+    rng = np.random.default_rng(30)
+    v = rng.integers(-8, 9, size=(5, 3000)).astype(np.float32)
+    s = np.array([1, -2, 3, 4, -5], dtype=np.float32)
+    np.testing.assert_array_equal(oneshot.allreduce(v, "float32", "premulsum", s).astype(np.float64),
+                                  sum(float(s[r]) * v[r].astype(np.float64) for r in range(5)))
+    x = rng.standard_normal((4, 3000)).astype(np.float32)
+    np.testing.assert_array_equal(oneshot.allreduce(x, "float32", "premulsum", np.ones(4, np.float32)),
+                                  oneshot.allreduce(x, "float32"))
+    xi = rng.integers(-2 ** 31, 2 ** 31, size=(3, 500)).astype(np.int32)
+    si = np.array([3, -7, 1001], dtype=np.int32)
+    gi = oneshot.allreduce(xi, "int32", "premulsum", si)
+    for j in range(500):
+        t = sum(int(si[r]) * int(xi[r, j]) for r in range(3)) % 2 ** 32
+        assert int(gi[j]) == (t - 2 ** 32 if t >= 2 ** 31 else t)
+    # bf16: scalar x input exact in the fp32 accumulator, rounded once at the end
+    xb = workloads._bf16_bits(np.array([[1.0], [2.0 ** -8]], dtype=np.float32).ravel()).reshape(2, 1)
+    sb = workloads._bf16_bits(np.array([1.0, 2.0], dtype=np.float32))
+    assert int(oneshot.allreduce(xb, "bfloat16", "premulsum", sb)[0]) == 0x3F81

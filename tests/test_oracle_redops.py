@@ -157,3 +157,85 @@ def test_unknown_op_is_rejected(monkeypatch):
     rc, _, _, _ = oracle.allreduce([np.ones((2, 8), dtype=np.float32)], [0, 1], 0x1, "SIMPLE",
                                    8192, 4, "float32", op="bogus")
     assert rc == oracle.INVALID
+
+
+# ------------------------------------------------------------ PreMulSum
+def _scalars(dtype, vals):
+    v = np.asarray(vals, dtype=np.float64)
+    if dtype == "int32":
+        return v.astype(np.int32)
+    if dtype == "float32":
+        return v.astype(np.float32)
+    return workloads._bf16_bits(v.astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128"])
+def test_premulsum_simulator_matches_closed_form(dtype, proto):
+    x = _draw(dtype, (4, 20011), 17, "sum")
+    sc = _scalars(dtype, [3, -2, 0.5, 7] if dtype != "int32" else [3, -2, 5, 7])
+    rc, out, _, _ = oracle.allreduce([x], [0, 2, 3, 1], 0x7, proto, SMALL_BUFF[proto], 4, dtype,
+                                     op="premulsum", scalars=sc, sched=1, seed=2)
+    assert rc == oracle.OK
+    want = cf.allreduce([x], [0, 2, 3, 1], 0x7, proto, SMALL_BUFF[proto], 4, dtype,
+                        op="premulsum", scalars=sc)[0]
+    for r in range(4):
+        np.testing.assert_array_equal(out[0][r], want)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+def test_premulsum_unit_scalars_is_the_sum(dtype):
+    x = _draw(dtype, (4, 9001), 18, "sum")
+    got = _sim_premul(x, dtype, _scalars(dtype, [1, 1, 1, 1]))
+    np.testing.assert_array_equal(got, _sim(x, "sum", dtype))
+
+
+def _sim_premul(x, dtype, sc, **kw):
+    rc, out, _, _ = oracle.allreduce([x], [0, 2, 3, 1], 0x7, "SIMPLE", SMALL_BUFF["SIMPLE"], 4,
+                                     dtype, op="premulsum", scalars=sc, **kw)
+    assert rc == oracle.OK
+    return out[0][0]
+
+
+def test_premulsum_power_of_two_scalars_scale_the_sum_exactly():
+    """Scaling every input by 1/4 scales each rounded partial by 1/4 too
+    (binary floating point, no underflow): the result is the sum's bits
+    times 1/4."""
+    x = _draw("float32", (4, 9001), 19, "sum")
+    got = _sim_premul(x, "float32", _scalars("float32", [0.25] * 4))
+    np.testing.assert_array_equal(got, _sim(x, "sum", "float32") * np.float32(0.25))
+
+
+def test_premulsum_integer_values_are_exact_and_per_rank():
+    """Distinct integer scalars on small integer inputs: the result is the
+    exact sum of s_r * x_r, so a scalar applied to the wrong rank's input
+    shows up."""
+    rng = np.random.default_rng(20)
+    v = rng.integers(-8, 9, size=(4, 5000)).astype(np.float32)
+    s = [1, 2, 3, 4]
+    want = sum(s[r] * v[r].astype(np.float64) for r in range(4))
+    for direct_read in (False, True):
+        got = _sim_premul(v, "float32", _scalars("float32", s), direct_read=direct_read)
+        np.testing.assert_array_equal(got.astype(np.float64), want)
+    xi = rng.integers(-2 ** 31, 2 ** 31, size=(4, 3000)).astype(np.int32)
+    si = [7, -3, 12345, -99999]
+    gi = _sim_premul(xi, "int32", _scalars("int32", si))
+    for j in range(0, 3000, 13):
+        t = sum(si[r] * int(xi[r, j]) for r in range(4)) % 2 ** 32
+        assert int(gi[j]) == (t - 2 ** 32 if t >= 2 ** 31 else t)
+
+
+def test_premulsum_rounds_the_product_once():
+    """fp32: float32(1/3) * 3 = 1.0000000298... rounds to 1.0 before the add."""
+    x = np.zeros((4, 4), dtype=np.float32)
+    x[1] = 3.0
+    got = _sim_premul(x, "float32", _scalars("float32", [1.0, np.float32(1 / 3), 1.0, 1.0]))
+    assert (got == 1.0).all()
+
+
+def test_premulsum_direct_read_scales_the_previous_input():
+    x = _draw("float32", (4, 30011), 21, "sum")
+    sc = _scalars("float32", [0.5, -1.5, 3.0, 1.25])
+    base = _sim_premul(x, "float32", sc)
+    for kw in (dict(direct=True), dict(direct_read=True), dict(direct=True, direct_read=True)):
+        np.testing.assert_array_equal(_sim_premul(x, "float32", sc, **kw), base)
