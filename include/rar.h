@@ -62,8 +62,14 @@ typedef enum { RAR_INT32 = 0, RAR_FLOAT32 = 1, RAR_BFLOAT16 = 2 } rar_dtype_t;
  *   RAR_MAX   x if x > acc      RAR_MIN   x if x < acc   (else acc, bits kept)
  *   RAR_AVG   acc + x; the owner divides its final sum by N (int32:
  *             truncating toward zero) before writing and forwarding it.
+ *   RAR_PREMULSUM  acc + s_r * x: rank r's input is first multiplied by
+ *             the rank's scalar s_r and rounded to the payload type (int32:
+ *             low 32 bits) where it enters the fold; only through the
+ *             *_premul entry points, which take the scalars.  (The pages do
+ *             not describe PreMulSum; this is the reading.)
  * Floating results round to the payload type after every hop. */
-typedef enum { RAR_SUM = 0, RAR_PROD = 1, RAR_MAX = 2, RAR_MIN = 3, RAR_AVG = 4 } rar_redop_t;
+typedef enum { RAR_SUM = 0, RAR_PROD = 1, RAR_MAX = 2, RAR_MIN = 3, RAR_AVG = 4,
+               RAR_PREMULSUM = 5 } rar_redop_t;
 
 typedef struct rar_comm* rar_comm_t;
 
@@ -189,6 +195,15 @@ rar_result_t rar_comm_create_rings(rar_comm_t* comm, int nranks, int nrings,
 rar_result_t rar_allreduce(rar_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                            size_t count, rar_dtype_t dtype, rar_redop_t op, void* stream);
 
+/* As rar_allreduce with RAR_PREMULSUM: scalars is a host array of `nranks`
+ * elements of `dtype` (bfloat16 as its 16-bit pattern), copied at call time;
+ * rank r's input is scaled by scalars[r].  Inside a group every call brings
+ * its own scalars.  Errors: as rar_allreduce; RAR_INVALID_ARGUMENT if
+ * scalars is NULL (count 0 aside). */
+rar_result_t rar_allreduce_premul(rar_comm_t comm, const void* const* sendbufs,
+                                  void* const* recvbufs, size_t count, rar_dtype_t dtype,
+                                  const void* scalars, void* stream);
+
 /* Fused works [C23 "RunWorkBatch 与 Fused Work"]: AllReduces queued between
  * start and end run as one launch; their elements are laid end to end and cut
  * into one contiguous range per channel, each channel executing its pieces in
@@ -242,6 +257,14 @@ typedef struct {
 rar_result_t rar_oneshot_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks,
                                    size_t count, rar_dtype_t dtype, rar_redop_t op,
                                    const rar_oneshot_tuning_t* tuning, void* stream);
+
+/* As rar_oneshot_allreduce with RAR_PREMULSUM: scalars is a host array of
+ * `nranks` elements of `dtype`; each input is scaled by its rank's scalar in
+ * the fp32 (int32) accumulator, then summed in rank order. */
+rar_result_t rar_oneshot_allreduce_premul(const void* const* sendbufs, void* const* recvbufs,
+                                          int nranks, size_t count, rar_dtype_t dtype,
+                                          const void* scalars, const rar_oneshot_tuning_t* tuning,
+                                          void* stream);
 
 /* Watchdog status: RAR_ABORTED if a launch on this communicator timed out in
  * a wait, else RAR_SUCCESS.  Does not synchronize; reflects launches the

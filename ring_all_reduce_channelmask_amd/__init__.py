@@ -47,6 +47,24 @@ def _check_tensors(sends, recvs, nranks):
     return n, _dtype_name(sends[0])
 
 
+def _scalar_buffer(scalars, dtype, nranks):
+    """PreMulSum scalars as a host array of payload-type elements: numbers
+    are converted (bfloat16 rounded to nearest even); a numpy uint16 array
+    for bfloat16 is taken as bit patterns."""
+    import numpy as np
+    if scalars is None or len(scalars) != nranks:
+        raise ValueError(f"premulsum needs {nranks} scalars")
+    if dtype == "bfloat16":
+        a = np.asarray(scalars)
+        if a.dtype != np.uint16:
+            import torch
+            a = torch.tensor(np.asarray(scalars, dtype=np.float32)).to(torch.bfloat16) \
+                .view(torch.int16).numpy().view(np.uint16)
+    else:
+        a = np.asarray(scalars, dtype=np.float32 if dtype == "float32" else np.int32)
+    return np.ascontiguousarray(a)
+
+
 def _stream_handle(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -86,12 +104,18 @@ class Comm:
     def handle(self):
         return self._h
 
-    def allreduce(self, sends, recvs=None, stream=None, op="sum"):
-        """Reduce over ranks with ``op`` (sum, prod, max, min, avg);
-        ``recvs=None`` runs in place."""
+    def allreduce(self, sends, recvs=None, stream=None, op="sum", scalars=None):
+        """Reduce over ranks with ``op`` (sum, prod, max, min, avg, or
+        premulsum with one scalar per rank); ``recvs=None`` runs in place."""
         recvs = sends if recvs is None else recvs
         n, dt = _check_tensors(sends, recvs, self.nranks)
         lib = _lib.load()
+        if op == "premulsum":
+            buf = _scalar_buffer(scalars, dt, self.nranks)
+            _lib.check(lib.rar_allreduce_premul(self._h, _ptr_array(sends), _ptr_array(recvs), n,
+                                                _lib.DTYPE[dt], buf.ctypes.data,
+                                                _stream_handle(stream)))
+            return
         _lib.check(lib.rar_allreduce(self._h, _ptr_array(sends), _ptr_array(recvs), n,
                                      _lib.DTYPE[dt], _lib.RED[op], _stream_handle(stream)))
 
@@ -156,7 +180,8 @@ def ring_allreduce(sends, recvs, ring_order, proto="SIMPLE", nchannels=1, buff_s
                                   buff_size, chunk_steps, _stream_handle(stream)))
 
 
-def oneshot_allreduce(sends, recvs=None, workgroups=0, waves=0, unroll=0, stream=None, op="sum"):
+def oneshot_allreduce(sends, recvs=None, workgroups=0, waves=0, unroll=0, stream=None, op="sum",
+                      scalars=None):
     """One-shot AllReduce of N equally sized device tensors (one per virtual
     rank): every output gets the fold of all inputs in rank order.
     ``recvs=None`` runs in place."""
@@ -164,6 +189,12 @@ def oneshot_allreduce(sends, recvs=None, workgroups=0, waves=0, unroll=0, stream
     nranks = len(sends)
     n, dt = _check_tensors(sends, recvs, nranks)
     tune = _lib.OneshotTuning(workgroups, waves, unroll, 0)
+    if op == "premulsum":
+        buf = _scalar_buffer(scalars, dt, nranks)
+        _lib.check(_lib.load().rar_oneshot_allreduce_premul(
+            _ptr_array(sends), _ptr_array(recvs), nranks, n, _lib.DTYPE[dt], buf.ctypes.data,
+            ctypes.byref(tune), _stream_handle(stream)))
+        return
     _lib.check(_lib.load().rar_oneshot_allreduce(_ptr_array(sends), _ptr_array(recvs), nranks, n,
                                                  _lib.DTYPE[dt], _lib.RED[op], ctypes.byref(tune),
                                                  _stream_handle(stream)))

@@ -14,7 +14,7 @@ DEBUG_DROP_RECV_HEAD, DEBUG_TRACE, DEBUG_LL_FLAG_WRAP8 = 1, 2, 4
 PROTO = {"LL": 0, "LL128": 1, "SIMPLE": 2}
 DTYPE = {"int32": 0, "float32": 1, "bfloat16": 2}
 SUM = 0
-RED = {"sum": 0, "prod": 1, "max": 2, "min": 3, "avg": 4}
+RED = {"sum": 0, "prod": 1, "max": 2, "min": 3, "avg": 4, "premulsum": 5}
 
 
 class Tuning(ctypes.Structure):
@@ -64,6 +64,8 @@ SIGNATURES = [
                                          _c.POINTER(Tuning)]),
     ("rar_allreduce", _c.c_int, [_c.c_void_p, _vpp, _vpp, _c.c_size_t, _c.c_int, _c.c_int,
                                  _c.c_void_p]),
+    ("rar_allreduce_premul", _c.c_int, [_c.c_void_p, _vpp, _vpp, _c.c_size_t, _c.c_int,
+                                        _c.c_void_p, _c.c_void_p]),
     ("rar_group_start", _c.c_int, [_c.c_void_p]),
     ("rar_group_end", _c.c_int, [_c.c_void_p, _c.c_void_p]),
     ("rar_comm_destroy", _c.c_int, [_c.c_void_p]),
@@ -71,6 +73,9 @@ SIGNATURES = [
                                   _c.c_int, _c.c_int, _c.c_size_t, _c.c_int, _c.c_void_p]),
     ("rar_oneshot_allreduce", _c.c_int, [_vpp, _vpp, _c.c_int, _c.c_size_t, _c.c_int, _c.c_int,
                                          _c.POINTER(OneshotTuning), _c.c_void_p]),
+    ("rar_oneshot_allreduce_premul", _c.c_int, [_vpp, _vpp, _c.c_int, _c.c_size_t, _c.c_int,
+                                                _c.c_void_p, _c.POINTER(OneshotTuning),
+                                                _c.c_void_p]),
     ("rar_comm_get_async_error", _c.c_int, [_c.c_void_p]),
     ("rar_comm_query_state", _c.c_int, [_c.c_void_p, _c.POINTER(_c.c_int64), _c.c_size_t,
                                         _c.POINTER(_c.c_size_t)]),

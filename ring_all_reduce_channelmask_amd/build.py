@@ -21,6 +21,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep fp32 arithmetic scalar: no packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every multiply and add rounds on its own (no fused multiply-add): the
+    # results must match the fold the oracle rounds step by step
+    "-ffp-contract=off",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -57,7 +57,14 @@ struct QueuedCall {
   size_t count;
   int dtype;
   int red;
+  std::vector<uint32_t> scalars;  // PreMulSum: one scalar per rank (payload bits)
 };
+
+// Scalar bits of rank r from a host array of payload-type elements.
+uint32_t scalar_bits(const void* scalars, int dtype, int r) {
+  if (dtype == RAR_BFLOAT16) return reinterpret_cast<const uint16_t*>(scalars)[r];
+  return reinterpret_cast<const uint32_t*>(scalars)[r];
+}
 
 size_t align_to(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -127,7 +134,11 @@ rar_result_t check_dtype(int dtype) {
 }
 
 rar_result_t check_op(int op) {
-  if (op < RAR_SUM || op > RAR_AVG) return fail(RAR_INVALID_ARGUMENT, "unknown reduction operator");
+  if (op < RAR_SUM || op > RAR_AVG) {
+    if (op == RAR_PREMULSUM)
+      return fail(RAR_INVALID_ARGUMENT, "RAR_PREMULSUM needs scalars: use the *_premul entry point");
+    return fail(RAR_INVALID_ARGUMENT, "unknown reduction operator");
+  }
   return RAR_SUCCESS;
 }
 
@@ -163,7 +174,9 @@ rar_result_t launch(rar_comm* c, const std::vector<QueuedCall>& calls, hipStream
   const size_t off_works = align_to(off_batches + plan.batches.size() * sizeof(rar::DevBatch), 64);
   const size_t off_ptrs = align_to(off_works + plan.works.size() * sizeof(rar::DevWork), 64);
   const size_t nptrs = calls.size() * (size_t)c->nranks * 2;
-  const size_t off_first = align_to(off_ptrs + nptrs * sizeof(void*), 64);
+  const size_t off_scalars = align_to(off_ptrs + nptrs * sizeof(void*), 64);
+  const size_t nscalars = calls.size() * (size_t)c->nranks;
+  const size_t off_first = align_to(off_scalars + nscalars * sizeof(uint32_t), 64);
   const size_t total = align_to(off_first + plan.first_batch.size() * sizeof(uint32_t), 64);
   std::vector<uint8_t> bytes(total, 0);
   std::memcpy(bytes.data() + off_batches, plan.batches.data(), plan.batches.size() * sizeof(rar::DevBatch));
@@ -174,6 +187,9 @@ rar_result_t launch(rar_comm* c, const std::vector<QueuedCall>& calls, hipStream
       ptrs[(w * c->nranks + r) * 2] = calls[w].send[r];
       ptrs[(w * c->nranks + r) * 2 + 1] = calls[w].recv[r];
     }
+  uint32_t* scal = reinterpret_cast<uint32_t*>(bytes.data() + off_scalars);
+  for (size_t w = 0; w < calls.size(); ++w)
+    for (int r = 0; r < c->nranks && !calls[w].scalars.empty(); ++r) scal[w * c->nranks + r] = calls[w].scalars[r];
   std::memcpy(bytes.data() + off_first, plan.first_batch.data(), plan.first_batch.size() * sizeof(uint32_t));
 
   if (bytes != c->last_upload) {
@@ -208,6 +224,7 @@ rar_result_t launch(rar_comm* c, const std::vector<QueuedCall>& calls, hipStream
   args.works = reinterpret_cast<const rar::DevWork*>(c->d_arena + off_works);
   args.ptrs = reinterpret_cast<void* const*>(c->d_arena + off_ptrs);
   args.first_batch = reinterpret_cast<const uint32_t*>(c->d_arena + off_first);
+  args.scalars = reinterpret_cast<const uint32_t*>(c->d_arena + off_scalars);
   args.wg_map = c->d_wgmap;
   args.epoch = ++c->epoch;
   void* params[] = {&args};
@@ -485,12 +502,15 @@ rar_result_t rar_comm_destroy(rar_comm_t c) {
   return RAR_SUCCESS;
 }
 
-rar_result_t rar_allreduce(rar_comm_t c, const void* const* sendbufs, void* const* recvbufs,
-                           size_t count, rar_dtype_t dtype, rar_redop_t op, void* stream) {
-  g_last_error.clear();
+static rar_result_t allreduce_impl(rar_comm_t c, const void* const* sendbufs, void* const* recvbufs,
+                           size_t count, rar_dtype_t dtype, int op, const void* scalars, void* stream) {
   if (!c) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
   if (rar_result_t r = check_dtype(dtype)) return r;
-  if (rar_result_t r = check_op(op)) return r;
+  if (op == RAR_PREMULSUM) {
+    if (!scalars) return fail(RAR_INVALID_ARGUMENT, "scalars is NULL");
+  } else if (rar_result_t r = check_op(op)) {
+    return r;
+  }
   if (c->in_group && !c->queue.empty() && (c->queue.front().dtype != dtype || c->queue.front().red != op))
     return fail(RAR_UNSUPPORTED, "all AllReduces of a group must share one dtype and operator");
   // nothing to move: no launch, no step advance, pointers are not looked at
@@ -503,6 +523,8 @@ rar_result_t rar_allreduce(rar_comm_t c, const void* const* sendbufs, void* cons
   q.count = count;
   q.dtype = dtype;
   q.red = op;
+  if (op == RAR_PREMULSUM)
+    for (int r = 0; r < c->nranks; ++r) q.scalars.push_back(scalar_bits(scalars, dtype, r));
   if (c->in_group) {
     c->queue.push_back(std::move(q));
     return RAR_SUCCESS;
@@ -510,6 +532,18 @@ rar_result_t rar_allreduce(rar_comm_t c, const void* const* sendbufs, void* cons
   std::vector<QueuedCall> one;
   one.push_back(std::move(q));
   return launch(c, one, reinterpret_cast<hipStream_t>(stream));
+}
+
+rar_result_t rar_allreduce(rar_comm_t c, const void* const* sendbufs, void* const* recvbufs,
+                           size_t count, rar_dtype_t dtype, rar_redop_t op, void* stream) {
+  g_last_error.clear();
+  return allreduce_impl(c, sendbufs, recvbufs, count, dtype, op, nullptr, stream);
+}
+
+rar_result_t rar_allreduce_premul(rar_comm_t c, const void* const* sendbufs, void* const* recvbufs,
+                                  size_t count, rar_dtype_t dtype, const void* scalars, void* stream) {
+  g_last_error.clear();
+  return allreduce_impl(c, sendbufs, recvbufs, count, dtype, RAR_PREMULSUM, scalars, stream);
 }
 
 rar_result_t rar_group_start(rar_comm_t c) {
@@ -561,13 +595,16 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
   return rar_allreduce(c, sendbufs, recvbufs, count, dtype, op, stream);
 }
 
-rar_result_t rar_oneshot_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks,
-                                   size_t count, rar_dtype_t dtype, rar_redop_t op,
-                                   const rar_oneshot_tuning_t* tuning, void* stream) {
-  g_last_error.clear();
+static rar_result_t oneshot_impl(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                 size_t count, rar_dtype_t dtype, int op, const void* scalars,
+                                 const rar_oneshot_tuning_t* tuning, void* stream) {
   if (nranks < 2 || nranks > rar::kMaxRanks) return fail(RAR_INVALID_ARGUMENT, "nranks must be in [2, 64]");
   if (rar_result_t r = check_dtype(dtype)) return r;
-  if (rar_result_t r = check_op(op)) return r;
+  if (op == RAR_PREMULSUM) {
+    if (!scalars) return fail(RAR_INVALID_ARGUMENT, "scalars is NULL");
+  } else if (rar_result_t r = check_op(op)) {
+    return r;
+  }
   rar_oneshot_tuning_t tune{0, 0, 0, 0};
   if (tuning) tune = *tuning;
   if (tune.workgroups < 0 || tune.workgroups > 65536)
@@ -604,6 +641,7 @@ rar_result_t rar_oneshot_allreduce(const void* const* sendbufs, void* const* rec
   for (int r = 0; r < nranks; ++r) {
     a.src[r] = sendbufs[r];
     a.dst[r] = recvbufs[r];
+    a.scalar[r] = op == RAR_PREMULSUM ? scalar_bits(scalars, dtype, r) : 0;
   }
   const int64_t vec = 16 / (int64_t)es;
   a.nranks = nranks;
@@ -620,6 +658,20 @@ rar_result_t rar_oneshot_allreduce(const void* const* sendbufs, void* const* rec
   RAR_HIP(hipLaunchKernel(rar::get_oneshot_kernel(dtype, op, unroll), dim3((unsigned)blocks), dim3(threads),
                           params, 0, reinterpret_cast<hipStream_t>(stream)));
   return RAR_SUCCESS;
+}
+
+rar_result_t rar_oneshot_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                   size_t count, rar_dtype_t dtype, rar_redop_t op,
+                                   const rar_oneshot_tuning_t* tuning, void* stream) {
+  g_last_error.clear();
+  return oneshot_impl(sendbufs, recvbufs, nranks, count, dtype, op, nullptr, tuning, stream);
+}
+
+rar_result_t rar_oneshot_allreduce_premul(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                          size_t count, rar_dtype_t dtype, const void* scalars,
+                                          const rar_oneshot_tuning_t* tuning, void* stream) {
+  g_last_error.clear();
+  return oneshot_impl(sendbufs, recvbufs, nranks, count, dtype, RAR_PREMULSUM, scalars, tuning, stream);
 }
 
 rar_result_t rar_comm_get_async_error(rar_comm_t c) {

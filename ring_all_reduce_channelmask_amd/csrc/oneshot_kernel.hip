@@ -56,17 +56,24 @@ __device__ __forceinline__ uint32_t red_i(uint32_t a, uint32_t b) {
 // Accumulator of one 16-byte vector: fp32 and int32 fold the words as they
 // are; bf16 widens each of the 8 elements to fp32 (exact) and rounds once in
 // out().  avg divides the final sum by N there (int32: truncating).
+// PreMulSum (R == kRedPreMulSum) scales every input by its rank's scalar
+// `s` in the accumulator's precision, then sums; other operators ignore `s`.
+template <int R>
+__device__ __forceinline__ float pre_f(float x, float s) {
+  return R == kRedPreMulSum ? x * s : x;
+}
+
 template <int R>
 struct AccF32 {
   using S = uint32_t;
   float a[4];
-  __device__ __forceinline__ void init(v4u x) {
+  __device__ __forceinline__ void init(v4u x, uint32_t s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = __uint_as_float(x[i]);
+    for (int i = 0; i < 4; ++i) a[i] = pre_f<R>(__uint_as_float(x[i]), __uint_as_float(s));
   }
-  __device__ __forceinline__ void add(v4u x) {
+  __device__ __forceinline__ void add(v4u x, uint32_t s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = red_f<R>(a[i], __uint_as_float(x[i]));
+    for (int i = 0; i < 4; ++i) a[i] = red_f<R>(a[i], pre_f<R>(__uint_as_float(x[i]), __uint_as_float(s)));
   }
   __device__ __forceinline__ v4u out(int n) const {
     v4u r;
@@ -74,9 +81,11 @@ struct AccF32 {
     for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(R == kRedAvg ? a[i] / (float)n : a[i]);
     return r;
   }
-  static __device__ __forceinline__ uint32_t elem_init(uint32_t x) { return x; }
-  static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint32_t x) {
-    return __float_as_uint(red_f<R>(__uint_as_float(acc), __uint_as_float(x)));
+  static __device__ __forceinline__ uint32_t elem_init(uint32_t x, uint32_t s) {
+    return __float_as_uint(pre_f<R>(__uint_as_float(x), __uint_as_float(s)));
+  }
+  static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint32_t x, uint32_t s) {
+    return __float_as_uint(red_f<R>(__uint_as_float(acc), pre_f<R>(__uint_as_float(x), __uint_as_float(s))));
   }
   static __device__ __forceinline__ uint32_t elem_out(uint32_t acc, int n) {
     return R == kRedAvg ? __float_as_uint(__uint_as_float(acc) / (float)n) : acc;
@@ -86,10 +95,16 @@ template <int R>
 struct AccI32 {
   using S = uint32_t;
   v4u a;
-  __device__ __forceinline__ void init(v4u x) { a = x; }
-  __device__ __forceinline__ void add(v4u x) {
+  static __device__ __forceinline__ uint32_t pre(uint32_t x, uint32_t s) {
+    return R == kRedPreMulSum ? x * s : x;  // low 32 bits
+  }
+  __device__ __forceinline__ void init(v4u x, uint32_t s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = red_i<R>(a[i], x[i]);
+    for (int i = 0; i < 4; ++i) a[i] = pre(x[i], s);
+  }
+  __device__ __forceinline__ void add(v4u x, uint32_t s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = red_i<R>(a[i], pre(x[i], s));
   }
   __device__ __forceinline__ v4u out(int n) const {
     if constexpr (R != kRedAvg) return a;
@@ -98,8 +113,10 @@ struct AccI32 {
     for (int i = 0; i < 4; ++i) r[i] = (uint32_t)((int32_t)a[i] / n);
     return r;
   }
-  static __device__ __forceinline__ uint32_t elem_init(uint32_t x) { return x; }
-  static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint32_t x) { return red_i<R>(acc, x); }
+  static __device__ __forceinline__ uint32_t elem_init(uint32_t x, uint32_t s) { return pre(x, s); }
+  static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint32_t x, uint32_t s) {
+    return red_i<R>(acc, pre(x, s));
+  }
   static __device__ __forceinline__ uint32_t elem_out(uint32_t acc, int n) {
     return R == kRedAvg ? (uint32_t)((int32_t)acc / n) : acc;
   }
@@ -108,18 +125,20 @@ template <int R>
 struct AccBF16 {
   using S = uint16_t;
   float lo[4], hi[4];  // element 2i in the low half of word i, 2i+1 in the high half
-  __device__ __forceinline__ void init(v4u x) {
+  __device__ __forceinline__ void init(v4u x, uint32_t s) {
+    const float fs = __uint_as_float(s << 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lo[i] = __uint_as_float(x[i] << 16);
-      hi[i] = __uint_as_float(x[i] & 0xffff0000u);
+      lo[i] = pre_f<R>(__uint_as_float(x[i] << 16), fs);
+      hi[i] = pre_f<R>(__uint_as_float(x[i] & 0xffff0000u), fs);
     }
   }
-  __device__ __forceinline__ void add(v4u x) {
+  __device__ __forceinline__ void add(v4u x, uint32_t s) {
+    const float fs = __uint_as_float(s << 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lo[i] = red_f<R>(lo[i], __uint_as_float(x[i] << 16));
-      hi[i] = red_f<R>(hi[i], __uint_as_float(x[i] & 0xffff0000u));
+      lo[i] = red_f<R>(lo[i], pre_f<R>(__uint_as_float(x[i] << 16), fs));
+      hi[i] = red_f<R>(hi[i], pre_f<R>(__uint_as_float(x[i] & 0xffff0000u), fs));
     }
   }
   __device__ __forceinline__ v4u out(int n) const {
@@ -132,11 +151,12 @@ struct AccBF16 {
     }
     return r;
   }
-  static __device__ __forceinline__ uint32_t elem_init(uint16_t x) {
-    return __float_as_uint(__uint_as_float((uint32_t)x << 16));
+  static __device__ __forceinline__ uint32_t elem_init(uint16_t x, uint32_t s) {
+    return __float_as_uint(pre_f<R>(__uint_as_float((uint32_t)x << 16), __uint_as_float(s << 16)));
   }
-  static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint16_t x) {
-    return __float_as_uint(red_f<R>(__uint_as_float(acc), __uint_as_float((uint32_t)x << 16)));
+  static __device__ __forceinline__ uint32_t elem_add(uint32_t acc, uint16_t x, uint32_t s) {
+    return __float_as_uint(
+        red_f<R>(__uint_as_float(acc), pre_f<R>(__uint_as_float((uint32_t)x << 16), __uint_as_float(s << 16))));
   }
   static __device__ __forceinline__ uint16_t elem_out(uint32_t acc, int n) {
     const float f = __uint_as_float(acc);
@@ -182,8 +202,8 @@ __global__ void __launch_bounds__(512) oneshot_kernel(OneshotArgs args) {
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             if (!live[u]) continue;
-            if (k0 + j == 0) acc[u].init(x[j][u]);
-            else acc[u].add(x[j][u]);
+            if (k0 + j == 0) acc[u].init(x[j][u], args.scalar[0]);
+            else acc[u].add(x[j][u], args.scalar[k0 + j]);
           }
         }
       }
@@ -202,8 +222,8 @@ __global__ void __launch_bounds__(512) oneshot_kernel(OneshotArgs args) {
   if (blockIdx.x == 0 && threadIdx.x < args.tail) {
     using S = typename Acc::S;
     const int64_t e = args.nvec * (16 / (int64_t)sizeof(S)) + threadIdx.x;
-    uint32_t a = Acc::elem_init(reinterpret_cast<const S*>(args.src[0])[e]);
-    for (int k = 1; k < N; ++k) a = Acc::elem_add(a, reinterpret_cast<const S*>(args.src[k])[e]);
+    uint32_t a = Acc::elem_init(reinterpret_cast<const S*>(args.src[0])[e], args.scalar[0]);
+    for (int k = 1; k < N; ++k) a = Acc::elem_add(a, reinterpret_cast<const S*>(args.src[k])[e], args.scalar[k]);
     const S v = (S)Acc::elem_out(a, N);
     for (int k = 0; k < N; ++k) reinterpret_cast<S*>(args.dst[k])[e] = v;
   }
@@ -226,6 +246,7 @@ const void* pick(int red, int unroll) {
     case kRedMax: return pick_unroll<Acc<kRedMax>>(unroll);
     case kRedMin: return pick_unroll<Acc<kRedMin>>(unroll);
     case kRedAvg: return pick_unroll<Acc<kRedAvg>>(unroll);
+    case kRedPreMulSum: return pick_unroll<Acc<kRedPreMulSum>>(unroll);
   }
   return nullptr;
 }

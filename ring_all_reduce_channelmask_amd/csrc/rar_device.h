@@ -21,8 +21,8 @@ constexpr uint32_t kIdleWg = 0xFFFFFFFFu;
 
 enum Proto : int32_t { kLL = 0, kLL128 = 1, kSimple = 2 };
 enum Dtype : int32_t { kInt32 = 0, kFloat32 = 1, kBFloat16 = 2 };
-enum Red : int32_t { kRedSum = 0, kRedProd = 1, kRedMax = 2, kRedMin = 3, kRedAvg = 4 };
-constexpr int kNumRed = 5;
+enum Red : int32_t { kRedSum = 0, kRedProd = 1, kRedMax = 2, kRedMin = 3, kRedAvg = 4, kRedPreMulSum = 5 };
+constexpr int kNumRed = 6;
 
 // Arguments of the one-shot kernel (by value: at most 64 ranks' pointers).
 struct OneshotArgs {
@@ -32,6 +32,7 @@ struct OneshotArgs {
   int64_t vec_per_block;       // contiguous vectors folded by one workgroup
   int32_t nranks;
   int32_t tail;                // elements after the last whole vector
+  uint32_t scalar[kMaxRanks];  // PreMulSum: each rank's scalar bits (bf16 in the low half)
 };
 
 // One (collective, channel) piece: what ncclDevWorkColl carries for runRing.
@@ -137,6 +138,7 @@ struct KernelArgs {
   const uint32_t* first_batch;  // [64] first batch of each channel id (0 = none)
   const uint32_t* wg_map;       // [grid] rank | n << 8 | lane << 16, or kIdleWg
   uint64_t epoch;               // launch counter of the communicator, from 1
+  const uint32_t* scalars;      // PreMulSum: [buf_index * N + rank] scalar bits (bf16 in the low half)
 };
 
 }  // namespace rar

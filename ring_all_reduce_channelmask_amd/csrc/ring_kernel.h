@@ -87,10 +87,17 @@ __device__ __forceinline__ float red_f(float a, float b) {
   else return a + b;
 }
 
+// PreMulSum: a rank's own input is multiplied by the rank's scalar, rounded
+// to the payload type, where it enters the fold; the fold is the sum's.
 template <int R>
 struct TyF32 {
   using S = uint32_t;
   static constexpr bool kPost = R == kRedAvg;
+  static constexpr bool kPre = R == kRedPreMulSum;
+  static __device__ __forceinline__ uint32_t pre_word(uint32_t x, uint32_t s) {
+    return __float_as_uint(__uint_as_float(x) * __uint_as_float(s));
+  }
+  static __device__ __forceinline__ S pre_elem(S x, uint32_t s) { return pre_word(x, s); }
   static __device__ __forceinline__ uint32_t red_word(uint32_t a, uint32_t b) {
     return __float_as_uint(red_f<R>(__uint_as_float(a), __uint_as_float(b)));
   }
@@ -104,6 +111,9 @@ template <int R>
 struct TyI32 {
   using S = uint32_t;
   static constexpr bool kPost = R == kRedAvg;
+  static constexpr bool kPre = R == kRedPreMulSum;
+  static __device__ __forceinline__ uint32_t pre_word(uint32_t x, uint32_t s) { return x * s; }
+  static __device__ __forceinline__ S pre_elem(S x, uint32_t s) { return x * s; }
   static __device__ __forceinline__ uint32_t red_word(uint32_t a, uint32_t b) {
     if constexpr (R == kRedProd) return a * b;  // low 32 bits
     else if constexpr (R == kRedMax) return (int32_t)b > (int32_t)a ? b : a;
@@ -120,6 +130,14 @@ template <int R>
 struct TyBF16 {
   using S = uint16_t;
   static constexpr bool kPost = R == kRedAvg;
+  static constexpr bool kPre = R == kRedPreMulSum;
+  // bf16 x bf16 is exact in fp32: one rounding, to bf16
+  static __device__ __forceinline__ uint16_t pre_elem(uint16_t x, uint32_t s) {
+    return (uint16_t)bf16_rne(__uint_as_float((uint32_t)x << 16) * __uint_as_float(s << 16));
+  }
+  static __device__ __forceinline__ uint32_t pre_word(uint32_t x, uint32_t s) {
+    return (uint32_t)pre_elem((uint16_t)(x & 0xffffu), s) | ((uint32_t)pre_elem((uint16_t)(x >> 16), s) << 16);
+  }
   static __device__ __forceinline__ uint32_t red_half(uint32_t a, uint32_t b) {  // bf16 in the low 16 bits
     const float fa = __uint_as_float(a << 16), fb = __uint_as_float(b << 16);
     if constexpr (R == kRedMax) return fb > fa ? b : a;
@@ -130,7 +148,7 @@ struct TyBF16 {
     return (uint16_t)red_half(a, b);
   }
   static __device__ __forceinline__ uint32_t red_word(uint32_t a, uint32_t b) {
-    if constexpr (R == kRedSum || R == kRedAvg) {
+    if constexpr (R == kRedSum || R == kRedAvg || R == kRedPreMulSum) {
       const uint32_t lo = bf16_rne(__uint_as_float(a << 16) + __uint_as_float(b << 16));
       const uint32_t hi = bf16_rne(__uint_as_float(a & 0xffff0000u) + __uint_as_float(b & 0xffff0000u));
       return lo | (hi << 16);
@@ -150,6 +168,10 @@ template <class Ty>
 __device__ __forceinline__ uint64_t red8(uint64_t a, uint64_t b) {
   return (uint64_t)Ty::red_word((uint32_t)a, (uint32_t)b) |
          ((uint64_t)Ty::red_word((uint32_t)(a >> 32), (uint32_t)(b >> 32)) << 32);
+}
+template <class Ty>
+__device__ __forceinline__ uint64_t pre8(uint64_t a, uint32_t s) {
+  return (uint64_t)Ty::pre_word((uint32_t)a, s) | ((uint64_t)Ty::pre_word((uint32_t)(a >> 32), s) << 32);
 }
 template <class Ty>
 __device__ __forceinline__ uint64_t post8(uint64_t a, int n) {
@@ -183,6 +205,7 @@ struct Ctx {
   int rank, next, prev, nranks, ring_index, lane, nlanes, sps, spc;
   bool direct;       // Simple: all-gather half straight into the next rank's receive buffer
   bool direct_read;  // Simple: the loop's first receive reads the previous rank's send buffer
+  uint32_t s_own, s_prev;  // PreMulSum scalars of this rank and the previous one (current work)
   int64_t step_bytes;       // channel slot: sets the slice geometry
   int64_t lane_step_bytes;  // this lane's slot in its own FIFO
   uint8_t* recv_fifo;
@@ -201,6 +224,7 @@ struct Ctx {
   bool drop_head;  // fault test: never publish head credit
   uint32_t ll_mask;  // LL flag period - 1: 2^32 - 1, or 0xFF in the wrap test mode
   uint8_t* stage;    // LL128: per-wave LDS tiles for the user <-> line layout change
+  const uint32_t* scalars;  // PreMulSum: [buf_index * N + rank] scalar bits
   bool aborted;
   // The receiving workgroup of the send connector shares this workgroup's L2:
   // payload stores that have completed (vmcnt drained) are already visible to
@@ -309,6 +333,15 @@ __device__ __forceinline__ v4u red16(v4u a, v4u b) {
   return r;
 }
 template <class Ty>
+__device__ __forceinline__ v4u pre16(v4u a, uint32_t s) {
+  v4u r;
+  r.x = Ty::pre_word(a.x, s);
+  r.y = Ty::pre_word(a.y, s);
+  r.z = Ty::pre_word(a.z, s);
+  r.w = Ty::pre_word(a.w, s);
+  return r;
+}
+template <class Ty>
 __device__ __forceinline__ v4u post16(v4u a, int n) {
   v4u r;
   r.x = Ty::post_word(a.x, n);
@@ -365,13 +398,18 @@ __device__ __forceinline__ void stv(void* base, int64_t i, v4u v) {
 // is the owner's final step, which also applies the post-op (divisor n_post).
 // `fin` / `fout` are FIFO slots, or user buffers in the direct variants
 // (kUserIn / kUserOut), which then take the user-buffer access hint.
+// PreMulSum scales the own input by s_own and, when `fin` is the previous
+// rank's raw input (kRawIn, direct read), that by s_in.
 template <class Ty, bool kRecv, bool kSrc, bool kDst, bool kSend, bool kUserIn = false,
-          bool kUserOut = false>
+          bool kUserOut = false, bool kRawIn = false>
 __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typename Ty::S* src,
                                             typename Ty::S* dst, typename Ty::S* fout, int64_t n,
-                                            int tid, int nthr, int n_post) {
+                                            int tid, int nthr, int n_post, uint32_t s_own = 0,
+                                            uint32_t s_in = 0) {
   using S = typename Ty::S;
   constexpr bool kPost = kRecv && kSrc && kDst && Ty::kPost;
+  constexpr bool kPreOwn = kSrc && Ty::kPre;
+  constexpr bool kPreIn = kRecv && kRawIn && Ty::kPre;
   constexpr int kVec = 16 / sizeof(S);
   constexpr int kUnroll = RAR_UNROLL;
   constexpr bool kNu = RAR_NT_USER != 0;
@@ -388,6 +426,8 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+      if constexpr (kPreOwn) b[u] = pre16<Ty>(b[u], s_own);
+      if constexpr (kPreIn) a[u] = pre16<Ty>(a[u], s_in);
       v4u r = (kRecv && kSrc) ? red16<Ty>(a[u], b[u]) : (kRecv ? a[u] : b[u]);
       if constexpr (kPost) r = post16<Ty>(r, n_post);
       if (kDst) stv<kNu, true>(dst, i + (int64_t)u * nthr, r);
@@ -398,6 +438,8 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
     v4u a = {0, 0, 0, 0}, b = a;
     if (kRecv) a = ldv<kNi, kUserIn>(fin, i);
     if (kSrc) b = ldv<kNu, true>(src, i);
+    if constexpr (kPreOwn) b = pre16<Ty>(b, s_own);
+    if constexpr (kPreIn) a = pre16<Ty>(a, s_in);
     v4u r = (kRecv && kSrc) ? red16<Ty>(a, b) : (kRecv ? a : b);
     if constexpr (kPost) r = post16<Ty>(r, n_post);
     if (kDst) stv<kNu, true>(dst, i, r);
@@ -407,6 +449,8 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
     S a = 0, b = 0;
     if (kRecv) a = G(fin)[e];
     if (kSrc) b = G(src)[e];
+    if constexpr (kPreOwn) b = Ty::pre_elem(b, s_own);
+    if constexpr (kPreIn) a = Ty::pre_elem(a, s_in);
     S r = (kRecv && kSrc) ? Ty::red_elem(a, b) : (kRecv ? a : b);
     if constexpr (kPost) r = Ty::post_elem(r, n_post);
     if (kDst) G(dst)[e] = r;
@@ -470,24 +514,28 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
       const int64_t e0 = s_off + lo;
       if (read_prev && OP == kOpRecvReduceSend) {
         // previous rank's raw input + own input -> FIFO
-        reduce_copy<Ty, true, true, false, true, true, false>(prev_src + e0, src + e0, dst + e0, fout,
-                                                              hi - lo, cx.tid, cx.workers, cx.nranks);
+        reduce_copy<Ty, true, true, false, true, true, false, true>(prev_src + e0, src + e0, dst + e0, fout,
+                                                                    hi - lo, cx.tid, cx.workers, cx.nranks,
+                                                                    cx.s_own, cx.s_prev);
       } else if (read_prev && OP == kOpRecvReduceCopySend) {
         // two ranks: previous rank's raw input + own input -> own output, forwarded
         if (cx.direct)
-          reduce_copy<Ty, true, true, true, true, true, true>(prev_src + e0, src + e0, dst + e0,
-                                                              next_dst + e0, hi - lo, cx.tid,
-                                                              cx.workers, cx.nranks);
+          reduce_copy<Ty, true, true, true, true, true, true, true>(prev_src + e0, src + e0, dst + e0,
+                                                                    next_dst + e0, hi - lo, cx.tid,
+                                                                    cx.workers, cx.nranks, cx.s_own,
+                                                                    cx.s_prev);
         else
-          reduce_copy<Ty, true, true, true, true, true, false>(prev_src + e0, src + e0, dst + e0, fout,
-                                                               hi - lo, cx.tid, cx.workers, cx.nranks);
+          reduce_copy<Ty, true, true, true, true, true, false, true>(prev_src + e0, src + e0, dst + e0, fout,
+                                                                     hi - lo, cx.tid, cx.workers, cx.nranks,
+                                                                     cx.s_own, cx.s_prev);
       } else if (!cx.direct || OP == kOpSend || OP == kOpRecvReduceSend) {
         reduce_copy<Ty, O::kRecv, O::kSrc, O::kDst, O::kSend>(fin, src + e0, dst + e0, fout, hi - lo,
-                                                               cx.tid, cx.workers, cx.nranks);
+                                                               cx.tid, cx.workers, cx.nranks, cx.s_own);
       } else if (OP == kOpRecvReduceCopySend) {
         // FIFO partial + own input -> own output and the next rank's output
         reduce_copy<Ty, true, true, true, true, false, true>(fin, src + e0, dst + e0, next_dst + e0,
-                                                             hi - lo, cx.tid, cx.workers, cx.nranks);
+                                                             hi - lo, cx.tid, cx.workers, cx.nranks,
+                                                             cx.s_own);
       } else if (OP == kOpRecvCopySend) {
         // already in the own output (written by prev) -> the next rank's output
         reduce_copy<Ty, true, false, false, true, true, true>(dst + e0, src + e0, dst + e0,
@@ -603,7 +651,10 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
             a[u] = load_relaxed(rl + 2 * j);
             b[u] = load_relaxed(rl + 2 * j + 1);
           }
-          if (O::kSrc) own[u] = load_bytes8<S>(sb + 8 * j, nbytes - 8 * j);
+          if (O::kSrc) {
+            own[u] = load_bytes8<S>(sb + 8 * j, nbytes - 8 * j);
+            if constexpr (Ty::kPre) own[u] = pre8<Ty>(own[u], cx.s_own);
+          }
         }
       }
 #pragma unroll
@@ -790,6 +841,7 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
             own[u].y = (uint32_t)(w0 >> 32);
             own[u].z = (uint32_t)w1;
             own[u].w = (uint32_t)(w1 >> 32);
+            if constexpr (Ty::kPre) own[u] = pre16<Ty>(own[u], cx.s_own);
           }
           wave_sync();  // the tile is read before it is written again
         }
@@ -876,6 +928,10 @@ __device__ void run_ring(Ctx& cx, const DevWork& w) {
   S* recvbuf = reinterpret_cast<S*>(G(ptrs)[((int64_t)w.buf_index * N + cx.rank) * 2 + 1]);
   S* next_recvbuf = reinterpret_cast<S*>(G(ptrs)[((int64_t)w.buf_index * N + cx.next) * 2 + 1]);
   const S* prev_sendbuf = reinterpret_cast<const S*>(G(ptrs)[((int64_t)w.buf_index * N + cx.prev) * 2]);
+  if constexpr (Ty::kPre) {
+    cx.s_own = G(cx.scalars)[(int64_t)w.buf_index * N + cx.rank];
+    cx.s_prev = G(cx.scalars)[(int64_t)w.buf_index * N + cx.prev];
+  }
   int workers = (int)w.n_waves * kWaveSize;
   cx.workers = workers < cx.nthreads ? workers : cx.nthreads;
   const int64_t loop_count = (int64_t)N * w.chunk_count;
@@ -1013,6 +1069,8 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.timeout = sh.comm.spin_timeout_ticks;
   cx.drop_head = (sh.comm.debug_flags & 1) != 0;
   cx.ll_mask = sh.comm.ll_flag_mask;
+  cx.scalars = args.scalars;
+  cx.s_own = cx.s_prev = 0;
   cx.stage = stage;
   cx.aborted = false;
   cx.trace = (sh.comm.debug_flags & 2) ? sh.comm.trace + (int64_t)blockIdx.x * sh.comm.trace_cap : nullptr;
@@ -1074,6 +1132,8 @@ const void* ring_kernel_table(int proto, int red) {
        ring_allreduce_kernel<Ty<kRedMin>, kSimple>},
       {ring_allreduce_kernel<Ty<kRedAvg>, kLL>, ring_allreduce_kernel<Ty<kRedAvg>, kLL128>,
        ring_allreduce_kernel<Ty<kRedAvg>, kSimple>},
+      {ring_allreduce_kernel<Ty<kRedPreMulSum>, kLL>, ring_allreduce_kernel<Ty<kRedPreMulSum>, kLL128>,
+       ring_allreduce_kernel<Ty<kRedPreMulSum>, kSimple>},
   };
   if (proto < 0 || proto > 2 || red < 0 || red >= kNumRed) return nullptr;
   return reinterpret_cast<const void*>(table[red][proto]);

@@ -162,3 +162,11 @@ def test_oneshot_validates_on_the_host():
     for kw, why in bad:
         assert _oneshot_raw(**kw) == _lib.INVALID_ARGUMENT, why
     assert _oneshot_raw(ok_s, ok_r, 16, op=7) == _lib.INVALID_ARGUMENT  # unknown operator
+    # PreMulSum only through the entry point that takes scalars
+    assert _oneshot_raw(ok_s, ok_r, 16, op=5) == _lib.INVALID_ARGUMENT
+    lib = _lib.load()
+    s = (ctypes.c_void_p * 2)(*ok_s)
+    r = (ctypes.c_void_p * 2)(*ok_r)
+    t = _lib.OneshotTuning(0, 0, 0, 0)
+    assert lib.rar_oneshot_allreduce_premul(s, r, 2, 16, _lib.DTYPE["float32"], None,
+                                            ctypes.byref(t), None) == _lib.INVALID_ARGUMENT
