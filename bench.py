@@ -32,7 +32,7 @@ TUNING = {
     "bf16_n8": dict(lanes=2, waves=8, launch_mode=1),
     "int32_n8": dict(lanes=2, waves=8, launch_mode=1),
     "ll_512k": dict(lanes=16, waves=2, launch_mode=1),
-    "fused_ll": dict(lanes=1, waves=4, launch_mode=1),
+    "fused_ll": dict(lanes=8, waves=4, launch_mode=1, deal_works=1),
     "simple_4k": dict(lanes=1, waves=4, launch_mode=1),
 }
 # Launch shape of the one-shot kernel per workload (performance only).
@@ -131,6 +131,8 @@ def main():
     ap.add_argument("--placement", type=int, default=None, choices=[0, 1])
     ap.add_argument("--direct", type=int, default=None, choices=[0, 1, 2, 3],
                     help="Simple direct variants: bit 0 write, bit 1 read")
+    ap.add_argument("--deal-works", type=int, default=None, choices=[0, 1],
+                    help="1: the lanes of a channel take its works in turn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the AllReduce, time a plain device copy of MIB MiB "
@@ -186,6 +188,8 @@ def main():
         tune["placement"] = args.placement
     if args.direct is not None:
         tune["direct"] = args.direct
+    if args.deal_works is not None:
+        tune["deal_works"] = args.deal_works
     torch.cuda.set_device(0)
     xs = workloads.inputs_for(w)
     N = w.nranks

@@ -123,6 +123,15 @@ typedef struct {
                             of traffic (6N-4)M, (5N-4)M with bit 0, (6N-6)M
                             with bit 1, (5N-6)M with both.  Buffers of
                             different ranks must not overlap.              */
+  int deal_works;        /* 0: the lanes of a channel split the lines of
+                            every step.  1: they take the channel's works
+                            in turn (work k of the channel runs whole on
+                            lane k mod lanes_per_channel, over that lane's
+                            own FIFO, which then holds the full buff_size).
+                            A fused group of many small works is bound by
+                            the latency of its dependent steps, not by
+                            bytes: dealing the works divides the steps each
+                            workgroup runs in sequence.  Timing only    */
 } rar_tuning_t;
 
 #define RAR_DEBUG_DROP_RECV_HEAD 1

@@ -21,7 +21,8 @@ class Tuning(ctypes.Structure):
     _fields_ = [("lanes_per_channel", ctypes.c_int), ("waves_per_lane", ctypes.c_int),
                 ("spin_timeout_us", ctypes.c_int), ("debug_flags", ctypes.c_int),
                 ("launch_mode", ctypes.c_int), ("placement", ctypes.c_int),
-                ("slices_per_chunk", ctypes.c_int), ("direct", ctypes.c_int)]
+                ("slices_per_chunk", ctypes.c_int), ("direct", ctypes.c_int),
+                ("deal_works", ctypes.c_int)]
 
 
 class OneshotTuning(ctypes.Structure):

@@ -324,7 +324,7 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
   for (int k = 0; k < nrings; ++k)
     if (!rar::build_ring(nranks, ring_orders + (size_t)k * nranks, &rings[k], &err))
       return fail(RAR_INVALID_ARGUMENT, "ring " + std::to_string(k) + ": " + err);
-  rar_tuning_t tune{0, 0, 0, 0, 0, 0, 0, 0};
+  rar_tuning_t tune{0, 0, 0, 0, 0, 0, 0, 0, 0};
   if (tuning) tune = *tuning;
   if (tune.lanes_per_channel < 0 || tune.lanes_per_channel > rar::kMaxLanes)
     return fail(RAR_INVALID_ARGUMENT, "lanes_per_channel must be in [0, 16]");
@@ -344,6 +344,8 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
     return fail(RAR_INVALID_ARGUMENT, "direct must be 0..3 (bit 0 write, bit 1 read)");
   if (tune.direct && (int)proto != rar::kSimple)
     return fail(RAR_UNSUPPORTED, "the direct variant exists for the Simple protocol only");
+  if (tune.deal_works != 0 && tune.deal_works != 1)
+    return fail(RAR_INVALID_ARGUMENT, "deal_works must be 0 or 1");
 
   int dev = 0;
   RAR_HIP(hipGetDevice(&dev));
@@ -395,7 +397,8 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
     release(c);
     return fail(RAR_HIP_ERROR, std::string(what) + " failed: " + hipGetErrorString(e));
   };
-  const int64_t lane_step = rar::lane_step_bytes(proto, buff_size, c->P);
+  // dealt works run whole on one lane: every lane FIFO holds the full buffer
+  const int64_t lane_step = rar::lane_step_bytes(proto, buff_size, tune.deal_works ? 1 : c->P);
   const size_t fifo_bytes = (size_t)nranks * c->C * c->P * rar::kSteps * (size_t)lane_step;
   const size_t counter_bytes = (size_t)nranks * c->C * c->P * sizeof(rar::ConnCounters);
   rar_result_t r;
@@ -457,6 +460,7 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
   const int spc = tune.slices_per_chunk ? tune.slices_per_chunk : rar::kSlicesPerChunk;
   hc.hot.slices_per_chunk = spc;
   hc.hot.direct = tune.direct;
+  hc.hot.deal_works = tune.deal_works;
   hc.hot.step_per_slice = (int)proto == rar::kSimple ? chunk_steps / spc : 1;
   hc.hot.channel_mask = channel_mask;
   hc.hot.fifo = c->d_fifo;

@@ -118,6 +118,7 @@ struct alignas(16) DevCommHot {
   uint64_t* placement;         // [grid] epoch << 8 | XCC id, written at kernel entry
   const uint32_t* wg_of;       // [(r * C + n) * P + p] -> workgroup index in the grid
   uint32_t ll_flag_mask;       // LL flag period - 1 (0xFFFFFFFF, or 0xFF in the wrap test mode)
+  int32_t deal_works;          // 1: work k of a channel runs whole on lane k mod n_lanes
 };
 static_assert(sizeof(DevCommHot) % 16 == 0, "hot fields are copied in 16-byte packs");
 

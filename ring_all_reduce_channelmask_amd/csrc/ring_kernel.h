@@ -16,6 +16,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "rar_device.h"
 
 namespace rar {
@@ -203,6 +205,9 @@ struct Ctx {
   void* const* ptrs;
   int tid, nthreads, workers;
   int rank, next, prev, nranks, ring_index, lane, nlanes, sps, spc;
+  // this workgroup's part of every step: part split_lane of split_lanes
+  // (the lane of nlanes, or the whole step when the works are dealt)
+  int split_lane, split_lanes;
   bool direct;       // Simple: all-gather half straight into the next rank's receive buffer
   bool direct_read;  // Simple: the loop's first receive reads the previous rank's send buffer
   uint32_t s_own, s_prev;  // PreMulSum scalars of this rank and the previous one (current work)
@@ -488,8 +493,8 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
     const int64_t s_off = (int64_t)s * slice;
     const int64_t s_n = clamp64(nelem - s_off, 0, slice);
     // this lane's part of the slice, in whole 16-byte vectors
-    const int64_t part = kVec * div_up(div_up(s_n, kVec), cx.nlanes);
-    const int64_t lo = clamp64((int64_t)cx.lane * part, 0, s_n);
+    const int64_t part = kVec * div_up(div_up(s_n, kVec), cx.split_lanes);
+    const int64_t lo = clamp64((int64_t)cx.split_lane * part, 0, s_n);
     const int64_t hi = clamp64(lo + part, 0, s_n);
     const uint64_t t0 = cx.trace ? now_ticks() : 0;
     const uint64_t step0 = cx.recv_step;
@@ -620,8 +625,8 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
   constexpr int U = kLlUnroll;
   const int64_t nbytes = nelem * (int64_t)sizeof(S);
   const int64_t nlines = div_up(nbytes, 8);
-  const int64_t part = div_up(nlines, cx.nlanes);
-  const int64_t lo = clamp64((int64_t)cx.lane * part, 0, nlines);
+  const int64_t part = div_up(nlines, cx.split_lanes);
+  const int64_t lo = clamp64((int64_t)cx.split_lane * part, 0, nlines);
   const int64_t hi = clamp64(lo + part, 0, nlines);
   const uint64_t t0 = cx.trace ? now_ticks() : 0;
   const uint64_t step0 = cx.recv_step;
@@ -712,13 +717,18 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
 // receiver is on another XCD), then the flag words.  Receiver: the flag lanes
 // poll every line of the wave, the wave votes until none is missing, then one
 // acquire fence precedes the data loads.
-constexpr int kLl128Unroll = 2;  // groups of 8 lines in flight per wave
+#ifndef RAR_LL128_UNROLL
+#define RAR_LL128_UNROLL 2
+#endif
+constexpr int kLl128Unroll = RAR_LL128_UNROLL;  // groups of 8 lines in flight per wave
 
-// Orders this wave's LDS accesses around a hand-off between its lanes.
+// Orders this wave's LDS accesses around a hand-off between its lanes.  The
+// fences cover LDS only ("local"): a fence over all address spaces would also
+// wait for the wave's outstanding global stores.
 __device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
 template <class S>
@@ -746,8 +756,8 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
   const int64_t nlines = div_up(nbytes, 120);
   // lanes take an even number of lines, so every group of 8 lines starts
   // 16-byte aligned in the user buffer (120 x 2 = 15 x 16)
-  const int64_t part = 2 * div_up(nlines, 2 * (int64_t)cx.nlanes);
-  const int64_t lo = clamp64((int64_t)cx.lane * part, 0, nlines);
+  const int64_t part = 2 * div_up(nlines, 2 * (int64_t)cx.split_lanes);
+  const int64_t lo = clamp64((int64_t)cx.split_lane * part, 0, nlines);
   const int64_t hi = clamp64(lo + part, 0, nlines);
   const uint64_t t0 = cx.trace ? now_ticks() : 0;
   const uint64_t step0 = cx.recv_step;
@@ -806,31 +816,60 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
       const int64_t ub = 16 * (int64_t)lid;  // this lane's 16 bytes of a group, user layout
       const bool ulane = lid < 60;
       const v4u zero = {0, 0, 0, 0};
-      for (int64_t g0 = first; g0 < hi; g0 += (int64_t)U * stride) {
-        v4u in[U], own[U];
-        int64_t gb[U], gvalid[U];
+      // The FIFO words (in) and user bytes (x) of U groups of 8 lines, group u
+      // starting at line g + u * stride.  whole(g): all U groups are full
+      // lines inside the step and the chunk.
+      auto whole = [&](int64_t g) {
+        const int64_t last_end = g + (int64_t)(U - 1) * stride + 8;
+        return last_end <= hi && 120 * last_end <= nbytes;
+      };
+      auto load_whole = [&](int64_t g, v4u* in, v4u* x) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t gs = g0 + (int64_t)u * stride;  // first line of group u
-          const int64_t ge = gs + 8 < hi ? gs + 8 : hi;
-          gb[u] = 120 * gs;
-          const int64_t gend = 120 * ge < nbytes ? 120 * ge : nbytes;
-          gvalid[u] = gs < hi ? gend - gb[u] : 0;  // payload bytes of the group
-          const int64_t j = gs + sub;
+          const int64_t j = g + (int64_t)u * stride + sub;
           in[u] = zero;
-          own[u] = zero;
-          if (O::kRecv && j < hi) {
+          if (O::kRecv) {
             in[u] = *G(reinterpret_cast<const v4u*>(rl + 16 * j + 2 * k));
             if (k == 7) in[u].z = in[u].w = 0;  // the flag word is not payload
           }
+        }
+        // lanes 60..63 hold no user bytes of a group: they repeat lane 0's
+        // load (in bounds) so that no load needs a branch around it
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          x[u] = O::kSrc ? ldv<kNu, true>(sb + 120 * (g + (int64_t)u * stride) + (ulane ? ub : 0), 0) : zero;
+      };
+      auto load_part = [&](int64_t g, v4u* in, v4u* x) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t gs = g + (int64_t)u * stride;  // first line of group u
+          const int64_t ge = gs + 8 < hi ? gs + 8 : hi;
+          const int64_t gend = 120 * ge < nbytes ? 120 * ge : nbytes;
+          const int64_t gvalid = gs < hi ? gend - 120 * gs : 0;  // payload bytes of the group
+          const int64_t j = gs + sub;
+          in[u] = zero;
+          x[u] = zero;
+          if (O::kRecv && j < hi) {
+            in[u] = *G(reinterpret_cast<const v4u*>(rl + 16 * j + 2 * k));
+            if (k == 7) in[u].z = in[u].w = 0;
+          }
           if (O::kSrc && ulane) {
-            v4u x = zero;
-            if (ub + 16 <= gvalid[u]) x = ldv<kNu, true>(sb + gb[u] + ub, 0);
-            else if (ub < gvalid[u]) x = load_bytes16<S>(sb + gb[u] + ub, gvalid[u] - ub, 16);
-            *reinterpret_cast<v4u*>(stage + u * 1024 + ub) = x;
+            if (ub + 16 <= gvalid) x[u] = ldv<kNu, true>(sb + 120 * gs + ub, 0);
+            else if (ub < gvalid) x[u] = load_bytes16<S>(sb + 120 * gs + ub, gvalid - ub, 16);
           }
         }
+      };
+      // Reduce and store the U groups at g whose loads are in `in` and `x`;
+      // kWhole: every group is whole (known at compile time: no bounds
+      // checks around the stores).
+      auto process = [&](auto kWhole, int64_t g, const v4u* in, const v4u* x) {
+        v4u own[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) own[u] = zero;
         if (O::kSrc) {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (ulane) *reinterpret_cast<v4u*>(stage + u * 1024 + ub) = x[u];
           wave_sync();
 #pragma unroll
           for (int u = 0; u < U; ++u) {
@@ -851,8 +890,8 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
           v[u] = (O::kRecv && O::kSrc) ? red16<Ty>(in[u], own[u]) : (O::kRecv ? in[u] : own[u]);
           if constexpr (OP == kOpRecvReduceCopySend && Ty::kPost) v[u] = post16<Ty>(v[u], cx.nranks);
           if (k == 7) v[u].z = v[u].w = 0;  // flag placeholder
-          const int64_t j = g0 + (int64_t)u * stride + sub;
-          if (O::kSend && j < hi) *G(reinterpret_cast<v4u*>(sl + 16 * j + 2 * k)) = v[u];
+          const int64_t j = g + (int64_t)u * stride + sub;
+          if (O::kSend && (kWhole || j < hi)) *G(reinterpret_cast<v4u*>(sl + 16 * j + 2 * k)) = v[u];
         }
         if (O::kDst) {
 #pragma unroll
@@ -865,12 +904,53 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             if (!ulane) continue;
-            const v4u x = *reinterpret_cast<const v4u*>(stage + u * 1024 + ub);
-            if (ub + 16 <= gvalid[u]) stv<kNu, true>(db + gb[u] + ub, 0, x);
-            else if (ub < gvalid[u]) store_bytes16<S>(db + gb[u] + ub, x, gvalid[u] - ub, 16);
+            const int64_t gs = g + (int64_t)u * stride;
+            const v4u y = *reinterpret_cast<const v4u*>(stage + u * 1024 + ub);
+            if (kWhole) {
+              stv<kNu, true>(db + 120 * gs + ub, 0, y);
+              continue;
+            }
+            const int64_t ge = gs + 8 < hi ? gs + 8 : hi;
+            const int64_t gend = 120 * ge < nbytes ? 120 * ge : nbytes;
+            const int64_t gvalid = gs < hi ? gend - 120 * gs : 0;
+            if (ub + 16 <= gvalid) stv<kNu, true>(db + 120 * gs + ub, 0, y);
+            else if (ub < gvalid) store_bytes16<S>(db + 120 * gs + ub, y, gvalid - ub, 16);
           }
           wave_sync();
         }
+      };
+      // Whole groups run software-pipelined: the next iteration's loads are
+      // issued before this iteration's stores, so waiting for them never
+      // waits for those stores too (the vector memory counter retires in
+      // order).  The partial groups at the end of a share follow unpipelined.
+      // Two register sets take turns (no copies between them, which would
+      // wait for the loads).  Without a next iteration the loads repeat the
+      // current one's (unused), so no branch surrounds them and the wait
+      // before their use stays exact.
+      const std::integral_constant<bool, true> kW{};
+      const std::integral_constant<bool, false> kP{};
+      const int64_t gstep = (int64_t)U * stride;
+      int64_t g0 = first;
+      if (g0 < hi && whole(g0)) {
+        v4u inA[U], xA[U], inB[U], xB[U];
+        load_whole(g0, inA, xA);
+        for (;;) {
+          bool more = g0 + gstep < hi && whole(g0 + gstep);
+          load_whole(more ? g0 + gstep : g0, inB, xB);
+          process(kW, g0, inA, xA);
+          g0 += gstep;
+          if (!more) break;
+          more = g0 + gstep < hi && whole(g0 + gstep);
+          load_whole(more ? g0 + gstep : g0, inA, xA);
+          process(kW, g0, inB, xB);
+          g0 += gstep;
+          if (!more) break;
+        }
+      }
+      for (; g0 < hi; g0 += gstep) {
+        v4u in[U], x[U];
+        load_part(g0, in, x);
+        process(kP, g0, in, x);
       }
       if (O::kSend) {
         // data words before flag words: drained into this L2, and written
@@ -1044,6 +1124,9 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.prev = me.prev;
   cx.lane = lane;
   cx.nlanes = sh.comm.n_lanes;
+  const bool deal = sh.comm.deal_works != 0;
+  cx.split_lane = deal ? 0 : lane;
+  cx.split_lanes = deal ? 1 : cx.nlanes;
   cx.sps = sh.comm.step_per_slice;
   cx.spc = sh.comm.slices_per_chunk;
   cx.step_bytes = sh.comm.step_bytes;
@@ -1095,12 +1178,15 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
 
   // RunWorkBatch [C23 "RunWorkBatch 与 Fused Work"]: the works of a batch run
   // in order; a change of active waves is fenced by a barrier; next_jump
-  // chains the channel's next batch.
+  // chains the channel's next batch.  With dealt works, the k-th work of the
+  // channel (counted over all its batches) runs on lane k mod n_lanes only.
   uint32_t b = first;
+  uint32_t seq = 0;
   while (b != 0) {
     const int nworks = sh.n_works;
-    for (int w = 0; w < nworks; ++w) {
+    for (int w = 0; w < nworks; ++w, ++seq) {
       if (w > 0 && sh.works[w].n_waves != sh.works[w - 1].n_waves) __syncthreads();
+      if (deal && (int)(seq % (uint32_t)cx.nlanes) != lane) continue;
       run_ring<Ty, PROTO>(cx, sh.works[w]);
       if (cx.aborted) break;
     }

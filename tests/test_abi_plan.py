@@ -116,6 +116,7 @@ def test_comm_create_validates_before_touching_a_device():
                    dict(nranks=4, ring_order=[0, 1, 2, 3], mask=1, chunk_steps=8),
                    dict(nranks=4, ring_order=[0, 1, 2, 3], mask=1, lanes=99),
                    dict(nranks=4, ring_order=[0, 1, 2, 3], mask=1, waves=9),
+                   dict(nranks=4, ring_order=[0, 1, 2, 3], mask=1, deal_works=2),
                    dict(nranks=4, ring_order=[[0, 1, 2, 3], [0, 1, 3, 3]], mask=3),
                    dict(nranks=3, ring_order=[[0, 1, 2]] * 65, mask=1)]:
         with pytest.raises(rar.RarError) as e:

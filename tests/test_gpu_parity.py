@@ -466,3 +466,50 @@ def test_direct_read_write_full_size_and_many_launches(placement):
     want = cf.allreduce([x], list(w.ring_order), w.mask, "SIMPLE", w.buff_size, 4, "float32")[0]
     for r in range(4):
         assert_bits_equal(to_host(recvs[r], "float32"), want, f"rank {r}")
+
+
+# ------------------------------------------------- works dealt to lanes
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128"])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+def test_dealt_works_vs_simulator(proto, dtype):
+    """Lanes that take a channel's works in turn instead of splitting every
+    step: a fused group over a sparse mask with a work count that is not a
+    multiple of the lanes, ragged sizes, a single work (one lane busy, the
+    others idle), and a group long enough to chain batches.  Same bits as the
+    simulator, launch after launch on one communicator."""
+    mask = 0b1011
+    buff = SMALL_BUFF[proto]
+    cs = 4 if proto == "SIMPLE" else 0
+    comm = _comm(nranks=4, ring_order=[0, 2, 3, 1], mask=mask, proto=proto, buff_size=buff,
+                 chunk_steps=cs, lanes=3, waves=2, deal_works=1)
+    groups = [
+        [_rand(dtype, (4, c), 700 + i) for i, c in enumerate([5000, 1, 777, 3001, 64, 9999, 17])],
+        [_rand(dtype, (4, 20011), 720)],
+        [_rand(dtype, (4, 50 + 13 * i), 730 + i) for i in range(70)],
+    ]
+    for xs in groups + groups[:1]:
+        _check_vs_sim(comm, xs, dtype, buff, 4)
+    comm.close()
+
+
+@pytest.mark.parametrize("placement", [0, 1])
+def test_dealt_works_with_direct_ops_and_in_place(placement):
+    """Dealt works under the Simple direct variants, a non-sum operator and in
+    place, with ranks spread over XCDs or not."""
+    buff = SMALL_BUFF["SIMPLE"]
+    xs = [_rand("float32", (4, c), 760 + i) for i, c in enumerate([4099, 12000, 5, 800, 2500])]
+    for direct in (0, 1, 3):
+        comm = _comm(nranks=4, ring_order=[1, 3, 0, 2], mask=0x6, proto="SIMPLE", buff_size=buff,
+                     chunk_steps=4, lanes=2, waves=4, deal_works=1, direct=direct,
+                     placement=placement)
+        got = run_hip(comm, xs, "float32", in_place=True)
+        want = cf.allreduce(xs, [1, 3, 0, 2], 0x6, "SIMPLE", buff, 4, "float32")
+        for i in range(len(xs)):
+            for r in range(4):
+                assert_bits_equal(got[i][r], want[i], f"direct {direct} work {i} rank {r}")
+        got = run_hip(comm, xs, "float32", op="max")
+        want = cf.allreduce(xs, [1, 3, 0, 2], 0x6, "SIMPLE", buff, 4, "float32", op="max")
+        for i in range(len(xs)):
+            for r in range(4):
+                assert_bits_equal(got[i][r], want[i], f"max direct {direct} work {i} rank {r}")
+        comm.close()
