@@ -44,6 +44,14 @@ __device__ __forceinline__ __attribute__((address_space(1))) T* G(T* p) {
   return (__attribute__((address_space(1))) T*)p;
 }
 
+// A value that is the same on every lane of the wave, moved to a scalar
+// register so that the compiler knows it is uniform.
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ---------------------------------------------------------------- ordering
 __device__ __forceinline__ uint64_t load_relaxed(const uint64_t* p) {
   return __hip_atomic_load(G(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -420,25 +428,38 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
   constexpr bool kNu = RAR_NT_USER != 0;
   constexpr bool kNi = kUserIn ? RAR_NT_DIRECT != 0 : RAR_NT_FIFO != 0;
   constexpr bool kNo = kUserOut ? RAR_NT_DIRECT != 0 : RAR_NT_FIFO != 0;
-  const int64_t nv = n / kVec;
-  int64_t i = tid;
-  for (; i + (int64_t)(kUnroll - 1) * nthr < nv; i += (int64_t)kUnroll * nthr) {
-    v4u a[kUnroll], b[kUnroll];
+  // The unrolled loop runs on wave-uniform indices (scalar registers, so it
+  // branches per wave): block ib covers ib + lane + u * nthr for every lane.
+  const int64_t nv = uni64(n / kVec);
+  const int nth = __builtin_amdgcn_readfirstlane(nthr);
+  const int lane = tid & 63;
+  const int64_t istep = (int64_t)kUnroll * nth;
+  auto full = [&](int64_t ib) { return ib + 63 + (int64_t)(kUnroll - 1) * nth < nv; };
+  auto load = [&](int64_t ib, v4u* a, v4u* b) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (kRecv) a[u] = ldv<kNi, kUserIn>(fin, i + (int64_t)u * nthr);
-      if (kSrc) b[u] = ldv<kNu, true>(src, i + (int64_t)u * nthr);
+      if (kRecv) a[u] = ldv<kNi, kUserIn>(fin, ib + lane + (int64_t)u * nth);
+      if (kSrc) b[u] = ldv<kNu, true>(src, ib + lane + (int64_t)u * nth);
     }
+  };
+  auto reduce_store = [&](int64_t ib, v4u* a, v4u* b) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if constexpr (kPreOwn) b[u] = pre16<Ty>(b[u], s_own);
       if constexpr (kPreIn) a[u] = pre16<Ty>(a[u], s_in);
       v4u r = (kRecv && kSrc) ? red16<Ty>(a[u], b[u]) : (kRecv ? a[u] : b[u]);
       if constexpr (kPost) r = post16<Ty>(r, n_post);
-      if (kDst) stv<kNu, true>(dst, i + (int64_t)u * nthr, r);
-      if (kSend) stv<kNo, kUserOut>(fout, i + (int64_t)u * nthr, r);
+      if (kDst) stv<kNu, true>(dst, ib + lane + (int64_t)u * nth, r);
+      if (kSend) stv<kNo, kUserOut>(fout, ib + lane + (int64_t)u * nth, r);
     }
+  };
+  int64_t ib = __builtin_amdgcn_readfirstlane(tid - lane);
+  for (; full(ib); ib += istep) {
+    v4u a[kUnroll], b[kUnroll];
+    load(ib, a, b);
+    reduce_store(ib, a, b);
   }
+  int64_t i = ib + lane;
   for (; i < nv; i += nthr) {
     v4u a = {0, 0, 0, 0}, b = a;
     if (kRecv) a = ldv<kNi, kUserIn>(fin, i);
@@ -752,16 +773,20 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
   using S = typename Ty::S;
   using O = OpTraits<OP>;
   constexpr int U = kLl128Unroll;
-  const int64_t nbytes = nelem * (int64_t)sizeof(S);
+  // the share's bounds and the wave index are the same on every lane of a
+  // wave: held in scalar registers, the loops below branch per wave rather
+  // than through lane masks
+  const int64_t nbytes = uni64(nelem * (int64_t)sizeof(S));
   const int64_t nlines = div_up(nbytes, 120);
   // lanes take an even number of lines, so every group of 8 lines starts
   // 16-byte aligned in the user buffer (120 x 2 = 15 x 16)
   const int64_t part = 2 * div_up(nlines, 2 * (int64_t)cx.split_lanes);
-  const int64_t lo = clamp64((int64_t)cx.split_lane * part, 0, nlines);
-  const int64_t hi = clamp64(lo + part, 0, nlines);
+  const int64_t lo = uni64(clamp64((int64_t)cx.split_lane * part, 0, nlines));
+  const int64_t hi = uni64(clamp64(lo + part, 0, nlines));
   const uint64_t t0 = cx.trace ? now_ticks() : 0;
   const uint64_t step0 = cx.recv_step;
-  const int wave = cx.tid >> 6, lid = cx.tid & 63, nw = cx.workers >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(cx.tid >> 6), lid = cx.tid & 63;
+  const int nw = __builtin_amdgcn_readfirstlane(cx.workers >> 6);
   const int sub = lid >> 3;  // line within the wave's group of 8
   const int k = lid & 7;     // 16-byte segment of the line
 
@@ -924,9 +949,8 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
       // waits for those stores too (the vector memory counter retires in
       // order).  The partial groups at the end of a share follow unpipelined.
       // Two register sets take turns (no copies between them, which would
-      // wait for the loads).  Without a next iteration the loads repeat the
-      // current one's (unused), so no branch surrounds them and the wait
-      // before their use stays exact.
+      // wait for the loads); the last whole iteration is peeled (nothing to
+      // prefetch), and no load sits under a branch, so the waits stay exact.
       const std::integral_constant<bool, true> kW{};
       const std::integral_constant<bool, false> kP{};
       const int64_t gstep = (int64_t)U * stride;
@@ -935,16 +959,22 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
         v4u inA[U], xA[U], inB[U], xB[U];
         load_whole(g0, inA, xA);
         for (;;) {
-          bool more = g0 + gstep < hi && whole(g0 + gstep);
-          load_whole(more ? g0 + gstep : g0, inB, xB);
+          if (!(g0 + gstep < hi && whole(g0 + gstep))) {
+            process(kW, g0, inA, xA);
+            g0 += gstep;
+            break;
+          }
+          load_whole(g0 + gstep, inB, xB);
           process(kW, g0, inA, xA);
           g0 += gstep;
-          if (!more) break;
-          more = g0 + gstep < hi && whole(g0 + gstep);
-          load_whole(more ? g0 + gstep : g0, inA, xA);
+          if (!(g0 + gstep < hi && whole(g0 + gstep))) {
+            process(kW, g0, inB, xB);
+            g0 += gstep;
+            break;
+          }
+          load_whole(g0 + gstep, inA, xA);
           process(kW, g0, inB, xB);
           g0 += gstep;
-          if (!more) break;
         }
       }
       for (; g0 < hi; g0 += gstep) {
