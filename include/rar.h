@@ -25,6 +25,15 @@
  *     [C23 "排障树": reusing a buffer before the stream completes corrupts it].
  *   - Calls on one communicator must be issued in order on one stream.
  *   - On any error nothing is launched; rar_get_last_error() gives detail.
+ *   - HIP graphs: rar_allreduce, rar_allreduce_premul and rar_group_end may
+ *     be called while their stream is being captured, on a communicator made
+ *     with launch_mode 1, when the launch plan fits in the 3,584 bytes that
+ *     travel inside the kernel arguments (every single AllReduce up to 16
+ *     channels and 8 ranks; small groups).  The captured kernel node reads
+ *     the buffers named at capture time; each replay is one more launch on
+ *     the communicator, stream-ordered with its other launches like an eager
+ *     call.  Otherwise the capturing call fails with RAR_UNSUPPORTED before
+ *     anything is enqueued.  The one-shot entry points capture as they are.
  */
 #ifndef RAR_H
 #define RAR_H
@@ -198,9 +207,9 @@ rar_result_t rar_comm_create_rings(rar_comm_t* comm, int nranks, int nrings,
  *                       FIFO steps untouched and does not look at the pointers.
  * Inside rar_group_start/rar_group_end the call is queued instead of launched.
  * Errors: RAR_INVALID_ARGUMENT (NULL or misaligned pointer, bad enum),
- * RAR_UNSUPPORTED (a group mixing dtypes or operators), RAR_ABORTED
- * (poisoned communicator),
- * RAR_HIP_ERROR (launch failed). */
+ * RAR_UNSUPPORTED (a group mixing dtypes or operators; under stream capture,
+ * a cooperative communicator or a plan too large to travel inline),
+ * RAR_ABORTED (poisoned communicator), RAR_HIP_ERROR (launch failed). */
 rar_result_t rar_allreduce(rar_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                            size_t count, rar_dtype_t dtype, rar_redop_t op, void* stream);
 

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cstdint>
 #include <cstring>
 #include <map>
@@ -94,7 +95,6 @@ struct rar_comm {
   rar::TraceRec* d_trace = nullptr;
   uint64_t* d_placement = nullptr;
   uint32_t* d_wg_of = nullptr;
-  uint64_t epoch = 0;
   uint32_t* d_trace_count = nullptr;
   uint8_t* d_arena = nullptr;
   size_t arena_cap = 0;
@@ -192,7 +192,31 @@ rar_result_t launch(rar_comm* c, const std::vector<QueuedCall>& calls, hipStream
     for (int r = 0; r < c->nranks && !calls[w].scalars.empty(); ++r) scal[w * c->nranks + r] = calls[w].scalars[r];
   std::memcpy(bytes.data() + off_first, plan.first_batch.data(), plan.first_batch.size() * sizeof(uint32_t));
 
-  if (bytes != c->last_upload) {
+  rar::KernelArgs args;
+  std::memset(&args, 0, offsetof(rar::KernelArgs, plan));
+  args.comm = c->d_comm;
+  args.wg_map = c->d_wgmap;
+  args.off_batches = (uint32_t)off_batches;
+  args.off_works = (uint32_t)off_works;
+  args.off_ptrs = (uint32_t)off_ptrs;
+  args.off_first = (uint32_t)off_first;
+  args.off_scalars = (uint32_t)off_scalars;
+  // Under stream capture the launch becomes a graph node whose arguments are
+  // copied at capture time: the plan must travel inline, and the launch must
+  // be a plain one.
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  RAR_HIP(hipStreamIsCapturing(stream, &capture));
+  const bool capturing = capture != hipStreamCaptureStatusNone;
+  if (capturing && c->launch_mode == 0)
+    return fail(RAR_UNSUPPORTED, "a cooperative launch cannot be captured: use launch_mode 1");
+  if (total <= (size_t)rar::kInlinePlanBytes) {
+    args.inline_plan = 1;
+    std::memcpy(args.plan, bytes.data(), total);
+  } else if (capturing) {
+    return fail(RAR_UNSUPPORTED, "a launch plan of " + std::to_string(total) +
+                                     " bytes exceeds the " + std::to_string(rar::kInlinePlanBytes) +
+                                     " bytes a captured launch carries inline");
+  } else if (bytes != c->last_upload) {
     if (total > c->arena_cap) {
       RAR_HIP(hipDeviceSynchronize());  // the old arena may still be read by a running launch
       (void)hipFree(c->d_arena);
@@ -218,15 +242,7 @@ rar_result_t launch(rar_comm* c, const std::vector<QueuedCall>& calls, hipStream
     c->last_upload.swap(bytes);
   }
 
-  rar::KernelArgs args;
-  args.comm = c->d_comm;
-  args.batches = reinterpret_cast<const rar::DevBatch*>(c->d_arena + off_batches);
-  args.works = reinterpret_cast<const rar::DevWork*>(c->d_arena + off_works);
-  args.ptrs = reinterpret_cast<void* const*>(c->d_arena + off_ptrs);
-  args.first_batch = reinterpret_cast<const uint32_t*>(c->d_arena + off_first);
-  args.scalars = reinterpret_cast<const uint32_t*>(c->d_arena + off_scalars);
-  args.wg_map = c->d_wgmap;
-  args.epoch = ++c->epoch;
+  if (!args.inline_plan) args.arena = c->d_arena;
   void* params[] = {&args};
   const void* fn = rar::get_kernel(dtype, c->proto, calls.front().red);
   if (!fn) return fail(RAR_INTERNAL_ERROR, "no kernel for this dtype/protocol/operator");

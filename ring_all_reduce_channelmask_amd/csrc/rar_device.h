@@ -115,7 +115,7 @@ struct alignas(16) DevCommHot {
   int32_t trace_cap;           // records per workgroup
   TraceRec* trace;             // [grid][trace_cap]
   uint32_t* trace_count;       // [grid] records written by the last launch
-  uint64_t* placement;         // [grid] epoch << 8 | XCC id, written at kernel entry
+  uint64_t* placement;         // [grid] launch count << 8 | XCC id, written at kernel entry
   const uint32_t* wg_of;       // [(r * C + n) * P + p] -> workgroup index in the grid
   uint32_t ll_flag_mask;       // LL flag period - 1 (0xFFFFFFFF, or 0xFF in the wrap test mode)
   int32_t deal_works;          // 1: work k of a channel runs whole on lane k mod n_lanes
@@ -130,16 +130,28 @@ struct alignas(16) DevComm {
   DevRank ranks[kMaxChannels][kMaxRanks];
 };
 
-// Kernel arguments (by value).
-struct KernelArgs {
+// Bytes of launch plan that travel inside the kernel arguments.  A plan that
+// fits (every single collective up to 16 channels and 8 ranks, small groups)
+// needs no upload before the launch, and a captured launch stays valid for
+// every replay of its graph.
+constexpr int kInlinePlanBytes = 3584;
+
+// Kernel arguments (by value).  The launch plan is one block of bytes, either
+// `plan` below (inline_plan = 1) or device memory at `arena`; the offsets
+// locate its tables inside it:
+//   batches      DevBatch[]  (batch 0 is a sentinel)
+//   works        DevWork[]
+//   ptrs         void*[(buf_index * N + rank) * 2 + {0 send, 1 recv}]
+//   first_batch  uint32[64]  first batch of each channel id (0 = none)
+//   scalars      uint32[buf_index * N + rank]  PreMulSum scalar bits (bf16 in the low half)
+struct alignas(16) KernelArgs {
   const DevComm* comm;
-  const DevBatch* batches;
-  const DevWork* works;
-  void* const* ptrs;            // [(buf_index * N + rank) * 2 + {0 send, 1 recv}]
-  const uint32_t* first_batch;  // [64] first batch of each channel id (0 = none)
-  const uint32_t* wg_map;       // [grid] rank | n << 8 | lane << 16, or kIdleWg
-  uint64_t epoch;               // launch counter of the communicator, from 1
-  const uint32_t* scalars;      // PreMulSum: [buf_index * N + rank] scalar bits (bf16 in the low half)
+  const uint32_t* wg_map;  // [grid] rank | n << 8 | lane << 16, or kIdleWg
+  const uint8_t* arena;    // the plan in device memory when it is not inline
+  uint32_t off_batches, off_works, off_ptrs, off_first, off_scalars;
+  uint32_t inline_plan;
+  alignas(16) uint8_t plan[kInlinePlanBytes];
 };
+static_assert(sizeof(KernelArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 }  // namespace rar

@@ -16,6 +16,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <type_traits>
 
 #include "rar_device.h"
@@ -1080,7 +1081,16 @@ __device__ __forceinline__ void copy16(void* dst, const void* src, int bytes, in
 // Load batch `b` into LDS with one wave [C23 "前两个 Warp 与 Work Loader"]:
 // the k-th set bit of offset_bitset names the k-th work (found through an LDS
 // scratch table), then 64 lanes x 16 bytes move up to 16 works of 64 bytes.
-__device__ void load_batch(Shmem& sh, const KernelArgs& a, uint32_t b, int lid) {
+// The tables of a launch plan (see KernelArgs).
+struct Plan {
+  const DevBatch* batches;
+  const DevWork* works;
+  void* const* ptrs;
+  const uint32_t* first_batch;
+  const uint32_t* scalars;
+};
+
+__device__ void load_batch(Shmem& sh, const Plan& a, uint32_t b, int lid) {
   const DevBatch hdr = a.batches[b];
   const uint64_t bits = hdr.offset_bitset;
   if (lid == 0) {
@@ -1107,6 +1117,18 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[PROTO == kLL128 ? kMaxWaves * kLl128Unroll * 1024 : 16];
   const uint32_t m = args.wg_map[blockIdx.x];
   if (m == kIdleWg) return;
+  // An inline plan is read where the dispatch put it, in the kernel-argument
+  // segment (global memory), through that segment's base pointer.  Taking
+  // the address of the parameter itself would let the compiler hand out a
+  // private copy, which global loads cannot reach.
+  const uint8_t* kernargs = (const uint8_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  const uint8_t* plan_base = args.inline_plan ? kernargs + offsetof(KernelArgs, plan) : args.arena;
+  Plan plan;
+  plan.batches = reinterpret_cast<const DevBatch*>(plan_base + args.off_batches);
+  plan.works = reinterpret_cast<const DevWork*>(plan_base + args.off_works);
+  plan.ptrs = reinterpret_cast<void* const*>(plan_base + args.off_ptrs);
+  plan.first_batch = reinterpret_cast<const uint32_t*>(plan_base + args.off_first);
+  plan.scalars = reinterpret_cast<const uint32_t*>(plan_base + args.off_scalars);
   const int tid = threadIdx.x, nthreads = blockDim.x;
   const int wave = tid >> 6, lid = tid & 63, nwaves = nthreads >> 6;
   const int rank = (int)(m & 0xFFu), n = (int)((m >> 8) & 0xFFu), lane = (int)((m >> 16) & 0xFFu);
@@ -1125,12 +1147,12 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   if (sh.channel_id < 0) return;  // n beyond popcount(mask): not a channel of this launch
   // Staging [C23 "前两个 Warp 与 Work Loader"]: wave 0 copies the
   // communicator hot fields, another wave the channel's first work batch.
-  const uint32_t first = args.first_batch[sh.channel_id];
+  const uint32_t first = plan.first_batch[sh.channel_id];
   if (wave == 0) copy16(&sh.comm, &comm->hot, (int)sizeof(DevCommHot), lid);
   const int loader = nwaves > 1 ? 1 : 0;
   if (wave == loader) {
     if (first != 0) {
-      load_batch(sh, args, first, lid);
+      load_batch(sh, plan, first, lid);
     } else if (lid == 0) {
       sh.n_works = 0;
       sh.batch = DevBatch{0, 0, 0};
@@ -1140,7 +1162,7 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
 
   Ctx cx;
   cx.sh = &sh;
-  cx.ptrs = args.ptrs;
+  cx.ptrs = plan.ptrs;
   cx.tid = tid;
   cx.nthreads = nthreads;
   cx.workers = nthreads;
@@ -1182,7 +1204,7 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.timeout = sh.comm.spin_timeout_ticks;
   cx.drop_head = (sh.comm.debug_flags & 1) != 0;
   cx.ll_mask = sh.comm.ll_flag_mask;
-  cx.scalars = args.scalars;
+  cx.scalars = plan.scalars;
   cx.s_own = cx.s_prev = 0;
   cx.stage = stage;
   cx.aborted = false;
@@ -1194,11 +1216,14 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   // learn the XCD of the workgroup that receives from it.  Same XCD = same
   // L2 = the cheap publication path; anything else takes the agent-scope
   // release.  The dispatcher is not trusted: the check runs every launch.
+  // Launches are counted on the device (each workgroup's own slot holds its
+  // count), so a launch replayed from a captured graph counts as well.
   if (tid == 0) {
     const uint32_t my_xcc = xcc_id();
-    store_relaxed(&sh.comm.placement[blockIdx.x], (args.epoch << 8) | my_xcc);
+    const uint64_t epoch = (load_relaxed(&sh.comm.placement[blockIdx.x]) >> 8) + 1;
+    store_relaxed(&sh.comm.placement[blockIdx.x], (epoch << 8) | my_xcc);
     const uint32_t peer = sh.comm.wg_of[((int64_t)me.next * C + n) * cx.nlanes + lane];
-    const bool ok = wait_geq(&sh.comm.placement[peer], args.epoch << 8, cx);
+    const bool ok = wait_geq(&sh.comm.placement[peer], epoch << 8, cx);
     sh.abort = ok ? 0 : 1;
     sh.local_send = ok && (load_relaxed(&sh.comm.placement[peer]) & 0xFFu) == my_xcc;
   }
@@ -1223,7 +1248,7 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
     if (cx.aborted) break;
     b = sh.batch.next_jump;
     __syncthreads();
-    if (b != 0 && wave == loader) load_batch(sh, args, b, lid);
+    if (b != 0 && wave == loader) load_batch(sh, plan, b, lid);
     __syncthreads();
   }
   // LL and LL128 publish no tail while running; record the sender step.
