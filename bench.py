@@ -133,6 +133,9 @@ def main():
                     help="Simple direct variants: bit 0 write, bit 1 read")
     ap.add_argument("--deal-works", type=int, default=None, choices=[0, 1],
                     help="1: the lanes of a channel take its works in turn")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the K steps as one captured HIP graph (kernel durations still "
+                         "come from K eagerly launched steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the AllReduce, time a plain device copy of MIB MiB "
@@ -251,6 +254,33 @@ def main():
     # span over back-to-back launches (launch gaps included)
     t_step = statistics.mean(per) if len(xs) > 1 else span / args.steps
     t_kernel = statistics.mean(per)
+    if args.graph:
+        # the same K steps captured into one HIP graph and replayed: the
+        # host's per-launch cost leaves the timed region
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            hcap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for _ in range(args.steps):
+                if len(xs) == 1:
+                    comm_lib.check(lib.rar_allreduce(comm.handle, sarr, rarr, w.counts[0], dcode,
+                                                     comm_lib.SUM, hcap))
+                else:
+                    comm_lib.check(lib.rar_group_start(comm.handle))
+                    for s_, r_ in zip(sends, recvs):
+                        comm.allreduce(s_, r_)
+                    comm_lib.check(lib.rar_group_end(comm.handle, hcap))
+        graph.replay()  # warm
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        g0.record()
+        graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if comm.async_error() != 0:
+            raise RuntimeError("the wait watchdog fired during the graph replay")
+        t_step = g0.elapsed_time(g1) * 1e-3 / args.steps
     # the N receive buffers must agree (a property of the method, not an oracle)
     for s in recvs:
         ref = s[0]
@@ -286,7 +316,8 @@ def main():
             "elems_per_rank": sum(w.counts), "collectives_per_step": len(w.counts),
             "lanes_per_channel": shape["lanes"], "waves_per_lane": shape["waves"],
             "grid": shape["grid"], "parallelism": f"{N} virtual ranks on 1 GPU",
-            "launch": "plain" if tune.get("launch_mode", 0) == 1 else "cooperative",
+            "launch": ("hip graph of plain launches" if args.graph else "plain")
+            if tune.get("launch_mode", 0) == 1 else "cooperative",
             "misalign_elems": args.misalign,
             "direct": int(tune.get("direct", 0)),
         },
