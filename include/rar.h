@@ -231,13 +231,20 @@ rar_result_t rar_allreduce_premul(rar_comm_t comm, const void* const* sendbufs,
 rar_result_t rar_group_start(rar_comm_t comm);
 rar_result_t rar_group_end(rar_comm_t comm, void* stream);
 
-/* Destroy after the stream has passed the last call.  NULL is a no-op. */
+/* Destroy after the stream has passed the last call, and after every HIP
+ * graph that captured a launch on this communicator has been destroyed or
+ * will not be replayed again (a replay would use freed memory).  NULL is a
+ * no-op. */
 rar_result_t rar_comm_destroy(rar_comm_t comm);
 
 /* One-shot form of the pages' problem statement: creates (and caches, keyed
  * by every argument that shapes the FIFOs) a communicator on first use, then
- * runs rar_allreduce.  The mask is the nchannels lowest bits.  Errors as for
- * rar_comm_create and rar_allreduce. */
+ * runs rar_allreduce.  The mask is the nchannels lowest bits.  Creation
+ * allocates and initialises device memory, which a stream capture does not
+ * allow: make the first call with a given shape outside any capture.  The
+ * cached communicators use the cooperative launch, so under capture this
+ * entry point fails with RAR_UNSUPPORTED.  Errors as for rar_comm_create and
+ * rar_allreduce. */
 rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks,
                             size_t count, rar_dtype_t dtype, rar_redop_t op,
                             const int* ring_order, rar_proto_t proto, int nchannels,

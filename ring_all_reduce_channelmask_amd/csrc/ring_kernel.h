@@ -708,8 +708,19 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
         if constexpr (OP == kOpRecvReduceCopySend && Ty::kPost) v = post8<Ty>(v, cx.nranks);
         if (O::kDst) store_bytes8<S>(db + 8 * j, v, nbytes - 8 * j);
         if (O::kSend) {
-          store_relaxed(sl + 2 * j, (v & 0xffffffffull) | ((uint64_t)sflag << 32));
-          store_relaxed(sl + 2 * j + 1, (v >> 32) | ((uint64_t)sflag << 32));
+          // to a receiver on this XCD at workgroup scope: the half-lines merge
+          // in the shared L2 instead of each being written through as an
+          // 8-byte partial write (measured at 64 MiB over 12 channels: 1100
+          // -> 643 us; no change at 512 KiB, which is latency-bound)
+          const uint64_t h0 = (v & 0xffffffffull) | ((uint64_t)sflag << 32);
+          const uint64_t h1 = (v >> 32) | ((uint64_t)sflag << 32);
+          if (cx.local_send) {
+            store_relaxed_xcd(sl + 2 * j, h0);
+            store_relaxed_xcd(sl + 2 * j + 1, h1);
+          } else {
+            store_relaxed(sl + 2 * j, h0);
+            store_relaxed(sl + 2 * j + 1, h1);
+          }
         }
       }
     }

@@ -2,7 +2,7 @@
 benchmark.  This module holds no arithmetic of the method: it only draws
 numbers.  Both the HIP path and the oracle receive the same arrays from here.
 
-The five workloads mirror the sizes the NCCL course pages measure (4 KiB,
+The workloads mirror the sizes the NCCL course pages measure (4 KiB,
 512 KiB and 64 MiB messages over 4 ranks, 1/4/12 channels, all three
 protocols), plus an 8-rank bf16/int32 case and a fused group of small
 collectives over a sparse channel mask.  Raw representations: float32 and
@@ -62,6 +62,9 @@ WORKLOADS = {
     "int32_n8": Workload("int32_n8", 8, (0, 3, 1, 6, 2, 7, 5, 4), 0xFFFF, "SIMPLE", "int32",
                          (32 * MiB,), 4 * MiB, 4, "int27", (4,),
                          "8 ranks, 16 channels, Simple, int32, 128 MiB/rank"),
+    "ll_64m": Workload("ll_64m", 4, (0, 2, 3, 1), 0xFFF, "LL", "float32", (16 * MiB,),
+                       512 * KiB, 4, "uniform", (3,),
+                       "4 ranks, 12 channels, LL, fp32, 64 MiB/rank"),
     "fused_ll": Workload("fused_ll", 4, (0, 1, 2, 3), 0b101101010011, "LL", "bfloat16",
                          (7168,) * 104, 512 * KiB, 4, "normal_half", (5,),
                          "104 fused bf16 AllReduces of 7168 elements, sparse mask, LL"),

@@ -31,15 +31,13 @@ def _fill(tensors, x, dtype):
         t.copy_(to_device(row, dtype))
 
 
-@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128"])
-@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
-def test_captured_allreduce_replays_match_oracle(proto, dtype):
+def _captured_replays(proto, dtype, **shape):
     import torch
     import ring_all_reduce_channelmask_amd as rar
     order, mask, buff = [0, 2, 3, 1], 0b1011, BUFF[proto]
     cs = 4 if proto == "SIMPLE" else 0
     comm = rar.Comm(4, order, mask, proto=proto, buff_size=buff, chunk_steps=cs, lanes=2,
-                    waves=2, launch_mode=1)
+                    waves=2, launch_mode=1, **shape)
     counts = [30011, 777]  # one collective, then a group of two
     sends = [[torch.empty(c, dtype=getattr(torch, dtype), device="cuda") for _ in range(4)]
              for c in counts]
@@ -83,6 +81,21 @@ def test_captured_allreduce_replays_match_oracle(proto, dtype):
         for r in range(4):
             assert_bits_equal(to_host(extra_out[r], dtype), want, f"eager after replay {rep}")
     comm.close()
+
+
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128"])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_captured_allreduce_replays_match_oracle(proto, dtype):
+    _captured_replays(proto, dtype)
+
+
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL128"])
+@pytest.mark.parametrize("shape", [dict(placement=1), dict(deal_works=1)],
+                         ids=["spread", "dealt"])
+def test_captured_replays_spread_and_dealt(proto, shape):
+    """The same with every rank of a pipeline on another XCD (the launch count
+    decides the placement each replay), and with works dealt to lanes."""
+    _captured_replays(proto, "float32", **shape)
 
 
 def test_capture_rejects_what_cannot_replay():
