@@ -2,8 +2,9 @@
 //
 // A communicator owns, on one HIP device: the FIFOs of every (rank, channel),
 // the head/tail counters of every connector lane, the abort words, the
-// workgroup map, and a small arena into which each launch's work batches,
-// works and buffer pointers are copied before the kernel runs.
+// workgroup map and placement table, and an arena for launch plans too large
+// to travel inside the kernel arguments (work batches, works, buffer
+// pointers, scalars).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
