@@ -171,3 +171,28 @@ def test_oneshot_validates_on_the_host():
     t = _lib.OneshotTuning(0, 0, 0, 0)
     assert lib.rar_oneshot_allreduce_premul(s, r, 2, 16, _lib.DTYPE["float32"], None,
                                             ctypes.byref(t), None) == _lib.INVALID_ARGUMENT
+
+
+def test_planner_matches_oracle_split_random():
+    """The host planner and the oracle's geometry agree on random launches:
+    any ring size, sparse or dense masks, every protocol and dtype, buffer
+    sizes on each protocol's quantum, and groups of ragged counts (zeros
+    included)."""
+    from hypothesis import given, settings, strategies as st
+
+    quantum = {"SIMPLE": 512, "LL": 256, "LL128": 2048}
+
+    @settings(max_examples=300, deadline=None, derandomize=True)
+    @given(N=st.integers(2, 64), mask=st.integers(1, 2 ** 64 - 1),
+           proto=st.sampled_from(["SIMPLE", "LL", "LL128"]),
+           units=st.integers(1, 64), cs=st.sampled_from([2, 4]),
+           dt=st.sampled_from(["int32", "float32", "bfloat16"]),
+           counts=st.lists(st.integers(0, 300000), min_size=1, max_size=40))
+    def check(N, mask, proto, units, cs, dt, counts):
+        buff = 8 * quantum[proto] * units
+        ours, cmax = rar.plan_pieces(N, mask, proto, buff, cs, dt, counts)
+        theirs, ocmax = oracle.geometry(N, mask, proto, buff, cs, dt, counts)
+        assert cmax == ocmax
+        assert ours == theirs
+
+    check()
