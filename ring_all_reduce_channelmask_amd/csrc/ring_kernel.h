@@ -754,10 +754,11 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
 // 128-byte line = 16 words: words 0..14 payload, word 15 = step+1 [C23
 // "LL128：15/16 Payload"].  A wave covers 8 lines per pass, 8 lanes per line,
 // 16 bytes per lane; lane 7 of each line holds word 14 and the flag word.
-// Sender: data words of all its lines, a drain (plus an L2 write-back when the
-// receiver is on another XCD), then the flag words.  Receiver: the flag lanes
-// poll every line of the wave, the wave votes until none is missing, then one
-// acquire fence precedes the data loads.
+// Sender: every wave stores the data words of its lines, drains (plus an L2
+// write-back when the receiver is on another XCD), then stores the flag words
+// (at workgroup scope to a receiver on this XCD).  Receiver: wave 0 polls the
+// flag word of every line of the workgroup's share, voting until none is
+// missing, issues one acquire, and a barrier lets every wave load its lines.
 #ifndef RAR_LL128_UNROLL
 #define RAR_LL128_UNROLL 2
 #endif
