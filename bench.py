@@ -12,6 +12,7 @@ course pages, the ring's algorithmic HBM bytes over the kernel's duration as a
 fraction of MI355X peak HBM bandwidth, and the CPU oracle timed on this host.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -45,6 +46,43 @@ ONESHOT_TUNING = {
 CSRC = os.path.join(ROOT, "ring_all_reduce_channelmask_amd", "csrc")
 KERNEL_SRC = {"ring": os.path.join(CSRC, "ring_kernel.h"),
               "oneshot": os.path.join(CSRC, "oneshot_kernel.hip")}
+
+
+class HipEvent:
+    """A timing event recorded straight through the HIP runtime torch has
+    loaded: recording costs about a microsecond of host time, against several
+    for torch.cuda.Event, so per-launch events do not slow the launch loop of
+    short kernels."""
+    _hip = None
+
+    def __init__(self):
+        if HipEvent._hip is None:
+            import torch  # noqa: F401  -- the runtime below is torch's
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._hip = hip
+        self._e = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreate(ctypes.byref(self._e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+
+    def record(self, stream_handle):
+        if HipEvent._hip.hipEventRecord(self._e, stream_handle) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both completed)."""
+        ms = ctypes.c_float()
+        if HipEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self._e, end._e) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self._e:
+            HipEvent._hip.hipEventDestroy(self._e)
 
 
 def kernel_fingerprint(algo="ring") -> str:
@@ -223,7 +261,7 @@ def main():
         # bracket the launch only, so host-side queueing is not timed as GPU work.
         if len(xs) == 1:
             if a is not None:
-                a.record(stream)
+                a.record(hstream)
             comm_lib.check(lib.rar_allreduce(comm.handle, sarr, rarr, w.counts[0], dcode,
                                              comm_lib.SUM, hstream))
         else:
@@ -231,16 +269,15 @@ def main():
             for s, r in zip(sends, recvs):
                 comm.allreduce(s, r)
             if a is not None:
-                a.record(stream)
-            comm_lib.check(comm_lib.load().rar_group_end(comm.handle, ctypes.c_void_p(stream.cuda_stream)))
+                a.record(hstream)
+            comm_lib.check(comm_lib.load().rar_group_end(comm.handle, hstream))
         if b is not None:
-            b.record(stream)
+            b.record(hstream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    ev = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for a, b in ev:
@@ -398,14 +435,13 @@ def run_oneshot(args, w):
     ctune = comm_lib.OneshotTuning(tune.get("workgroups", 0), tune.get("waves", 0),
                                    tune.get("unroll", 0), 0)
     dcode = comm_lib.DTYPE[w.dtype]
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    ev = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for a, b in ev:
-        a.record(stream)
+        a.record(hstream)
         comm_lib.check(lib.rar_oneshot_allreduce(sarr, rarr, N, w.counts[0], dcode, comm_lib.SUM,
                                                  ctypes.byref(ctune), hstream))
-        b.record(stream)
+        b.record(hstream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) * 1e-3 for a, b in ev]
