@@ -513,3 +513,30 @@ def test_dealt_works_with_direct_ops_and_in_place(placement):
             for r in range(4):
                 assert_bits_equal(got[i][r], want[i], f"max direct {direct} work {i} rank {r}")
         comm.close()
+
+
+# ------------------------------------------------- the maxima
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128"])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+def test_maximum_ranks_and_channels(proto, dtype):
+    """64 ranks on a random ring over the first and last channel ids, and 2
+    ranks over all 64 channels, in a ragged group; bit for bit with the
+    closed form (int32 also with the plain wrapped sum)."""
+    buff = SMALL_BUFF[proto]
+    cs = 4 if proto == "SIMPLE" else 0
+    rng = np.random.default_rng(64)
+    order = [int(v) for v in rng.permutation(64)]
+    for N, ring, mask, counts in ((64, order, (1 << 63) | 1, [1, 5003, 64 * 37 + 3]),
+                                  (2, [1, 0], (1 << 64) - 1, [100003, 7])):
+        comm = _comm(nranks=N, ring_order=ring, mask=mask, proto=proto, buff_size=buff,
+                     chunk_steps=cs, lanes=1, waves=2)
+        xs = [_rand(dtype, (N, c), 640 + c) for c in counts]
+        got = run_hip(comm, xs, dtype)
+        comm.close()
+        want = cf.allreduce(xs, ring, mask, proto, buff, 4, dtype)
+        for i, x in enumerate(xs):
+            if dtype == "int32":
+                s = (x.astype(np.int64).sum(axis=0) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+                np.testing.assert_array_equal(want[i], s)
+            for r in range(N):
+                assert_bits_equal(got[i][r], want[i], f"N {N} work {i} rank {r}")
