@@ -217,6 +217,39 @@ def test_dropped_head_credit_stalls_after_nccl_steps_and_watchdog_ends_it():
     fresh.close()
 
 
+@pytest.mark.parametrize("proto", ["LL", "LL128"])
+def test_dropped_head_stalls_ll_protocols_after_nccl_steps(proto):
+    """The same fault in the flag protocols: with receivers never handing
+    slots back, every workgroup completes exactly NCCL_STEPS sending units
+    (the timeline records one per completed unit; the loop's final receive
+    sends nothing) and then waits for credit that never comes; the bounded
+    waits end the launch with RAR_ABORTED."""
+    import ring_all_reduce_channelmask_amd as rar
+    import torch
+    from ring_all_reduce_channelmask_amd import _lib
+    from .gpu_util import to_device
+    comm = _comm(nranks=4, ring_order=[0, 2, 3, 1], mask=0x3, proto=proto,
+                 buff_size=SMALL_BUFF[proto], lanes=2, waves=2, timeout_us=2000,
+                 debug_flags=_lib.DEBUG_DROP_RECV_HEAD | _lib.DEBUG_TRACE)
+    x = _rand("float32", (4, 1 << 16), 14)
+    sends = [to_device(x[r], "float32") for r in range(4)]
+    recvs = [torch.empty_like(s) for s in sends]
+    comm.allreduce(sends, recvs)
+    torch.cuda.synchronize()
+    assert comm.async_error() == _lib.ABORTED
+    sending = {}
+    for rec in comm.read_trace():
+        key = (rec["rank"], rec["channel_id"], rec["lane"])
+        sending[key] = sending.get(key, 0) + (rec["op"] != 4)  # 4 = recv
+    assert len(sending) == 4 * 2 * 2
+    assert set(sending.values()) == {8}
+    assert set(comm.query_state()[1::2]) == {0}
+    with pytest.raises(rar.RarError) as e:
+        comm.allreduce(sends, recvs)
+    assert e.value.code == _lib.ABORTED
+    comm.close()
+
+
 # ------------------------------------------------------------- full sizes
 def _bench_tuning():
     import bench  # the launch shapes bench.py times
