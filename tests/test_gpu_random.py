@@ -1,0 +1,75 @@
+"""Randomized parity of the HIP path with the oracle's closed form.
+
+Derandomized hypothesis draws (the same cases every run): ring size and
+order (one ring or one per channel), channel mask, protocol, payload type,
+operator, ragged groups, in place or not, lanes and waves, dealt works, the
+Simple direct variants and placement.  Every result must match bit for bit."""
+import numpy as np
+import pytest
+
+from oracle import closed_form as cf
+from ring_all_reduce_channelmask_amd import workloads as wl
+
+from .gpu_util import assert_bits_equal, run_hip
+
+pytestmark = pytest.mark.gpu
+
+QUANTUM = {"SIMPLE": 512, "LL": 256, "LL128": 2048}
+
+
+def _draw(rng, dtype, shape):
+    if dtype == "int32":
+        return rng.integers(-2 ** 31, 2 ** 31, size=shape).astype(np.int32)
+    v = rng.standard_normal(shape).astype(np.float32)
+    return v if dtype == "float32" else wl._bf16_bits(v.ravel()).reshape(shape)
+
+
+def test_random_launches_match_closed_form():
+    from hypothesis import HealthCheck, assume, given, settings, strategies as st
+    import ring_all_reduce_channelmask_amd as rar
+    from ring_all_reduce_channelmask_amd import _lib
+
+    ran = []
+
+    @settings(max_examples=300, deadline=None, derandomize=True,
+              suppress_health_check=list(HealthCheck))
+    @given(N=st.integers(2, 16), seed=st.integers(0, 2 ** 32 - 1),
+           nbits=st.integers(1, 6), proto=st.sampled_from(["SIMPLE", "LL", "LL128"]),
+           units=st.integers(1, 6), dtype=st.sampled_from(["int32", "float32", "bfloat16"]),
+           op=st.sampled_from(["sum", "prod", "max", "min", "avg"]),
+           counts=st.lists(st.integers(0, 100000), min_size=1, max_size=5),
+           nrings=st.integers(1, 3), in_place=st.booleans(), lanes=st.integers(1, 4),
+           waves=st.integers(1, 8), deal=st.booleans(), direct=st.integers(0, 3),
+           placement=st.integers(0, 1))
+    def check(N, seed, nbits, proto, units, dtype, op, counts, nrings, in_place, lanes, waves,
+              deal, direct, placement):
+        rng = np.random.default_rng(seed)
+        rings = [[int(v) for v in rng.permutation(N)] for _ in range(nrings)]
+        ids = rng.choice(64, size=nbits, replace=False)
+        mask = int(sum(1 << int(i) for i in ids))
+        buff = 8 * QUANTUM[proto] * units
+        cs = 4 if proto == "SIMPLE" else 0
+        if proto != "SIMPLE":
+            direct = 0
+        order = rings if nrings > 1 else rings[0]
+        try:
+            comm = rar.Comm(N, order, mask, proto=proto, buff_size=buff, chunk_steps=cs,
+                            lanes=lanes, waves=waves, deal_works=int(deal), direct=direct,
+                            placement=placement, launch_mode=1)
+        except rar.RarError as e:
+            assume(e.code != _lib.UNSUPPORTED)  # a grid that cannot be co-resident
+            raise
+        try:
+            xs = [_draw(rng, dtype, (N, c)) for c in counts]
+            got = run_hip(comm, xs, dtype, in_place=in_place, op=op)
+        finally:
+            comm.close()
+        want = cf.allreduce(xs, order, mask, proto, buff, 4, dtype, op=op)
+        for w in range(len(xs)):
+            for r in range(N):
+                assert_bits_equal(got[w][r], want[w], f"work {w} rank {r}")
+        ran.append((N, proto, dtype, op, len(counts)))
+
+    check()
+    print(f"{len(ran)} random launches checked", flush=True)
+    assert len(ran) >= 150, "too few launches ran"
