@@ -17,9 +17,10 @@ def to_host(t, dtype):
     return t.cpu().numpy()
 
 
-def run_hip(comm, inputs, dtype, in_place=False, op="sum"):
-    """inputs: list over collectives of [N, count] arrays.  Returns a list of
-    [N, count] arrays (what every rank's receive buffer holds)."""
+def run_hip(comm, inputs, dtype, in_place=False, op="sum", scalars=None):
+    """inputs: list over collectives of [N, count] arrays; ``scalars``: for
+    premulsum, one array of N payload elements per collective.  Returns a
+    list of [N, count] arrays (what every rank's receive buffer holds)."""
     import torch
     N = comm.nranks
     sends, recvs = [], []
@@ -29,12 +30,13 @@ def run_hip(comm, inputs, dtype, in_place=False, op="sum"):
                                  for t in s]
         sends.append(s)
         recvs.append(r_)
+    sc = scalars if scalars is not None else [None] * len(inputs)
     if len(inputs) == 1:
-        comm.allreduce(sends[0], recvs[0], op=op)
+        comm.allreduce(sends[0], recvs[0], op=op, scalars=sc[0])
     else:
         with comm.group():
-            for s, r_ in zip(sends, recvs):
-                comm.allreduce(s, r_, op=op)
+            for s, r_, k in zip(sends, recvs, sc):
+                comm.allreduce(s, r_, op=op, scalars=k)
     torch.cuda.synchronize()
     assert comm.async_error() == 0, "watchdog fired"
     return [np.stack([to_host(t, dtype) for t in r_]) for r_ in recvs]

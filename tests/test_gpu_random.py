@@ -36,7 +36,7 @@ def test_random_launches_match_closed_form():
     @given(N=st.integers(2, 16), seed=st.integers(0, 2 ** 32 - 1),
            nbits=st.integers(1, 6), proto=st.sampled_from(["SIMPLE", "LL", "LL128"]),
            units=st.integers(1, 6), dtype=st.sampled_from(["int32", "float32", "bfloat16"]),
-           op=st.sampled_from(["sum", "prod", "max", "min", "avg"]),
+           op=st.sampled_from(["sum", "prod", "max", "min", "avg", "premulsum"]),
            counts=st.lists(st.integers(0, 100000), min_size=1, max_size=5),
            nrings=st.integers(1, 3), in_place=st.booleans(), lanes=st.integers(1, 4),
            waves=st.integers(1, 8), deal=st.booleans(), direct=st.integers(0, 3),
@@ -61,10 +61,12 @@ def test_random_launches_match_closed_form():
             raise
         try:
             xs = [_draw(rng, dtype, (N, c)) for c in counts]
-            got = run_hip(comm, xs, dtype, in_place=in_place, op=op)
+            scs = [_draw(rng, dtype, (N,)) for _ in counts] if op == "premulsum" else None
+            got = run_hip(comm, xs, dtype, in_place=in_place, op=op, scalars=scs)
         finally:
             comm.close()
-        want = cf.allreduce(xs, order, mask, proto, buff, 4, dtype, op=op)
+        want = cf.allreduce(xs, order, mask, proto, buff, 4, dtype, op=op,
+                            scalars=None if scs is None else np.stack(scs))
         for w in range(len(xs)):
             for r in range(N):
                 assert_bits_equal(got[w][r], want[w], f"work {w} rank {r}")
