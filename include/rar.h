@@ -149,7 +149,8 @@ typedef struct {
 
 /* Create a communicator: the ring, the active channels, the protocol and the
  * FIFOs for every (rank, channel).  Allocates N * popcount(mask) * buffSize
- * bytes of FIFO plus counters on the current HIP device and zeroes them.
+ * bytes of FIFO (rounded up per lane; lanes_per_channel times that with
+ * deal_works) plus counters on the current HIP device and zeroes them.
  *
  *   nranks       2..64 virtual ranks
  *   ring_order   [nranks] user ranks listed along `next`; must be a
