@@ -70,6 +70,9 @@ PLAN_CASES = [
     (4, 0b101101010011, "LL", 512 * 1024, 4, "bfloat16", [7168] * 104),
     (3, 0x5, "LL128", 8 * 2048, 4, "int32", [1, 0, 77, 4099, 3]),
     (2, 1 << 63, "SIMPLE", 8 * 512, 2, "float32", [0, 5]),
+    # element, channel and byte offsets beyond 2^31 and 2^32
+    (4, (1 << 64) - 1, "SIMPLE", 4 << 20, 4, "int32", [(1 << 31) + 5, 3, (1 << 33) + 17]),
+    (3, 0xF0F, "LL128", 4915200, 4, "bfloat16", [(1 << 32) + 9, 0, 1 << 31]),
 ]
 
 

@@ -573,3 +573,38 @@ def test_maximum_ranks_and_channels(proto, dtype):
                 np.testing.assert_array_equal(want[i], s)
             for r in range(N):
                 assert_bits_equal(got[i][r], want[i], f"N {N} work {i} rank {r}")
+
+
+
+@pytest.mark.parametrize("proto", ["SIMPLE", "LL", "LL128", "oneshot"])
+def test_more_than_2g_elements(proto):
+    """A collective of 2^31 + 5 int32 elements (8 GiB per buffer) over 64
+    channels, so element offsets, channel offsets and byte offsets all pass
+    2^31.  int32 sums wrap, so the result does not depend on the fold order:
+    every element is checked on the device against the plain wrapped sum."""
+    import torch
+    count, block = (1 << 31) + 5, 1 << 27
+    sends = [torch.empty(count, dtype=torch.int32, device="cuda") for _ in range(2)]
+    want = torch.empty(count, dtype=torch.int32, device="cuda")
+    for lo in range(0, count, block):
+        i = torch.arange(lo, min(lo + block, count), dtype=torch.int64, device="cuda")
+        x0 = (i * 2654435761 + 12345) & 0xFFFFFFFF
+        x1 = (i * 40503 + 977) & 0xFFFFFFFF
+        wrap = lambda v: torch.where(v >= 1 << 31, v - (1 << 32), v).to(torch.int32)
+        sends[0][lo:lo + i.numel()] = wrap(x0)
+        sends[1][lo:lo + i.numel()] = wrap(x1)
+        want[lo:lo + i.numel()] = wrap((x0 + x1) & 0xFFFFFFFF)
+    del i, x0, x1
+    recvs = [torch.empty_like(s) for s in sends]
+    if proto == "oneshot":
+        import ring_all_reduce_channelmask_amd as rar
+        rar.oneshot_allreduce(sends, recvs)
+        torch.cuda.synchronize()
+    else:
+        comm = _comm(nranks=2, ring_order=[1, 0], mask=(1 << 64) - 1, proto=proto, launch_mode=1)
+        comm.allreduce(sends, recvs)
+        torch.cuda.synchronize()
+        assert comm.async_error() == 0
+        comm.close()
+    for r in range(2):
+        assert torch.equal(recvs[r], want), f"rank {r}"
