@@ -549,6 +549,25 @@ def test_algorithmic_bytes():
                                          direct_read=True) == (5 * N - 6) * M
 
 
+
+@pytest.mark.parametrize("proto,chunk_elems", [("SIMPLE", 1024), ("LL", 64), ("LL128", 480)])
+@pytest.mark.parametrize("N", [2, 3, 4, 8])
+def test_algorithmic_bytes_match_simulated_traffic(proto, chunk_elems, N):
+    """The roofline's algorithmic bytes equal the traffic the simulator
+    counts: every FIFO byte is written once and read once (2 x the wire bytes
+    all ranks send) and every rank reads its input and writes its output once
+    (2 N M).  Counts are whole loops of full chunks, so LL and LL128 lines are
+    full and the wire/payload ratios exact (2 and 16/15)."""
+    count = 2 * N * chunk_elems
+    M = count * 4
+    x = np.ones((N, count), dtype=np.float32)
+    rc, _, st, _ = oracle.allreduce([x], list(range(N)), 0x1, proto, SMALL_BUFF[proto], 4,
+                                    "float32")
+    assert rc == oracle.OK
+    wire = sum(st.wire_sent[r] for r in range(N))
+    counted = 2 * wire + 2 * N * M
+    assert abs(metrics.algorithmic_bytes(M, N, proto) - counted) <= 1e-9 * counted
+
 # ------------------------------------------------------------- direct variant
 @pytest.mark.parametrize("N", [2, 3, 4, 8])
 def test_direct_variant_same_result_and_completes(N):
