@@ -35,7 +35,7 @@ TUNING = {
     "ll_512k": dict(lanes=16, waves=2, launch_mode=1),
     "ll_64m": dict(lanes=8, waves=4, launch_mode=1),
     "fused_ll": dict(lanes=16, waves=4, launch_mode=1, deal_works=1),
-    "simple_4k": dict(lanes=1, waves=4, launch_mode=1),
+    "simple_4k": dict(lanes=1, waves=2, launch_mode=1, slices_per_chunk=1),
 }
 # Launch shape of the one-shot kernel per workload (performance only).
 ONESHOT_TUNING = {

@@ -95,7 +95,7 @@ struct rar_comm {
   int debug_flags = 0;
   rar::TraceRec* d_trace = nullptr;
   uint64_t* d_placement = nullptr;
-  uint32_t* d_wg_of = nullptr;
+  uint32_t* d_wg_peer = nullptr;
   uint32_t* d_trace_count = nullptr;
   uint8_t* d_arena = nullptr;
   size_t arena_cap = 0;
@@ -118,7 +118,7 @@ void release(rar_comm* c) {
   (void)hipFree(c->d_arena);
   (void)hipFree(c->d_trace);
   (void)hipFree(c->d_placement);
-  (void)hipFree(c->d_wg_of);
+  (void)hipFree(c->d_wg_peer);
   (void)hipFree(c->d_trace_count);
   (void)hipFree(c->d_wgmap);
   (void)hipFree(c->d_abort);
@@ -424,17 +424,32 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
   if ((r = guard(hipMalloc(&c->d_abort, 256), "hipMalloc(abort)"))) return r;
   if ((r = guard(hipMalloc(&c->d_wgmap, wg.size() * sizeof(uint32_t)), "hipMalloc(wgmap)"))) return r;
   if ((r = guard(hipMalloc(&c->d_comm, sizeof(rar::DevComm)), "hipMalloc(comm)"))) return r;
+  // wg_peer[g]: the workgroup that receives from workgroup g (same dense
+  // channel and lane, the next rank on that channel's ring)
   std::vector<uint32_t> wg_of((size_t)nranks * c->C * c->P, 0);
   for (size_t g = 0; g < wg.size(); ++g)
     if (wg[g] != rar::kIdleWg) {
       const uint32_t m = wg[g];
       wg_of[((size_t)(m & 0xFF) * c->C + ((m >> 8) & 0xFF)) * c->P + ((m >> 16) & 0xFF)] = (uint32_t)g;
     }
+  std::vector<int> channel_ids;
+  for (int id = 0; id < rar::kMaxChannels; ++id)
+    if ((channel_mask >> id) & 1) channel_ids.push_back(id);
+  std::vector<uint32_t> wg_peer(wg.size(), 0);
+  for (size_t g = 0; g < wg.size(); ++g) {
+    wg_peer[g] = (uint32_t)g;
+    if (wg[g] == rar::kIdleWg) continue;
+    const uint32_t m = wg[g];
+    const int rank = (int)(m & 0xFF), n = (int)((m >> 8) & 0xFF), lane = (int)((m >> 16) & 0xFF);
+    const int next = rings[channel_ids[n] % nrings].next[rank];
+    wg_peer[g] = wg_of[((size_t)next * c->C + n) * c->P + lane];
+  }
   if ((r = guard(hipMalloc(&c->d_placement, wg.size() * sizeof(uint64_t)), "hipMalloc(placement)"))) return r;
   if ((r = guard(hipMemset(c->d_placement, 0, wg.size() * sizeof(uint64_t)), "hipMemset(placement)"))) return r;
-  if ((r = guard(hipMalloc(&c->d_wg_of, wg_of.size() * sizeof(uint32_t)), "hipMalloc(wg_of)"))) return r;
-  if ((r = guard(hipMemcpy(c->d_wg_of, wg_of.data(), wg_of.size() * sizeof(uint32_t), hipMemcpyHostToDevice),
-                 "hipMemcpy(wg_of)")))
+  if ((r = guard(hipMalloc(&c->d_wg_peer, wg_peer.size() * sizeof(uint32_t)), "hipMalloc(wg_peer)"))) return r;
+  if ((r = guard(hipMemcpy(c->d_wg_peer, wg_peer.data(), wg_peer.size() * sizeof(uint32_t),
+                           hipMemcpyHostToDevice),
+                 "hipMemcpy(wg_peer)")))
     return r;
   constexpr int kTraceCap = 4096;
   if (tune.debug_flags & 2) {
@@ -490,7 +505,7 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
   hc.hot.trace = c->d_trace;
   hc.hot.trace_count = c->d_trace_count;
   hc.hot.placement = c->d_placement;
-  hc.hot.wg_of = c->d_wg_of;
+  hc.hot.wg_peer = c->d_wg_peer;
   hc.hot.ll_flag_mask = (tune.debug_flags & RAR_DEBUG_LL_FLAG_WRAP8) ? 0xFFu : 0xFFFFFFFFu;
   for (int id = 0; id < rar::kMaxChannels; ++id) {
     if (!((channel_mask >> id) & 1)) continue;

@@ -116,7 +116,7 @@ struct alignas(16) DevCommHot {
   TraceRec* trace;             // [grid][trace_cap]
   uint32_t* trace_count;       // [grid] records written by the last launch
   uint64_t* placement;         // [grid] launch count << 8 | XCC id, written at kernel entry
-  const uint32_t* wg_of;       // [(r * C + n) * P + p] -> workgroup index in the grid
+  const uint32_t* wg_peer;     // [grid] -> workgroup that receives from this one
   uint32_t ll_flag_mask;       // LL flag period - 1 (0xFFFFFFFF, or 0xFF in the wrap test mode)
   int32_t deal_works;          // 1: work k of a channel runs whole on lane k mod n_lanes
 };

@@ -214,6 +214,8 @@ struct alignas(16) Shmem {
   int32_t n_works;
   int32_t abort;
   int32_t local_send;
+  uint32_t first_batch;  // the channel's first work batch
+  DevRank me;            // this rank's place on the channel's ring
 };
 
 // Per-thread view of the workgroup's channel (values are uniform).
@@ -1142,7 +1144,13 @@ template <class Ty, int PROTO>
 __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   __shared__ Shmem sh;
   __shared__ __attribute__((aligned(16))) uint8_t stage[PROTO == kLL128 ? kMaxWaves * kLl128Unroll * 1024 : 16];
+  const DevComm* comm = args.comm;
+  // Startup is a chain of dependent loads, so the independent ones go out
+  // together: the workgroup map and the channel mask here, the ring position,
+  // step counters, channel batch and placement check below, between the same
+  // two barriers.
   const uint32_t m = args.wg_map[blockIdx.x];
+  const uint64_t mask = comm->hot.channel_mask;
   if (m == kIdleWg) return;
   // An inline plan is read where the dispatch put it, in the kernel-argument
   // segment (global memory), through that segment's base pointer.  Taking
@@ -1159,22 +1167,44 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   const int tid = threadIdx.x, nthreads = blockDim.x;
   const int wave = tid >> 6, lid = tid & 63, nwaves = nthreads >> 6;
   const int rank = (int)(m & 0xFFu), n = (int)((m >> 8) & 0xFFu), lane = (int)((m >> 16) & 0xFFu);
-  const DevComm* comm = args.comm;
+  // Placement handshake, first half: one lane publishes this workgroup's XCD
+  // with its launch count (each workgroup's own slot holds the count, so a
+  // launch replayed from a captured graph counts as well).  The second half,
+  // below, reads what the receiving workgroup published; both publish at
+  // entry, so that read rarely has to wait.
+  const int hs_wave = nwaves - 1;
+  const bool hs_lane = wave == hs_wave && lid == 0;
+  uint64_t epoch = 0;
+  uint32_t my_xcc = 0, peer_wg = 0;
+  if (hs_lane) {
+    uint64_t* slot = &comm->hot.placement[blockIdx.x];
+    peer_wg = comm->hot.wg_peer[blockIdx.x];
+    my_xcc = xcc_id();
+    epoch = (load_relaxed(slot) >> 8) + 1;
+    store_relaxed(slot, (epoch << 8) | my_xcc);
+  }
   // Block -> channel [C23 "Kernel 如何把 Block 映射到 Channel"]: the lanes of
   // wave 0 scan the 64 mask bits; the dense index n picks the n-th set bit.
   if (wave == 0) {
     if (lid == 0) {
       sh.channel_id = -1;
       sh.abort = 0;
+      sh.local_send = 0;
     }
-    const uint64_t mask = comm->hot.channel_mask;
-    if (((mask >> lid) & 1ull) && __popcll(mask & ((1ull << lid) - 1ull)) == n) sh.channel_id = lid;
+    // the lane of the channel id also fetches what depends on it alone
+    if (((mask >> lid) & 1ull) && __popcll(mask & ((1ull << lid) - 1ull)) == n) {
+      sh.channel_id = lid;
+      sh.first_batch = plan.first_batch[lid];
+      sh.me = comm->ranks[lid][rank];
+    }
   }
   __syncthreads();
   if (sh.channel_id < 0) return;  // n beyond popcount(mask): not a channel of this launch
+  const int C = __popcll(mask);
+  const int nlanes = comm->hot.n_lanes;
   // Staging [C23 "前两个 Warp 与 Work Loader"]: wave 0 copies the
   // communicator hot fields, another wave the channel's first work batch.
-  const uint32_t first = plan.first_batch[sh.channel_id];
+  const uint32_t first = sh.first_batch;
   if (wave == 0) copy16(&sh.comm, &comm->hot, (int)sizeof(DevCommHot), lid);
   const int loader = nwaves > 1 ? 1 : 0;
   if (wave == loader) {
@@ -1183,6 +1213,44 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
     } else if (lid == 0) {
       sh.n_works = 0;
       sh.batch = DevBatch{0, 0, 0};
+    }
+  }
+  // step counters, read from global memory by every thread
+  const DevRank me = sh.me;
+  ConnCounters* rc = comm->hot.counters + ((int64_t)rank * C + n) * nlanes + lane;
+  ConnCounters* sc = comm->hot.counters + ((int64_t)me.next * C + n) * nlanes + lane;
+  // Steps persist across launches: this workgroup alone writes its receive
+  // head and its send tail, so they hold where it stopped last time.
+  const uint64_t recv_step0 = load_relaxed(&rc->head.value);
+  const uint64_t send_step0 = load_relaxed(&sc->tail.value);
+  // Placement handshake, second half: same XCD as the receiver = same L2 =
+  // the cheap publication path; anything else takes the agent-scope release.
+  // The dispatcher is not trusted: the check runs every launch.
+  if (hs_lane) {
+    const uint64_t* peer = &comm->hot.placement[peer_wg];
+    const uint64_t timeout = comm->hot.spin_timeout_ticks;
+    const uint32_t* abort_flag = comm->hot.abort_flag;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    uint64_t v = load_relaxed(peer);
+    bool ok = true;
+    for (uint32_t it = 1; v < (epoch << 8); ++it) {
+      __builtin_amdgcn_s_sleep(1);
+      v = load_relaxed(peer);
+      if ((it & 31u) == 0 && v < (epoch << 8) &&
+          (__hip_atomic_load(G(abort_flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
+           __builtin_amdgcn_s_memrealtime() - t0 > timeout)) {
+        ok = false;
+        break;
+      }
+    }
+    if (ok) {
+      sh.local_send = (v & 0xFFu) == my_xcc;
+    } else {
+      // the receiving workgroup never arrived (or another waiter gave up):
+      // raise the communicator's abort word, as every bounded wait does
+      __hip_atomic_store(G(comm->hot.abort_flag), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(G(comm->hot.abort_host), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      sh.abort = 1;
     }
   }
   __syncthreads();
@@ -1195,14 +1263,13 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.workers = nthreads;
   cx.rank = rank;
   cx.nranks = sh.comm.n_ranks;
-  const DevRank me = comm->ranks[sh.channel_id][rank];
   cx.ring_index = me.index;
   cx.next = me.next;
   cx.direct = (sh.comm.direct & 1) != 0;
   cx.direct_read = (sh.comm.direct & 2) != 0;
   cx.prev = me.prev;
   cx.lane = lane;
-  cx.nlanes = sh.comm.n_lanes;
+  cx.nlanes = nlanes;
   const bool deal = sh.comm.deal_works != 0;
   cx.split_lane = deal ? 0 : lane;
   cx.split_lanes = deal ? 1 : cx.nlanes;
@@ -1210,20 +1277,15 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.spc = sh.comm.slices_per_chunk;
   cx.step_bytes = sh.comm.step_bytes;
   cx.lane_step_bytes = sh.comm.lane_step_bytes;
-  const int C = sh.comm.n_channels;
   // each lane of a connector has its own FIFO of kSteps slots
   cx.recv_fifo = sh.comm.fifo + (((int64_t)rank * C + n) * cx.nlanes + lane) * sh.comm.lane_buff_bytes;
   cx.send_fifo = sh.comm.fifo + (((int64_t)me.next * C + n) * cx.nlanes + lane) * sh.comm.lane_buff_bytes;
-  ConnCounters* rc = sh.comm.counters + ((int64_t)rank * C + n) * cx.nlanes + lane;
-  ConnCounters* sc = sh.comm.counters + ((int64_t)me.next * C + n) * cx.nlanes + lane;
   cx.recv_tail = &rc->tail.value;
   cx.recv_head = &rc->head.value;
   cx.send_tail = &sc->tail.value;
   cx.send_head = &sc->head.value;
-  // Steps persist across launches: this workgroup alone writes its receive
-  // head and its send tail, so they hold where it stopped last time.
-  cx.recv_step = load_relaxed(cx.recv_head);
-  cx.send_step = load_relaxed(cx.send_tail);
+  cx.recv_step = recv_step0;
+  cx.send_step = send_step0;
   cx.tail_cache = 0;
   cx.head_cache = 0;
   cx.abort_flag = sh.comm.abort_flag;
@@ -1238,24 +1300,7 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   cx.trace = (sh.comm.debug_flags & 2) ? sh.comm.trace + (int64_t)blockIdx.x * sh.comm.trace_cap : nullptr;
   cx.trace_n = 0;
   cx.trace_cap = (uint32_t)sh.comm.trace_cap;
-
-  // Placement handshake: publish this workgroup's XCD for this launch, then
-  // learn the XCD of the workgroup that receives from it.  Same XCD = same
-  // L2 = the cheap publication path; anything else takes the agent-scope
-  // release.  The dispatcher is not trusted: the check runs every launch.
-  // Launches are counted on the device (each workgroup's own slot holds its
-  // count), so a launch replayed from a captured graph counts as well.
-  if (tid == 0) {
-    const uint32_t my_xcc = xcc_id();
-    const uint64_t epoch = (load_relaxed(&sh.comm.placement[blockIdx.x]) >> 8) + 1;
-    store_relaxed(&sh.comm.placement[blockIdx.x], (epoch << 8) | my_xcc);
-    const uint32_t peer = sh.comm.wg_of[((int64_t)me.next * C + n) * cx.nlanes + lane];
-    const bool ok = wait_geq(&sh.comm.placement[peer], epoch << 8, cx);
-    sh.abort = ok ? 0 : 1;
-    sh.local_send = ok && (load_relaxed(&sh.comm.placement[peer]) & 0xFFu) == my_xcc;
-  }
-  __syncthreads();
-  cx.local_send = sh.local_send;
+  cx.local_send = sh.local_send != 0;
   if (sh.abort) return;
 
   // RunWorkBatch [C23 "RunWorkBatch 与 Fused Work"]: the works of a batch run
