@@ -296,17 +296,21 @@ def main():
         # the same K steps captured into one HIP graph and replayed: the
         # host's per-launch cost leaves the timed region
         graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            hcap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-            for _ in range(args.steps):
-                if len(xs) == 1:
-                    comm_lib.check(lib.rar_allreduce(comm.handle, sarr, rarr, w.counts[0], dcode,
-                                                     comm_lib.SUM, hcap))
-                else:
-                    comm_lib.check(lib.rar_group_start(comm.handle))
-                    for s_, r_ in zip(sends, recvs):
-                        comm.allreduce(s_, r_)
-                    comm_lib.check(lib.rar_group_end(comm.handle, hcap))
+        try:
+            with torch.cuda.graph(graph):
+                hcap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                for _ in range(args.steps):
+                    if len(xs) == 1:
+                        comm_lib.check(lib.rar_allreduce(comm.handle, sarr, rarr, w.counts[0], dcode,
+                                                         comm_lib.SUM, hcap))
+                    else:
+                        comm_lib.check(lib.rar_group_start(comm.handle))
+                        for s_, r_ in zip(sends, recvs):
+                            comm.allreduce(s_, r_)
+                        comm_lib.check(lib.rar_group_end(comm.handle, hcap))
+        except comm_lib.RarError as e:
+            print(f"--graph: this workload cannot be captured ({e})", file=sys.stderr)
+            sys.exit(2)
         graph.replay()  # warm
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
