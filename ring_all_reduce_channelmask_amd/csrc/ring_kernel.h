@@ -1304,16 +1304,28 @@ __global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
   if (sh.abort) return;
 
   // RunWorkBatch [C23 "RunWorkBatch 与 Fused Work"]: the works of a batch run
-  // in order; a change of active waves is fenced by a barrier; next_jump
-  // chains the channel's next batch.  With dealt works, the k-th work of the
-  // channel (counted over all its batches) runs on lane k mod n_lanes only.
+  // in order; a change of active waves between two works the workgroup runs
+  // is fenced by a barrier; next_jump chains the channel's next batch.  With
+  // dealt works, the k-th work of the channel (counted over all its batches)
+  // runs on lane k mod n_lanes only, and the other lanes step over it.
   uint32_t b = first;
-  uint32_t seq = 0;
+  int dealt = 0;         // with dealt works: the lane that runs the batch's first work
+  int prev_waves = -1;   // active waves of the previous work this workgroup ran
   while (b != 0) {
     const int nworks = sh.n_works;
-    for (int w = 0; w < nworks; ++w, ++seq) {
-      if (w > 0 && sh.works[w].n_waves != sh.works[w - 1].n_waves) __syncthreads();
-      if (deal && (int)(seq % (uint32_t)cx.nlanes) != lane) continue;
+    // every work of the batch, or (dealt) this lane's first one and then
+    // every n_lanes-th
+    int w0 = 0, wstep = 1;
+    if (deal) {
+      w0 = lane - dealt;
+      if (w0 < 0) w0 += cx.nlanes;
+      wstep = cx.nlanes;
+      dealt = (dealt + nworks) % cx.nlanes;
+    }
+    for (int w = w0; w < nworks; w += wstep) {
+      const int nw = sh.works[w].n_waves;
+      if (prev_waves >= 0 && nw != prev_waves) __syncthreads();
+      prev_waves = nw;
       run_ring<Ty, PROTO>(cx, sh.works[w]);
       if (cx.aborted) break;
     }
