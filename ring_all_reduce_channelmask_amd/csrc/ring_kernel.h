@@ -592,8 +592,14 @@ __device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* 
     // a receiver on another XCD additionally needs them written back.
     if (cx.tid == cx.nthreads - 2 && O::kRecv && !cx.drop_head) store_relaxed(cx.recv_head, cx.recv_step);
     if (cx.tid == cx.nthreads - 1 && O::kSend) {
-      if (!cx.local_send && !skip_send) release_fence();
-      store_relaxed(cx.send_tail, cx.send_step);
+      // to a receiver on this XCD the tail, like the payload before it, only
+      // has to reach the shared L2: a workgroup-scope store
+      if (cx.local_send) {
+        store_relaxed_xcd(cx.send_tail, cx.send_step);
+      } else {
+        if (!skip_send) release_fence();
+        store_relaxed(cx.send_tail, cx.send_step);
+      }
     }
   }
 }
