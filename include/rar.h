@@ -343,7 +343,9 @@ typedef struct {
 
 /* The channel split of a launch of `nworks` collectives of `counts[i]`
  * elements.  Writes at most `cap` pieces, returns the total in *npieces and
- * the protocol's chunk maximum (elements) in *chunk_max. */
+ * the protocol's chunk maximum (elements) in *chunk_max (may be NULL).
+ * RAR_INVALID_ARGUMENT for a bad shape or dtype, nworks < 1, NULL counts or
+ * npieces, a negative cap, or NULL pieces with cap > 0. */
 rar_result_t rar_plan_pieces(int nranks, uint64_t channel_mask, rar_proto_t proto,
                              size_t buff_size, int chunk_steps, rar_dtype_t dtype, int nworks,
                              const size_t* counts, rar_piece_t* pieces, int cap, int* npieces,

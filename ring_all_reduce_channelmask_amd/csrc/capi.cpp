@@ -299,6 +299,7 @@ rar_result_t rar_plan_pieces(int nranks, uint64_t channel_mask, rar_proto_t prot
     return fail(RAR_INVALID_ARGUMENT, err);
   if (rar_result_t r = check_dtype(dtype)) return r;
   if (nworks < 1 || !counts || !npieces) return fail(RAR_INVALID_ARGUMENT, "bad work list");
+  if (cap < 0 || (cap > 0 && !pieces)) return fail(RAR_INVALID_ARGUMENT, "bad piece buffer");
   std::vector<size_t> cv(counts, counts + nworks);
   const int64_t es = rar::elem_size(dtype);
   const std::vector<rar::Piece> ps = rar::split_channels(channel_mask, proto, buff_size, chunk_steps, es, cv);
@@ -625,8 +626,19 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
   if (!c) {
     rar_result_t r = rar_comm_create(&c, nranks, ring_order, mask, proto, buff_size, chunk_steps, nullptr);
     if (r != RAR_SUCCESS) return r;
-    std::lock_guard<std::mutex> lk(g_cache_mu);
-    g_cache[key] = c;
+    rar_comm* extra = nullptr;
+    {
+      std::lock_guard<std::mutex> lk(g_cache_mu);
+      auto it = g_cache.find(key);
+      if (it == g_cache.end()) {
+        g_cache[key] = c;
+      } else {
+        // another thread cached the same shape meanwhile: use that one
+        extra = c;
+        c = it->second;
+      }
+    }
+    if (extra) release(extra);
   }
   return rar_allreduce(c, sendbufs, recvbufs, count, dtype, op, stream);
 }

@@ -199,3 +199,21 @@ def test_planner_matches_oracle_split_random():
         assert ours == theirs
 
     check()
+
+
+def test_plan_pieces_buffer_checks_and_count_query():
+    """rar_plan_pieces with cap = 0 and no buffer returns the piece count
+    only; a negative cap or a NULL buffer with cap > 0 is an invalid
+    argument."""
+    lib = _lib.load()
+    counts = (ctypes.c_size_t * 2)(100000, 7)
+    n, cmax = ctypes.c_int(), ctypes.c_int64()
+    rc = lib.rar_plan_pieces(4, 0xF, _lib.PROTO["SIMPLE"], 65536, 4, _lib.DTYPE["float32"], 2,
+                             counts, None, 0, ctypes.byref(n), ctypes.byref(cmax))
+    assert rc == 0
+    ours, _ = rar.plan_pieces(4, 0xF, "SIMPLE", 65536, 4, "float32", [100000, 7])
+    assert n.value == len(ours)
+    for cap, buf in ((-1, None), (4, None)):
+        rc = lib.rar_plan_pieces(4, 0xF, _lib.PROTO["SIMPLE"], 65536, 4, _lib.DTYPE["float32"], 2,
+                                 counts, buf, cap, ctypes.byref(n), ctypes.byref(cmax))
+        assert rc == _lib.INVALID_ARGUMENT
