@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 # guarantee, and consecutive launches are ~20 us closer together.
 TUNING = {
     "simple_64m": dict(lanes=5, waves=8, launch_mode=1),
-    "ll128_64m": dict(lanes=10, waves=4, launch_mode=1),
+    "ll128_64m": dict(lanes=16, waves=4, launch_mode=1),
     "bf16_n8": dict(lanes=2, waves=8, launch_mode=1),
     "int32_n8": dict(lanes=2, waves=8, launch_mode=1),
     "ll_512k": dict(lanes=16, waves=2, launch_mode=1),

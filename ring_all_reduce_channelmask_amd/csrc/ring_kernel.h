@@ -1146,8 +1146,12 @@ __device__ void load_batch(Shmem& sh, const Plan& a, uint32_t b, int lid) {
 }  // namespace
 
 // ---------------------------------------------------------------- entry
+// LL128 workgroups are small (4 waves in the measured shape) and the protocol
+// wants many of them: capping its registers at three waves per SIMD lets three
+// such workgroups share a CU (bf16 then spills a few hundred bytes per lane).
 template <class Ty, int PROTO>
-__global__ void __launch_bounds__(512) ring_allreduce_kernel(KernelArgs args) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PROTO == kLL128 ? 3 : 1)))
+ring_allreduce_kernel(KernelArgs args) {
   __shared__ Shmem sh;
   __shared__ __attribute__((aligned(16))) uint8_t stage[PROTO == kLL128 ? kMaxWaves * kLl128Unroll * 1024 : 16];
   const DevComm* comm = args.comm;
