@@ -112,12 +112,13 @@ typedef struct {
                             a pipeline found split falls back to the
                             agent-scope release).  1: spread the ranks over
                             different XCDs (every hop crosses L2s)         */
-  int slices_per_chunk;  /* Simple: slices per chunk, 2 (0 = default) or 4
-                            (needs chunk_steps 4).  Each slice still moves
+  int slices_per_chunk;  /* Simple: slices per chunk, 1, 2 (0 = default)
+                            or 4 (needs chunk_steps 4).  Each slice moves
                             StepPerSlice = chunk_steps / slices FIFO steps
                             and every call still consumes chunk_steps steps;
-                            smaller slices keep fewer FIFO bytes in flight.
-                            Timing only: results are identical            */
+                            smaller slices keep fewer FIFO bytes in flight,
+                            fewer slices mean fewer dependent hops for small
+                            messages.  Timing only: results are identical */
   int direct;            /* Simple only, bit mask of the direct variants
                             [C23 "发布顺序与 Fence", direct read/write].
                             Bit 0, direct write: the rank that completes a
