@@ -608,3 +608,34 @@ def test_more_than_2g_elements(proto):
         comm.close()
     for r in range(2):
         assert torch.equal(recvs[r], want), f"rank {r}"
+
+
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bfloat16"])
+@pytest.mark.parametrize("op", ["sum", "prod", "avg", "premulsum"])
+def test_ll128_benchmark_shape_every_dtype_and_operator(dtype, op):
+    """LL128 in the launch shape the benchmark uses (16 lanes x 4 waves over
+    12 channels: 768 workgroups, three per CU, possible because the LL128
+    kernels keep to three waves' registers per SIMD; the bf16 ones spill),
+    for every payload type and the operators with the heaviest kernels, on
+    a ragged 3-collective group, bit for bit against the closed form."""
+    rng = np.random.default_rng([["int32", "float32", "bfloat16"].index(dtype),
+                                 ["sum", "prod", "avg", "premulsum"].index(op)])
+    import bench
+    tune = dict(bench.TUNING["ll128_64m"])
+    assert (tune["lanes"], tune["waves"]) == (16, 4)
+    comm = _comm(nranks=4, ring_order=[0, 2, 3, 1], mask=0xFFF, proto="LL128", **tune)
+    counts = [1 << 20, 123457, 5]
+    if dtype == "int32":
+        xs = [rng.integers(-2 ** 31, 2 ** 31, size=(4, c)).astype(np.int32) for c in counts]
+    else:
+        xs = [_rand(dtype, (4, c), int(rng.integers(1 << 20))) for c in counts]
+    scs = [_rand(dtype, (4,), 7 + i) for i in range(len(counts))] if op == "premulsum" else None
+    if scs is not None and dtype == "int32":
+        scs = [rng.integers(-9, 10, size=4).astype(np.int32) for _ in counts]
+    got = run_hip(comm, xs, dtype, op=op, scalars=scs)
+    comm.close()
+    want = cf.allreduce(xs, [0, 2, 3, 1], 0xFFF, "LL128", 4915200, 4, dtype, op=op,
+                        scalars=None if scs is None else np.stack(scs))
+    for i in range(len(xs)):
+        for r in range(4):
+            assert_bits_equal(got[i][r], want[i], f"{dtype} {op} work {i} rank {r}")
