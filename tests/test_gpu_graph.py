@@ -143,3 +143,50 @@ def test_captured_oneshot_replays():
         want = oneshot.allreduce(xs, "float32")
         for r in range(4):
             assert_bits_equal(y[r].cpu().numpy(), want, f"replay {rep} rank {r}")
+
+
+@pytest.mark.parametrize("key", ["simple_4k", "ll_512k", "simple_64m", "ll128_64m"])
+def test_benchmark_shapes_replayed_from_a_graph(key):
+    """The ring workloads at full size in the launch shape the benchmark
+    times (its TUNING table), captured once and replayed with fresh inputs,
+    an eager launch of the same communicator after each replay; every
+    result bit for bit against the closed form."""
+    import torch
+    import bench
+    import ring_all_reduce_channelmask_amd as rar
+    w = wl.WORKLOADS[key]
+    N, count = w.nranks, w.counts[0]
+    cs = w.chunk_steps if w.proto == "SIMPLE" else 0
+    comm = rar.Comm(N, list(w.ring_order), w.mask, proto=w.proto, buff_size=w.buff_size,
+                    chunk_steps=cs, **bench.TUNING[key])
+    sends = [torch.empty(count, dtype=getattr(torch, w.dtype), device="cuda") for _ in range(N)]
+    recvs = [torch.empty_like(t) for t in sends]
+    _fill(sends, wl.inputs_for(w)[0], w.dtype)
+    comm.allreduce(sends, recvs)  # eager launch before the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        comm.allreduce(sends, recvs)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        x = _rand(w.dtype, (N, count), 1000 + rep)
+        _fill(sends, x, w.dtype)
+        for t in recvs:
+            t.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert comm.async_error() == 0
+        want = cf.allreduce([x], list(w.ring_order), w.mask, w.proto, w.buff_size, w.chunk_steps,
+                            w.dtype)[0]
+        for r in range(N):
+            assert_bits_equal(to_host(recvs[r], w.dtype), want, f"{key} replay {rep} rank {r}")
+        for t in recvs:
+            t.fill_(0)
+        comm.allreduce(sends, recvs)
+        torch.cuda.synchronize()
+        assert comm.async_error() == 0
+        for r in range(N):
+            assert_bits_equal(to_host(recvs[r], w.dtype), want, f"{key} eager {rep} rank {r}")
+    del graph
+    comm.close()
