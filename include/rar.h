@@ -45,6 +45,11 @@
 extern "C" {
 #endif
 
+/* Result codes.  As the pages' library reports every failure as a result
+ * code (the ring builder returns an internal error with the message "ring
+ * does not loop back") [C12 "Graph 如何变成完整 ring"], each entry point
+ * returns one of these and never throws; the message of the last failure on
+ * the calling thread is kept for rar_get_last_error(). */
 typedef enum {
   RAR_SUCCESS = 0,
   RAR_INVALID_ARGUMENT = 1, /* a precondition below is violated            */
@@ -204,7 +209,8 @@ rar_result_t rar_comm_create_rings(rar_comm_t* comm, int nranks, int nrings,
  *                       [C23 "LL128：15/16 Payload" stages misaligned user
  *                       data; here the hardware's unaligned vector accesses
  *                       serve it].  recvbufs[r] == sendbufs[r] runs in place;
- *                       other overlap is not allowed.
+ *                       no other two of the 2N buffers may overlap (checked
+ *                       on the host: RAR_INVALID_ARGUMENT, nothing queued).
  *   count               elements per rank; 0 launches nothing, leaves the
  *                       FIFO steps untouched and does not look at the pointers.
  * Inside rar_group_start/rar_group_end the call is queued instead of launched.
@@ -232,21 +238,43 @@ rar_result_t rar_allreduce_premul(rar_comm_t comm, const void* const* sendbufs,
  * rar_group_end with nothing queued is a no-op. */
 rar_result_t rar_group_start(rar_comm_t comm);
 rar_result_t rar_group_end(rar_comm_t comm, void* stream);
+/* Close an open group without launching it: the queued calls are dropped
+ * and nothing reaches the device or the FIFO steps.  For callers whose
+ * queueing failed halfway (the pages' group brackets [C2 "1 communicator":
+ * ncclGroupStart/End around the per-rank calls] leave no half-built group
+ * behind).  A communicator without an open group is left as it is. */
+rar_result_t rar_group_discard(rar_comm_t comm);
 
-/* Destroy after the stream has passed the last call, and after every HIP
+/* Release the communicator's FIFOs, counters and launch-plan memory.  The
+ * pages' clean-up order ends with destroying the communicator, after the
+ * collectives that use it and the buffers they touch are done with
+ * [C2 "4 User Buffer Registration", the ncclCommDestroy step]: destroy after
+ * the stream has passed the last call, and after every HIP
  * graph that captured a launch on this communicator has been destroyed or
  * will not be replayed again (a replay would use freed memory).  NULL is a
  * no-op. */
 rar_result_t rar_comm_destroy(rar_comm_t comm);
 
-/* One-shot form of the pages' problem statement: creates (and caches, keyed
+/* The collective call with its communicator set-up folded in: the
+ * single-process set-up that builds one communicator for all ranks at once
+ * [C2 "1 communicator": ncclCommInitAll] followed by the stream-ordered
+ * AllReduce call (send and receive buffers, count, type, operator, stream)
+ * [C2 "2 CUDA stream": ncclAllReduce(d_in, d_out, count, ncclFloat, ncclSum,
+ * comm, stream)], with the ring, protocol, channels, buffer size and chunk
+ * steps as arguments instead of tuner choices.  It creates (and caches, keyed
  * by every argument that shapes the FIFOs) a communicator on first use, then
  * runs rar_allreduce.  The mask is the nchannels lowest bits.  Creation
  * allocates and initialises device memory, which a stream capture does not
  * allow: make the first call with a given shape outside any capture.  The
  * cached communicators use the cooperative launch, so under capture this
- * entry point fails with RAR_UNSUPPORTED.  Errors as for rar_comm_create and
- * rar_allreduce. */
+ * entry point fails with RAR_UNSUPPORTED.  Buffers are checked before
+ * anything touches the device: NULL, misaligned or overlapping buffers of
+ * different ranks give RAR_INVALID_ARGUMENT.  A cached communicator may be
+ * used from several threads and streams: calls on it are serialised by a
+ * lock, and a call on another stream than the previous one first makes its
+ * stream wait for the previous launch (hipStreamWaitEvent), since both
+ * share one set of FIFOs and step counters.  Errors as for rar_comm_create
+ * and rar_allreduce. */
 rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks,
                             size_t count, rar_dtype_t dtype, rar_redop_t op,
                             const int* ring_order, rar_proto_t proto, int nchannels,
@@ -352,8 +380,12 @@ rar_result_t rar_plan_pieces(int nranks, uint64_t channel_mask, rar_proto_t prot
                              const size_t* counts, rar_piece_t* pieces, int cap, int* npieces,
                              int64_t* chunk_max);
 
+/* Name of a result code, and the message of the last failing call on the
+ * calling thread (empty if the last call succeeded), as the pages' ring
+ * builder pairs its result code with a warning that says what failed
+ * [C12 "Graph 如何变成完整 ring"].  Both return static or thread-local
+ * storage owned by the library: valid until the thread's next call. */
 const char* rar_get_error_string(rar_result_t r);
-/* Detail of the last failing call on this thread (empty if none). */
 const char* rar_get_last_error(void);
 
 #ifdef __cplusplus

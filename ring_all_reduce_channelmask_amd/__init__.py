@@ -121,12 +121,17 @@ class Comm:
 
     @contextlib.contextmanager
     def group(self, stream=None):
+        """Queue the body's AllReduces and launch them as one fused launch
+        when the body ends normally.  If the body raises, the partly queued
+        group is dropped (nothing is launched) and the exception propagates."""
         lib = _lib.load()
         _lib.check(lib.rar_group_start(self._h))
         try:
             yield self
-        finally:
-            _lib.check(lib.rar_group_end(self._h, _stream_handle(stream)))
+        except BaseException:
+            lib.rar_group_discard(self._h)
+            raise
+        _lib.check(lib.rar_group_end(self._h, _stream_handle(stream)))
 
     def async_error(self):
         return _lib.load().rar_comm_get_async_error(self._h)

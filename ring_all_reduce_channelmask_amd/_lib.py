@@ -69,6 +69,7 @@ SIGNATURES = [
                                         _c.c_void_p, _c.c_void_p]),
     ("rar_group_start", _c.c_int, [_c.c_void_p]),
     ("rar_group_end", _c.c_int, [_c.c_void_p, _c.c_void_p]),
+    ("rar_group_discard", _c.c_int, [_c.c_void_p]),
     ("rar_comm_destroy", _c.c_int, [_c.c_void_p]),
     ("ring_allreduce", _c.c_int, [_vpp, _vpp, _c.c_int, _c.c_size_t, _c.c_int, _c.c_int, _ip,
                                   _c.c_int, _c.c_int, _c.c_size_t, _c.c_int, _c.c_void_p]),

@@ -17,9 +17,7 @@
 #include <string>
 #include <vector>
 
-#include "plan.h"
-#include "rar.h"
-#include "rar_device.h"
+#include "capi_internal.h"
 
 namespace rar {
 const void* get_ring_kernel_i32(int proto, int red);
@@ -39,13 +37,24 @@ const void* get_kernel(int dtype, int proto, int red) {
 }  // namespace rar
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-rar_result_t fail(rar_result_t r, const std::string& msg) {
+namespace rar {
+rar_result_t set_error(rar_result_t r, const std::string& msg) {
   g_last_error = msg;
   return r;
 }
+void clear_error() { g_last_error.clear(); }
+}  // namespace rar
+
+namespace {
+
+using rar::QueuedCall;
+using rar::check_dtype;
+using rar::check_op;
+using rar::check_rank_buffers;
+rar_result_t fail(rar_result_t r, const std::string& msg) { return rar::set_error(r, msg); }
 
 #define RAR_HIP(expr)                                                                      \
   do {                                                                                     \
@@ -54,21 +63,11 @@ rar_result_t fail(rar_result_t r, const std::string& msg) {
       return fail(RAR_HIP_ERROR, std::string(#expr) + " failed: " + hipGetErrorString(e_)); \
   } while (0)
 
-struct QueuedCall {
-  std::vector<void*> send, recv;
-  size_t count;
-  int dtype;
-  int red;
-  std::vector<uint32_t> scalars;  // PreMulSum: one scalar per rank (payload bits)
-};
-
 // Scalar bits of rank r from a host array of payload-type elements.
 uint32_t scalar_bits(const void* scalars, int dtype, int r) {
   if (dtype == RAR_BFLOAT16) return reinterpret_cast<const uint16_t*>(scalars)[r];
   return reinterpret_cast<const uint32_t*>(scalars)[r];
 }
-
-size_t align_to(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 }  // namespace
 
@@ -106,13 +105,136 @@ struct rar_comm {
   bool upload_pending = false;
   bool in_group = false;
   std::vector<QueuedCall> queue;
+  // ring_allreduce's cached communicators: callers may reach one from
+  // several threads and streams, so its calls are serialised here, and a
+  // call on a new stream waits for the previous launch (last_done).
+  std::mutex call_mu;
+  hipEvent_t last_done = nullptr;
+  hipStream_t last_stream = nullptr;
+  bool has_last = false;
 };
+
+namespace rar {
+
+rar_result_t check_dtype(int dtype) {
+  if (dtype != RAR_INT32 && dtype != RAR_FLOAT32 && dtype != RAR_BFLOAT16)
+    return set_error(RAR_INVALID_ARGUMENT, "unknown dtype");
+  return RAR_SUCCESS;
+}
+
+rar_result_t check_op(int op) {
+  if (op < RAR_SUM || op > RAR_AVG) {
+    if (op == RAR_PREMULSUM)
+      return set_error(RAR_INVALID_ARGUMENT, "RAR_PREMULSUM needs scalars: use the *_premul entry point");
+    return set_error(RAR_INVALID_ARGUMENT, "unknown reduction operator");
+  }
+  return RAR_SUCCESS;
+}
+
+// Buffers of one collective: none NULL, each aligned to its element size,
+// and no two of the 2N buffers overlapping, except that a rank's receive
+// buffer may be its own send buffer (in place).  The direct variants write
+// into the next rank's receive buffer and read the previous rank's send
+// buffer, so an overlap between ranks would corrupt an input before it is
+// read.  Host-side only: no device call.
+rar_result_t check_rank_buffers(int nranks, const void* const* sendbufs, void* const* recvbufs,
+                                size_t count, int dtype) {
+  if (!sendbufs || !recvbufs) return set_error(RAR_INVALID_ARGUMENT, "sendbufs/recvbufs is NULL");
+  const size_t es = (size_t)rar::elem_size(dtype);
+  if (count > (SIZE_MAX / 2) / es) return set_error(RAR_INVALID_ARGUMENT, "count too large");
+  const uintptr_t bytes = count * es;
+  std::vector<std::pair<uintptr_t, int>> ranges;
+  ranges.reserve(2 * (size_t)nranks);
+  for (int r = 0; r < nranks; ++r) {
+    if (!sendbufs[r] || !recvbufs[r])
+      return set_error(RAR_INVALID_ARGUMENT, "buffer of rank " + std::to_string(r) + " is NULL");
+    const uintptr_t s = reinterpret_cast<uintptr_t>(sendbufs[r]);
+    const uintptr_t d = reinterpret_cast<uintptr_t>(recvbufs[r]);
+    if ((s | d) & (es - 1))
+      return set_error(RAR_INVALID_ARGUMENT,
+                  "buffer of rank " + std::to_string(r) + " is not aligned to its element size");
+    ranges.push_back({s, r});
+    if (d != s) ranges.push_back({d, r});
+  }
+  // sorted by start: two ranges overlap iff a start lies inside its predecessor
+  std::sort(ranges.begin(), ranges.end());
+  for (size_t i = 1; i < ranges.size(); ++i)
+    if (ranges[i].first - ranges[i - 1].first < bytes)
+      return set_error(RAR_INVALID_ARGUMENT, "buffers of ranks " + std::to_string(ranges[i - 1].second) + " and " +
+                                            std::to_string(ranges[i].second) + " overlap");
+  return RAR_SUCCESS;
+}
+
+
+PlanBlock build_plan_block(const std::vector<QueuedCall>& calls, int nranks, uint64_t mask, int proto,
+                           size_t buff, int chunk_steps, int n_channels, int n_waves) {
+  PlanBlock out;
+  const int64_t es = elem_size(calls.front().dtype);
+  std::vector<size_t> counts;
+  for (const QueuedCall& q : calls) counts.push_back(q.count);
+  const std::vector<Piece> pieces = split_channels(mask, proto, buff, chunk_steps, es, counts);
+  if (pieces.empty()) return out;  // nothing to move
+  const BatchPlan plan = encode_batches(pieces, n_channels, n_waves);
+  auto align_to = [](size_t v, size_t a) { return (v + a - 1) / a * a; };
+  const size_t off_batches = 0;
+  const size_t off_works = align_to(off_batches + plan.batches.size() * sizeof(DevBatch), 64);
+  const size_t off_ptrs = align_to(off_works + plan.works.size() * sizeof(DevWork), 64);
+  const size_t nptrs = calls.size() * (size_t)nranks * 2;
+  const size_t off_scalars = align_to(off_ptrs + nptrs * sizeof(void*), 64);
+  const size_t nscalars = calls.size() * (size_t)nranks;
+  const size_t off_first = align_to(off_scalars + nscalars * sizeof(uint32_t), 64);
+  const size_t total = align_to(off_first + plan.first_batch.size() * sizeof(uint32_t), 64);
+  out.bytes.assign(total, 0);
+  uint8_t* b = out.bytes.data();
+  std::memcpy(b + off_batches, plan.batches.data(), plan.batches.size() * sizeof(DevBatch));
+  std::memcpy(b + off_works, plan.works.data(), plan.works.size() * sizeof(DevWork));
+  void** ptrs = reinterpret_cast<void**>(b + off_ptrs);
+  for (size_t w = 0; w < calls.size(); ++w)
+    for (int r = 0; r < nranks; ++r) {
+      ptrs[(w * nranks + r) * 2] = calls[w].send[r];
+      ptrs[(w * nranks + r) * 2 + 1] = calls[w].recv[r];
+    }
+  uint32_t* scal = reinterpret_cast<uint32_t*>(b + off_scalars);
+  for (size_t w = 0; w < calls.size(); ++w)
+    for (int r = 0; r < nranks && !calls[w].scalars.empty(); ++r) scal[w * nranks + r] = calls[w].scalars[r];
+  std::memcpy(b + off_first, plan.first_batch.data(), plan.first_batch.size() * sizeof(uint32_t));
+  out.off_batches = (uint32_t)off_batches;
+  out.off_works = (uint32_t)off_works;
+  out.off_ptrs = (uint32_t)off_ptrs;
+  out.off_scalars = (uint32_t)off_scalars;
+  out.off_first = (uint32_t)off_first;
+  return out;
+}
+
+rar_result_t check_ring_call(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                             size_t count, int dtype, int op, const int* ring_order, int proto,
+                             int nchannels, size_t* buff_size, int* chunk_steps, uint64_t* mask,
+                             RingInfo* ring) {
+  if (nchannels < 1 || nchannels > 64) return set_error(RAR_INVALID_ARGUMENT, "nchannels must be in [1, 64]");
+  if (nranks < 2 || nranks > 64 || !ring_order)
+    return set_error(RAR_INVALID_ARGUMENT, "nranks must be in [2, 64] with a ring_order");
+  *mask = nchannels == 64 ? ~0ull : ((1ull << nchannels) - 1);
+  if (*buff_size == 0) *buff_size = default_buff_size(proto);
+  if (*chunk_steps == 0) *chunk_steps = 4;
+  std::string err;
+  if (!check_shape(nranks, *mask, proto, *buff_size, *chunk_steps, &err))
+    return set_error(RAR_INVALID_ARGUMENT, err);
+  if (!build_ring(nranks, ring_order, ring, &err)) return set_error(RAR_INVALID_ARGUMENT, err);
+  if (rar_result_t r = check_dtype(dtype)) return r;
+  if (rar_result_t r = check_op(op)) return r;
+  if (count == 0) return RAR_SUCCESS;  // the pointers are not looked at
+  if (count > (size_t(1) << 40)) return set_error(RAR_INVALID_ARGUMENT, "count too large");
+  return check_rank_buffers(nranks, sendbufs, recvbufs, count, dtype);
+}
+
+}  // namespace rar
 
 namespace {
 
 void release(rar_comm* c) {
   if (!c) return;
   if (c->upload_done) (void)hipEventDestroy(c->upload_done);
+  if (c->last_done) (void)hipEventDestroy(c->last_done);
   if (c->h_stage) (void)hipHostFree(c->h_stage);
   if (c->h_abort) (void)hipHostFree(c->h_abort);
   (void)hipFree(c->d_arena);
@@ -128,80 +250,27 @@ void release(rar_comm* c) {
   delete c;
 }
 
-rar_result_t check_dtype(int dtype) {
-  if (dtype != RAR_INT32 && dtype != RAR_FLOAT32 && dtype != RAR_BFLOAT16)
-    return fail(RAR_INVALID_ARGUMENT, "unknown dtype");
-  return RAR_SUCCESS;
-}
-
-rar_result_t check_op(int op) {
-  if (op < RAR_SUM || op > RAR_AVG) {
-    if (op == RAR_PREMULSUM)
-      return fail(RAR_INVALID_ARGUMENT, "RAR_PREMULSUM needs scalars: use the *_premul entry point");
-    return fail(RAR_INVALID_ARGUMENT, "unknown reduction operator");
-  }
-  return RAR_SUCCESS;
-}
-
-rar_result_t check_buffers(const rar_comm* c, const void* const* sendbufs, void* const* recvbufs,
-                           int dtype) {
-  if (!sendbufs || !recvbufs) return fail(RAR_INVALID_ARGUMENT, "sendbufs/recvbufs is NULL");
-  const uintptr_t align = (uintptr_t)rar::elem_size(dtype);
-  for (int r = 0; r < c->nranks; ++r) {
-    if (!sendbufs[r] || !recvbufs[r])
-      return fail(RAR_INVALID_ARGUMENT, "buffer of rank " + std::to_string(r) + " is NULL");
-    if ((reinterpret_cast<uintptr_t>(sendbufs[r]) | reinterpret_cast<uintptr_t>(recvbufs[r])) & (align - 1))
-      return fail(RAR_INVALID_ARGUMENT,
-                  "buffer of rank " + std::to_string(r) + " is not aligned to its element size");
-  }
-  return RAR_SUCCESS;
-}
-
 // Copy the launch description into the device arena (skipped when it is
 // byte-identical to the previous launch's) and launch the kernel.
 rar_result_t launch(rar_comm* c, const std::vector<QueuedCall>& calls, hipStream_t stream) {
   const int dtype = calls.front().dtype;
-  const int64_t es = rar::elem_size(dtype);
-  std::vector<size_t> counts;
-  for (const QueuedCall& q : calls) counts.push_back(q.count);
-  const std::vector<rar::Piece> pieces =
-      rar::split_channels(c->mask, c->proto, c->buff, c->chunk_steps, es, counts);
-  if (pieces.empty()) return RAR_SUCCESS;  // nothing to move: no launch, no step advance
+  rar::PlanBlock pb = rar::build_plan_block(calls, c->nranks, c->mask, c->proto, c->buff, c->chunk_steps,
+                                            c->C, c->W);
+  if (pb.bytes.empty()) return RAR_SUCCESS;  // nothing to move: no launch, no step advance
   if (__atomic_load_n(c->h_abort, __ATOMIC_ACQUIRE))
     return fail(RAR_ABORTED, "a previous launch on this communicator hit the wait watchdog");
-  const rar::BatchPlan plan = rar::encode_batches(pieces, c->C, c->W);
-
-  const size_t off_batches = 0;
-  const size_t off_works = align_to(off_batches + plan.batches.size() * sizeof(rar::DevBatch), 64);
-  const size_t off_ptrs = align_to(off_works + plan.works.size() * sizeof(rar::DevWork), 64);
-  const size_t nptrs = calls.size() * (size_t)c->nranks * 2;
-  const size_t off_scalars = align_to(off_ptrs + nptrs * sizeof(void*), 64);
-  const size_t nscalars = calls.size() * (size_t)c->nranks;
-  const size_t off_first = align_to(off_scalars + nscalars * sizeof(uint32_t), 64);
-  const size_t total = align_to(off_first + plan.first_batch.size() * sizeof(uint32_t), 64);
-  std::vector<uint8_t> bytes(total, 0);
-  std::memcpy(bytes.data() + off_batches, plan.batches.data(), plan.batches.size() * sizeof(rar::DevBatch));
-  std::memcpy(bytes.data() + off_works, plan.works.data(), plan.works.size() * sizeof(rar::DevWork));
-  void** ptrs = reinterpret_cast<void**>(bytes.data() + off_ptrs);
-  for (size_t w = 0; w < calls.size(); ++w)
-    for (int r = 0; r < c->nranks; ++r) {
-      ptrs[(w * c->nranks + r) * 2] = calls[w].send[r];
-      ptrs[(w * c->nranks + r) * 2 + 1] = calls[w].recv[r];
-    }
-  uint32_t* scal = reinterpret_cast<uint32_t*>(bytes.data() + off_scalars);
-  for (size_t w = 0; w < calls.size(); ++w)
-    for (int r = 0; r < c->nranks && !calls[w].scalars.empty(); ++r) scal[w * c->nranks + r] = calls[w].scalars[r];
-  std::memcpy(bytes.data() + off_first, plan.first_batch.data(), plan.first_batch.size() * sizeof(uint32_t));
+  std::vector<uint8_t>& bytes = pb.bytes;
+  const size_t total = bytes.size();
 
   rar::KernelArgs args;
   std::memset(&args, 0, offsetof(rar::KernelArgs, plan));
   args.comm = c->d_comm;
   args.wg_map = c->d_wgmap;
-  args.off_batches = (uint32_t)off_batches;
-  args.off_works = (uint32_t)off_works;
-  args.off_ptrs = (uint32_t)off_ptrs;
-  args.off_first = (uint32_t)off_first;
-  args.off_scalars = (uint32_t)off_scalars;
+  args.off_batches = pb.off_batches;
+  args.off_works = pb.off_works;
+  args.off_ptrs = pb.off_ptrs;
+  args.off_first = pb.off_first;
+  args.off_scalars = pb.off_scalars;
   // Under stream capture the launch becomes a graph node whose arguments are
   // copied at capture time: the plan must travel inline, and the launch must
   // be a plain one.
@@ -552,8 +621,8 @@ static rar_result_t allreduce_impl(rar_comm_t c, const void* const* sendbufs, vo
     return fail(RAR_UNSUPPORTED, "all AllReduces of a group must share one dtype and operator");
   // nothing to move: no launch, no step advance, pointers are not looked at
   if (count == 0) return RAR_SUCCESS;
-  if (rar_result_t r = check_buffers(c, sendbufs, recvbufs, dtype)) return r;
   if (count > (size_t(1) << 40)) return fail(RAR_INVALID_ARGUMENT, "count too large");
+  if (rar_result_t r = check_rank_buffers(c->nranks, sendbufs, recvbufs, count, dtype)) return r;
   QueuedCall q;
   for (int r = 0; r < c->nranks; ++r) q.send.push_back(const_cast<void*>(sendbufs[r]));
   q.recv.assign(recvbufs, recvbufs + c->nranks);
@@ -592,6 +661,14 @@ rar_result_t rar_group_start(rar_comm_t c) {
   return RAR_SUCCESS;
 }
 
+rar_result_t rar_group_discard(rar_comm_t c) {
+  g_last_error.clear();
+  if (!c) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
+  c->in_group = false;
+  c->queue.clear();
+  return RAR_SUCCESS;
+}
+
 rar_result_t rar_group_end(rar_comm_t c, void* stream) {
   g_last_error.clear();
   if (!c) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
@@ -607,12 +684,13 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
                             rar_dtype_t dtype, rar_redop_t op, const int* ring_order, rar_proto_t proto,
                             int nchannels, size_t buff_size, int chunk_steps, void* stream) {
   g_last_error.clear();
-  if (nchannels < 1 || nchannels > 64) return fail(RAR_INVALID_ARGUMENT, "nchannels must be in [1, 64]");
-  if (nranks < 2 || nranks > 64 || !ring_order)
-    return fail(RAR_INVALID_ARGUMENT, "nranks must be in [2, 64] with a ring_order");
-  const uint64_t mask = nchannels == 64 ? ~0ull : ((1ull << nchannels) - 1);
-  if (buff_size == 0) buff_size = rar::default_buff_size(proto);
-  if (chunk_steps == 0) chunk_steps = 4;
+  // every argument is checked on the host before the device is touched
+  uint64_t mask = 0;
+  rar::RingInfo ring;
+  if (rar_result_t r = rar::check_ring_call(sendbufs, recvbufs, nranks, count, dtype, op, ring_order, proto,
+                                            nchannels, &buff_size, &chunk_steps, &mask, &ring))
+    return r;
+  if (count == 0) return RAR_SUCCESS;  // nothing to move: no launch, pointers not looked at
   int dev = 0;
   RAR_HIP(hipGetDevice(&dev));
   std::vector<int64_t> key = {dev, nranks, (int64_t)mask, (int64_t)proto, (int64_t)buff_size, chunk_steps};
@@ -640,7 +718,19 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
     }
     if (extra) release(extra);
   }
-  return rar_allreduce(c, sendbufs, recvbufs, count, dtype, op, stream);
+  // One set of FIFOs and step counters serves every caller of this shape:
+  // launches must follow each other.  Same stream: stream order does it.
+  // Another stream: that stream first waits for the previous launch.
+  std::lock_guard<std::mutex> lk(c->call_mu);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (!c->last_done) RAR_HIP(hipEventCreateWithFlags(&c->last_done, hipEventDisableTiming));
+  if (c->has_last && c->last_stream != hs) RAR_HIP(hipStreamWaitEvent(hs, c->last_done, 0));
+  const rar_result_t r = rar_allreduce(c, sendbufs, recvbufs, count, dtype, op, stream);
+  if (r != RAR_SUCCESS) return r;
+  RAR_HIP(hipEventRecord(c->last_done, hs));
+  c->last_stream = hs;
+  c->has_last = true;
+  return RAR_SUCCESS;
 }
 
 static rar_result_t oneshot_impl(const void* const* sendbufs, void* const* recvbufs, int nranks,
@@ -661,28 +751,8 @@ static rar_result_t oneshot_impl(const void* const* sendbufs, void* const* recvb
   if (tune.unroll != 0 && tune.unroll != 1 && tune.unroll != 2 && tune.unroll != 4)
     return fail(RAR_INVALID_ARGUMENT, "unroll must be 0, 1, 2 or 4");
   if (count == 0) return RAR_SUCCESS;  // nothing to move: no launch, pointers not inspected
-  if (!sendbufs || !recvbufs) return fail(RAR_INVALID_ARGUMENT, "sendbufs/recvbufs is NULL");
+  if (rar_result_t r = check_rank_buffers(nranks, sendbufs, recvbufs, count, dtype)) return r;
   const size_t es = (size_t)rar::elem_size(dtype);
-  if (count > (SIZE_MAX / 2) / es) return fail(RAR_INVALID_ARGUMENT, "count too large");
-  const uintptr_t bytes = count * es;
-  // [lo, hi) of every buffer; a receive buffer may be its own rank's send
-  // buffer (in place) and must not overlap anything else
-  std::vector<std::pair<uintptr_t, int>> ranges;
-  for (int r = 0; r < nranks; ++r) {
-    if (!sendbufs[r] || !recvbufs[r])
-      return fail(RAR_INVALID_ARGUMENT, "buffer of rank " + std::to_string(r) + " is NULL");
-    const uintptr_t s = reinterpret_cast<uintptr_t>(sendbufs[r]);
-    const uintptr_t d = reinterpret_cast<uintptr_t>(recvbufs[r]);
-    if ((s | d) & (es - 1))
-      return fail(RAR_INVALID_ARGUMENT, "buffer of rank " + std::to_string(r) + " is not aligned to its element size");
-    ranges.push_back({s, r});
-    if (d != s) ranges.push_back({d, r});
-  }
-  std::sort(ranges.begin(), ranges.end());
-  for (size_t i = 1; i < ranges.size(); ++i)
-    if (ranges[i].first - ranges[i - 1].first < bytes)
-      return fail(RAR_INVALID_ARGUMENT, "buffers of ranks " + std::to_string(ranges[i - 1].second) + " and " +
-                                            std::to_string(ranges[i].second) + " overlap");
 
   rar::OneshotArgs a;
   std::memset(&a, 0, sizeof(a));

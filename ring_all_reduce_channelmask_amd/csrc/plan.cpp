@@ -188,11 +188,16 @@ BatchPlan encode_batches(const std::vector<Piece>& pieces, int n_channels, int n
 std::vector<uint32_t> make_wg_map(int nranks, int n_channels, int n_lanes, bool spread) {
   constexpr int kXcds = 8;
   const int pipes = n_channels * n_lanes;
+  if (!spread) {
+    std::vector<uint32_t> map(wg_grid_size(nranks, pipes));
+    for (size_t g = 0; g < map.size(); ++g) map[g] = wg_entry((uint32_t)g, nranks, n_lanes, pipes);
+    return map;
+  }
   std::vector<std::vector<uint32_t>> per_xcd(kXcds);
   for (int q = 0; q < pipes; ++q) {
     const int n = q / n_lanes, lane = q % n_lanes;
     for (int r = 0; r < nranks; ++r)
-      per_xcd[(q + (spread ? r : 0)) % kXcds].push_back((uint32_t)r | ((uint32_t)n << 8) |
+      per_xcd[(q + r) % kXcds].push_back((uint32_t)r | ((uint32_t)n << 8) |
                                                          ((uint32_t)lane << 16));
   }
   size_t depth = 0;

@@ -130,6 +130,27 @@ struct alignas(16) DevComm {
   DevRank ranks[kMaxChannels][kMaxRanks];
 };
 
+// The workgroup map in closed form.  The dispatcher hands block g to XCD
+// g mod 8, so the map puts the N ranks of one (channel, lane) pipeline on one
+// XCD: XCD x takes pipelines q = x, x + 8, x + 16, ... (q = n * lanes + lane),
+// and its k-th workgroup is rank k mod N of pipeline x + 8 * (k / N).  Slots
+// past the last pipeline stay idle.  The host planner builds the map from
+// these, and the no-alloc entry point builds it on the device.
+__host__ __device__ inline uint32_t wg_grid_size(int nranks, int pipes) {
+  return 8u * (uint32_t)nranks * (uint32_t)((pipes + 7) / 8);
+}
+__host__ __device__ inline uint32_t wg_entry(uint32_t g, int nranks, int n_lanes, int pipes) {
+  const uint32_t x = g % 8u, k = g / 8u;
+  const uint32_t q = x + 8u * (k / (uint32_t)nranks), r = k % (uint32_t)nranks;
+  if (q >= (uint32_t)pipes) return 0xFFFFFFFFu;
+  return r | ((q / (uint32_t)n_lanes) << 8) | ((q % (uint32_t)n_lanes) << 16);
+}
+// The workgroup of rank `rank` in the pipeline of workgroup g.
+__host__ __device__ inline uint32_t wg_of_rank(uint32_t g, int nranks, int rank) {
+  const uint32_t x = g % 8u, k = g / 8u;
+  return ((k / (uint32_t)nranks) * (uint32_t)nranks + (uint32_t)rank) * 8u + x;
+}
+
 // Bytes of launch plan that travel inside the kernel arguments.  A plan that
 // fits (every single collective up to 16 channels and 8 ranks, small groups)
 // needs no upload before the launch, and a captured launch stays valid for

@@ -217,3 +217,95 @@ def test_plan_pieces_buffer_checks_and_count_query():
         rc = lib.rar_plan_pieces(4, 0xF, _lib.PROTO["SIMPLE"], 65536, 4, _lib.DTYPE["float32"], 2,
                                  counts, buf, cap, ctypes.byref(n), ctypes.byref(cmax))
         assert rc == _lib.INVALID_ARGUMENT
+
+
+def _ptrs(vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+@pytest.mark.parametrize("entry", ["ring", "oneshot"])
+def test_overlapping_ranks_rejected_before_any_device_call(entry):
+    """Buffers of different ranks that overlap are refused on the host (no
+    HIP call is made: this container has no GPU, so any device call would
+    fail with a HIP error instead)."""
+    lib = _lib.load()
+    N, count, base = 4, 1000, 1 << 32
+    order = (ctypes.c_int * N)(0, 2, 3, 1)
+    sends = [base + r * 8192 for r in range(N)]
+    cases = {
+        "recv of rank 1 inside send of rank 2": (sends, [base + 65536 + r * 8192 for r in range(N)],
+                                                  {1: sends[2] + 4}),
+        "two ranks share a send buffer": ([sends[0], sends[0], sends[2], sends[3]], None, {}),
+        "recv of rank 3 = send of rank 0": (sends, [base + 65536 + r * 8192 for r in range(N)],
+                                            {3: sends[0]}),
+    }
+    for what, (s, r, patch) in cases.items():
+        s = list(s)
+        r = list(r) if r is not None else [base + 65536 + k * 8192 for k in range(N)]
+        for k, v in patch.items():
+            r[k] = v
+        if entry == "ring":
+            rc = lib.ring_allreduce(_ptrs(s), _ptrs(r), N, count, _lib.DTYPE["float32"], 0, order,
+                                    _lib.PROTO["SIMPLE"], 2, 0, 0, None)
+        else:
+            rc = lib.rar_oneshot_allreduce(_ptrs(s), _ptrs(r), N, count, _lib.DTYPE["float32"], 0,
+                                           None, None)
+        assert rc == _lib.INVALID_ARGUMENT, what
+        assert b"overlap" in lib.rar_get_last_error(), what
+
+
+def test_ring_allreduce_checks_arguments_on_the_host():
+    lib = _lib.load()
+    N = 4
+    order = (ctypes.c_int * N)(0, 1, 1, 2)   # not a permutation
+    s = _ptrs([(1 << 32) + k * 8192 for k in range(N)])
+    r = _ptrs([(1 << 33) + k * 8192 for k in range(N)])
+    assert lib.ring_allreduce(s, r, N, 100, 1, 0, order, 2, 1, 0, 0, None) == _lib.INVALID_ARGUMENT
+    order = (ctypes.c_int * N)(0, 1, 2, 3)
+    # misaligned fp32 buffer, bad dtype, bad operator, bad chunk steps
+    bad = _ptrs([(1 << 32) + 2] + [(1 << 32) + k * 8192 for k in range(1, N)])
+    assert lib.ring_allreduce(bad, r, N, 100, 1, 0, order, 2, 1, 0, 0, None) == _lib.INVALID_ARGUMENT
+    assert lib.ring_allreduce(s, r, N, 100, 7, 0, order, 2, 1, 0, 0, None) == _lib.INVALID_ARGUMENT
+    assert lib.ring_allreduce(s, r, N, 100, 1, 9, order, 2, 1, 0, 0, None) == _lib.INVALID_ARGUMENT
+    assert lib.ring_allreduce(s, r, N, 100, 1, 0, order, 2, 1, 0, 8, None) == _lib.INVALID_ARGUMENT
+    # nothing to move: success without touching the device
+    assert lib.ring_allreduce(None, None, N, 0, 1, 0, order, 2, 1, 0, 0, None) == _lib.SUCCESS
+
+
+def test_group_discard_rejects_null():
+    lib = _lib.load()
+    assert lib.rar_group_discard(None) == _lib.INVALID_ARGUMENT
+
+
+def test_group_context_discards_on_error(monkeypatch):
+    """Comm.group(): a body that raises drops the queued calls (the C call
+    rar_group_discard) and launches nothing; the body's exception is the one
+    that propagates.  Checked against a stand-in library that records calls."""
+    calls = []
+
+    class FakeLib:
+        def rar_group_start(self, h):
+            calls.append("start")
+            return 0
+
+        def rar_group_end(self, h, s):
+            calls.append("end")
+            return 0
+
+        def rar_group_discard(self, h):
+            calls.append("discard")
+            return 0
+
+    monkeypatch.setattr(_lib, "load", lambda: FakeLib())
+    monkeypatch.setattr(rar, "_stream_handle", lambda s: None)
+    c = rar.Comm.__new__(rar.Comm)
+    c._h = ctypes.c_void_p(1)
+    with pytest.raises(KeyError):
+        with c.group():
+            raise KeyError("queueing failed")
+    assert calls == ["start", "discard"]
+    calls.clear()
+    with c.group():
+        pass
+    assert calls == ["start", "end"]
+    c._h = None
