@@ -280,6 +280,31 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
                             const int* ring_order, rar_proto_t proto, int nchannels,
                             size_t buff_size, int chunk_steps, void* stream);
 
+/* For callers that cannot allocate device memory (code that runs under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * ring_allreduce with the same arguments and the same results, bit for bit,
+ * that keeps no communicator.  Its device state (FIFOs, step counters, abort
+ * words, workgroup map, ring table) lives in one static device array of
+ * 64 MiB per GPU, which the library holds from its first use on that GPU
+ * until the process ends.  Each call lays the state out afresh (a small
+ * set-up kernel clears what must start at zero, then the ring kernel runs),
+ * so no call depends on an earlier one; the call makes no hipMalloc,
+ * hipFree or memset and copies nothing to the device.  Shapes whose state
+ * exceeds 64 MiB (N * nchannels * buff_size for the FIFOs, plus under 1 MiB)
+ * fail with RAR_INVALID_ARGUMENT, and a launch plan larger than the 3,584
+ * bytes that travel inside the kernel arguments with RAR_UNSUPPORTED.
+ * Every call on one GPU shares that GPU's array: calls that can overlap in
+ * time on one GPU (other streams, other threads) race and corrupt each
+ * other; issue them in order on one stream.  A cooperative launch, or a
+ * plain one while the stream is being captured (the grid fits the device at
+ * once, checked).  The wait watchdog still bounds every wait, but with no
+ * host-mapped word it cannot report an abort: the call's outputs are then
+ * undefined.  Errors as for ring_allreduce. */
+rar_result_t ring_allreduce_noalloc(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                    size_t count, rar_dtype_t dtype, rar_redop_t op,
+                                    const int* ring_order, rar_proto_t proto, int nchannels,
+                                    size_t buff_size, int chunk_steps, void* stream);
+
 /* One-shot AllReduce [C2 "5 Symmetric Memory", "6.1 LSA": with every rank's
  * buffer reachable by plain loads, one kernel finishes the reduction in one
  * hop instead of the ring's 2(N-1)].  Afterwards every recvbufs[r][i] holds

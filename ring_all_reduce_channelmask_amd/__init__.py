@@ -16,7 +16,7 @@ import ctypes
 from . import _lib
 from ._lib import RarError  # noqa: F401
 
-__all__ = ["Comm", "ring_allreduce", "oneshot_allreduce", "ring_info", "plan_pieces", "RarError"]
+__all__ = ["Comm", "ring_allreduce", "ring_allreduce_noalloc", "oneshot_allreduce", "ring_info", "plan_pieces", "RarError"]
 
 
 def _dtype_name(t):
@@ -183,6 +183,18 @@ def ring_allreduce(sends, recvs, ring_order, proto="SIMPLE", nchannels=1, buff_s
     _lib.check(lib.ring_allreduce(_ptr_array(sends), _ptr_array(recvs), nranks, n,
                                   _lib.DTYPE[dt], _lib.RED[op], order, _lib.PROTO[proto], nchannels,
                                   buff_size, chunk_steps, _stream_handle(stream)))
+
+
+def ring_allreduce_noalloc(sends, recvs, ring_order, proto="SIMPLE", nchannels=1, buff_size=0,
+                           chunk_steps=0, stream=None, op="sum"):
+    """ring_allreduce with its device state in the library's static array:
+    no device allocation (see include/rar.h for the size limit)."""
+    nranks = len(sends)
+    n, dt = _check_tensors(sends, recvs, nranks)
+    order = (ctypes.c_int * nranks)(*ring_order)
+    _lib.check(_lib.load().ring_allreduce_noalloc(
+        _ptr_array(sends), _ptr_array(recvs), nranks, n, _lib.DTYPE[dt], _lib.RED[op], order,
+        _lib.PROTO[proto], nchannels, buff_size, chunk_steps, _stream_handle(stream)))
 
 
 def oneshot_allreduce(sends, recvs=None, workgroups=0, waves=0, unroll=0, stream=None, op="sum",

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "librar.so")
 SOURCES = ["csrc/ring_kernel_i32.hip", "csrc/ring_kernel_f32.hip", "csrc/ring_kernel_bf16.hip",
-           "csrc/oneshot_kernel.hip", "csrc/plan.cpp", "csrc/capi.cpp"]
+           "csrc/oneshot_kernel.hip", "csrc/plan.cpp", "csrc/capi.cpp", "csrc/noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
