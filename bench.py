@@ -87,8 +87,12 @@ class HipEvent:
         return ms.value
 
     def __del__(self):
-        if HipEvent._hip is not None and self._e:
-            HipEvent._hip.hipEventDestroy(self._e)
+        hip = getattr(type(self), "_hip", None)
+        if hip is not None and self._e:
+            try:
+                hip.hipEventDestroy(self._e)
+            except Exception:  # interpreter shutdown: the runtime may be gone
+                pass
 
 
 def kernel_fingerprint(algo="ring") -> str:

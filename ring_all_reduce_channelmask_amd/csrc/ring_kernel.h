@@ -299,7 +299,7 @@ __device__ __forceinline__ bool should_stop(Ctx& cx, uint64_t t0) {
 // Spin until *p >= want (relaxed reads; the caller issues any acquire fence).
 // `cache` keeps the last value read [C23 "Simple 的 Credit 与 Step": the wait
 // loop reloads connStepCache only while it is short of the desired step].
-__device__ bool wait_cached(const uint64_t* p, uint64_t want, uint64_t& cache, Ctx& cx) {
+__device__ __forceinline__ bool wait_cached(const uint64_t* p, uint64_t want, uint64_t& cache, Ctx& cx) {
   if (cache >= want) return true;
   cache = load_relaxed(p);
   if (cache >= want) return true;
@@ -500,7 +500,7 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
 // of the last wave) [C23 "Primitive API 是模板组合", "Simple 的线程角色",
 // "发布顺序与 Fence", "Slice Size"].  Empty slices still wait and post.
 template <class Ty, int OP>
-__device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
+__device__ __forceinline__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
                             typename Ty::S* next_dst, const typename Ty::S* prev_src, bool raw,
                             int64_t nelem, int chunk) {
   using S = typename Ty::S;
@@ -656,7 +656,7 @@ __device__ __forceinline__ void store_bytes8(uint8_t* p, uint64_t v, int64_t val
 }
 
 template <class Ty, int OP>
-__device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
+__device__ __forceinline__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
                         int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
@@ -771,6 +771,21 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
 #define RAR_LL128_UNROLL 2
 #endif
 constexpr int kLl128Unroll = RAR_LL128_UNROLL;  // groups of 8 lines in flight per wave
+// How many iterations of a wave's whole-group loop its flags trail the data
+// (0, 1 or 2); timing only.
+#ifndef RAR_LL128_FLAG_LAG
+#define RAR_LL128_FLAG_LAG 0
+#endif
+
+// Wait until at most K of this wave's vector memory operations are
+// outstanding.  The counter retires them in the order they were issued, so
+// every operation issued before the last K has completed.  The asm is also
+// a compiler barrier: no memory access moves across it.
+template <int K>
+__device__ __forceinline__ void wait_vmem_below() {
+  static_assert(K >= 0 && K <= 63, "vmcnt holds 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory");
+}
 
 // Orders this wave's LDS accesses around a hand-off between its lanes.  The
 // fences cover LDS only ("local"): a fence over all address spaces would also
@@ -797,7 +812,7 @@ __device__ __forceinline__ void store_bytes16(uint8_t* p, v4u v, int64_t valid, 
 }
 
 template <class Ty, int OP>
-__device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
+__device__ __forceinline__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
                            int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
@@ -983,26 +998,76 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
       const std::integral_constant<bool, true> kW{};
       const std::integral_constant<bool, false> kP{};
       const int64_t gstep = (int64_t)U * stride;
+      // Flags to a receiver on this XCD go out while the step is still
+      // being written, kLag iterations behind the data (iteration i = the
+      // U groups at first + i * gstep).  Whole-group iterations issue, in
+      // program order, L(i+1) (kLoads loads) and then S(i) (kStores
+      // stores).  The wait before a flag counts only operations that
+      // program order puts after that iteration's stores and that no
+      // compiler reordering can remove: with lag 2, at the start of
+      // iteration i at least L(i), S(i-1) (and L(i+1) unless i is the last)
+      // follow S(i-2), so at most kStores + kLoads outstanding retires it;
+      // with lag 1, L(i+1) follows S(i-1), or nothing does in the last
+      // iteration; with lag 0 the wait is for everything.  The vector memory
+      // counter retires operations in issue order, and spills or anything
+      // else the compiler interleaves only add operations.  A flag then
+      // lands in L2 after its line's data, and soon enough to merge with
+      // the line while it is still there (a flag stored after the whole
+      // step found most half-lines written back already, and they went to
+      // memory twice).  Other flags, and every flag to a receiver on
+      // another XCD, follow the drain at the end of the step.
+      constexpr int kLag = RAR_LL128_FLAG_LAG;
+      constexpr int kLoads = U * ((O::kRecv ? 1 : 0) + (O::kSrc ? 1 : 0));
+      constexpr int kStores = U * ((O::kSend ? 1 : 0) + (O::kDst ? 1 : 0));
+      // outstanding operations allowed at the start of an iteration, when
+      // the next iteration's loads were issued (kMid) or not (kLast)
+      constexpr int kMid = kLag == 2 ? kStores + kLoads : kLag == 1 ? kLoads : 0;
+      constexpr int kLast = kLag == 2 ? kStores + kLoads : 0;
+      const bool early = O::kSend && __builtin_amdgcn_readfirstlane(cx.local_send ? 1 : 0) != 0;
+      int64_t pub = first;  // first group of the oldest iteration whose flags are not out
+      // flags of iteration `pub` once the iteration starting at g is kLag
+      // ahead of it
+      auto publish = [&](auto kWait, int64_t g) {
+        if (!early || g < pub + kLag * gstep) return;
+        wait_vmem_below<decltype(kWait)::value>();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t j = pub + (int64_t)u * stride + sub;
+          if (k == 7) store_relaxed_xcd(sl + 16 * j + 15, sflag);
+        }
+        pub += gstep;
+      };
+      const std::integral_constant<int, kMid> kWaitMid{};
+      const std::integral_constant<int, kLast> kWaitLast{};
+      const std::integral_constant<int, 0> kWaitAll{};
       int64_t g0 = first;
       if (g0 < hi && whole(g0)) {
         v4u inA[U], xA[U], inB[U], xB[U];
         load_whole(g0, inA, xA);
         for (;;) {
           if (!(g0 + gstep < hi && whole(g0 + gstep))) {
+            if constexpr (kLag > 0) publish(kWaitLast, g0);
             process(kW, g0, inA, xA);
+            if constexpr (kLag == 0) publish(kWaitAll, g0 + gstep);
             g0 += gstep;
             break;
           }
           load_whole(g0 + gstep, inB, xB);
+          if constexpr (kLag > 0) publish(kWaitMid, g0);
           process(kW, g0, inA, xA);
+          if constexpr (kLag == 0) publish(kWaitAll, g0 + gstep);
           g0 += gstep;
           if (!(g0 + gstep < hi && whole(g0 + gstep))) {
+            if constexpr (kLag > 0) publish(kWaitLast, g0);
             process(kW, g0, inB, xB);
+            if constexpr (kLag == 0) publish(kWaitAll, g0 + gstep);
             g0 += gstep;
             break;
           }
           load_whole(g0 + gstep, inA, xA);
+          if constexpr (kLag > 0) publish(kWaitMid, g0);
           process(kW, g0, inB, xB);
+          if constexpr (kLag == 0) publish(kWaitAll, g0 + gstep);
           g0 += gstep;
         }
       }
@@ -1016,7 +1081,7 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
         // back when the receiver runs on another XCD
         drain_vmem();
         if (!cx.local_send) release_fence();
-        for (int64_t g = first; g < hi; g += stride) {
+        for (int64_t g = pub; g < hi; g += stride) {
           const int64_t j = g + sub;
           // to a receiver on this XCD the flag goes out at workgroup scope: it
           // merges into the line in L2 instead of being written through as
@@ -1065,7 +1130,7 @@ __device__ __forceinline__ void prim(Ctx& cx, const typename Ty::S* sendbuf, typ
 // chunk to alignUp(divUp(rem, N), 16 bytes); per loop the 2N-1 calls with
 // chunk indices in ring-position coordinates.
 template <class Ty, int PROTO>
-__device__ void run_ring(Ctx& cx, const DevWork& w) {
+__device__ __forceinline__ void run_ring(Ctx& cx, const DevWork& w) {
   using S = typename Ty::S;
   constexpr int kVec = 16 / sizeof(S);
   const int N = cx.nranks, ix = cx.ring_index;
@@ -1125,7 +1190,7 @@ struct Plan {
   const uint32_t* scalars;
 };
 
-__device__ void load_batch(Shmem& sh, const Plan& a, uint32_t b, int lid) {
+__device__ __forceinline__ void load_batch(Shmem& sh, const Plan& a, uint32_t b, int lid) {
   const DevBatch hdr = a.batches[b];
   const uint64_t bits = hdr.offset_bitset;
   if (lid == 0) {
