@@ -54,26 +54,35 @@ KERNEL_SRC = {"ring": os.path.join(CSRC, "ring_kernel.h"),
               "oneshot": os.path.join(CSRC, "oneshot_kernel.hip")}
 
 
+# hipEventDisableSystemFence: a timing-only event, recorded without the
+# system-scope fence (an L2 write-back and invalidation) that a default event
+# performs; measured on MI355X, default events between back-to-back short
+# launches added about 3.5 us of device time each.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
 class HipEvent:
     """A timing event recorded straight through the HIP runtime torch has
     loaded: recording costs about a microsecond of host time, against several
     for torch.cuda.Event, so per-launch events do not slow the launch loop of
-    short kernels."""
+    short kernels.  Timing only (no fence): the caller synchronizes the
+    device before it reads results."""
     _hip = None
 
-    def __init__(self):
+    def __init__(self, flags=HIP_EVENT_DISABLE_SYSTEM_FENCE):
         if HipEvent._hip is None:
             import torch  # noqa: F401  -- the runtime below is torch's
             hip = ctypes.CDLL("libamdhip64.so.7")
             hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
             hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                 ctypes.c_void_p]
             hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
             HipEvent._hip = hip
         self._e = ctypes.c_void_p()
-        if HipEvent._hip.hipEventCreate(ctypes.byref(self._e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self._e), flags) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
 
     def record(self, stream_handle):
         if HipEvent._hip.hipEventRecord(self._e, stream_handle) != 0:
@@ -141,23 +150,62 @@ def place(t, off):
     return v
 
 
+def cpu_threads():
+    """Host threads this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS where the environment sets it (a shared GPU machine grants
+    each GPU a share of its cores)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
 def cpu_baseline(w, xs, algo="ring", budget_s=12.0, max_runs=5):
     """The oracle, as it stands, on the same workload: the state-machine
-    simulator for the ring, the written-out fold for the one-shot."""
+    simulator for the ring (its channel-parallel mode, one thread per channel
+    up to the host threads available), the written-out fold for the one-shot.
+    Returns (median seconds, runs, threads used, outputs of the last run)."""
+    import numpy as np
+
     import oracle
     from oracle import oneshot
     times = []
+    threads = min(cpu_threads(), bin(w.mask).count("1")) if algo == "ring" else 1
+    outs = None
     t_all = time.perf_counter()
     while len(times) < max_runs and (time.perf_counter() - t_all) < budget_s:
         t0 = time.perf_counter()
         if algo == "ring":
-            rc, _, _, _ = oracle.allreduce(xs, list(w.ring_order), w.mask, w.proto, w.buff_size,
-                                           w.chunk_steps, w.dtype)
+            rc, outs, _, _ = oracle.allreduce(xs, list(w.ring_order), w.mask, w.proto, w.buff_size,
+                                              w.chunk_steps, w.dtype, threads=threads)
             assert rc == oracle.OK
         else:
-            oneshot.allreduce(xs[0], w.dtype)
+            outs = [np.broadcast_to(oneshot.allreduce(xs[0], w.dtype), xs[0].shape)]
         times.append(time.perf_counter() - t0)
-    return statistics.median(times), len(times)
+    return statistics.median(times), len(times), threads, outs
+
+
+def parity_with(outs, recvs, dtype):
+    """Every rank's receive buffer equals the oracle's output, bit for bit."""
+    import numpy as np
+    import torch
+    for want, got in zip(outs, recvs):
+        for r, t in enumerate(got):
+            g = t.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bfloat16" \
+                else t.cpu().numpy()
+            if not np.array_equal(np.ascontiguousarray(g).view(np.uint8),
+                                  np.ascontiguousarray(want[r]).view(np.uint8)):
+                return False
+    return True
+
+
+def spread(per):
+    """Median, mean and coefficient of variation of per-launch durations (s)."""
+    m = statistics.mean(per)
+    cv = statistics.pstdev(per) / m if len(per) > 1 and m > 0 else 0.0
+    return {"kernel_median_ms": round(statistics.median(per) * 1e3, 4),
+            "kernel_mean_ms": round(m * 1e3, 4), "kernel_cv": round(cv, 4), "runs": len(per)}
 
 
 def main():
@@ -284,23 +332,47 @@ def main():
         if b is not None:
             b.record(hstream)
 
+    grouped = len(xs) > 1
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if not grouped:
+        # The timed region: K launches back to back between one pair of
+        # events, so the step includes the gaps between launches and no
+        # per-launch event.
+        e0, e1 = HipEvent(), HipEvent()
+        t0 = time.perf_counter()
+        e0.record(hstream)
+        for _ in range(args.steps):
+            step()
+        e1.record(hstream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        t_step = e0.elapsed_time(e1) * 1e-3 / args.steps
+    else:
+        # A fused group is queued on the host call by call and launched by
+        # group_end: the step is that launch, bracketed by its own events
+        # (the queueing before it is host work, not timed).
+        ev = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for a, b in ev:
+            step(a, b)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        t_step = statistics.mean([a.elapsed_time(b) * 1e-3 for a, b in ev])
+    # The kernel pass, right after: K more launches, each between its own
+    # pair of timing-only events on the launch stream, give the kernel's
+    # duration per launch.  For a group, a sleep kernel keeps the device busy
+    # while the host queues the group, so the events see the launch alone.
     ev = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for a, b in ev:
+        if grouped and hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(1 << 21)  # about 1 ms of device clock cycles
         step(a, b)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     if comm.async_error() != 0:
         raise RuntimeError("the wait watchdog fired during the timed region")
     per = [a.elapsed_time(b) * 1e-3 for a, b in ev]            # seconds, one launch each
-    span = ev[0][0].elapsed_time(ev[-1][1]) * 1e-3
-    # a fused group's step is its launch; a single collective's step is the
-    # span over back-to-back launches (launch gaps included)
-    t_step = statistics.mean(per) if len(xs) > 1 else span / args.steps
     t_kernel = statistics.mean(per)
     if args.graph:
         # the same K steps captured into one HIP graph and replayed: the
@@ -394,21 +466,29 @@ def main():
             "alg_bytes_per_launch": alg_bytes,
             "kernel_ms": round(t_kernel * 1e3, 4),
         },
+        "stability": spread(per),
+        "parity": None,
         "kernel_sha": kernel_fingerprint(),
     }
     if not args.no_cpu_baseline:
-        t_cpu, runs = cpu_baseline(w, xs)
+        t_cpu, runs, threads, outs = cpu_baseline(w, xs)
         model, ncpu = cpu_info()
         out["cpu_baseline"] = {
             "value": round(metrics.busbw_gbps(M, t_cpu, N), 4),
             "unit": "GB/s",
-            "cores": 1,
+            "cores": threads,
             "kind": "oracle",
-            "sample": f"the whole {w.key} collective ({N} ranks x {M >> 20} MiB) in the "
-                      f"single-threaded C++ state-machine oracle, median of {runs} runs, "
-                      f"{t_cpu:.3f} s each; host {model}, {ncpu} CPUs visible",
+            "sample": f"the whole {w.key} collective ({N} ranks x {M >> 20} MiB) in the C++ "
+                      f"state-machine oracle, its channels on {threads} threads, median of "
+                      f"{runs} runs, {t_cpu:.3f} s each; host {model}, {ncpu} CPUs visible",
         }
+        # outside every timed region: the receive buffers of the last launch
+        # against the oracle's output for the same inputs
+        out["parity"] = parity_with(outs, recvs, w.dtype)
     print(json.dumps(out), flush=True)
+    if out["parity"] is False:
+        print("bench.py: the GPU result differs from the oracle's", file=sys.stderr)
+        sys.exit(1)
     comm.close()
 
 
@@ -456,17 +536,29 @@ def run_oneshot(args, w):
     ctune = comm_lib.OneshotTuning(tune.get("workgroups", 0), tune.get("waves", 0),
                                    tune.get("unroll", 0), 0)
     dcode = comm_lib.DTYPE[w.dtype]
-    ev = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(hstream)
+
+    def one():
         comm_lib.check(lib.rar_oneshot_allreduce(sarr, rarr, N, w.counts[0], dcode, comm_lib.SUM,
                                                  ctypes.byref(ctune), hstream))
-        b.record(hstream)
+
+    # timed region: K launches back to back between one pair of events
+    e0, e1 = HipEvent(), HipEvent()
+    t0 = time.perf_counter()
+    e0.record(hstream)
+    for _ in range(args.steps):
+        one()
+    e1.record(hstream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    t_step = e0.elapsed_time(e1) * 1e-3 / args.steps
+    # kernel pass: K more launches, each between its own timing-only events
+    ev = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(hstream)
+        one()
+        b.record(hstream)
+    torch.cuda.synchronize()
     per = [a.elapsed_time(b) * 1e-3 for a, b in ev]
-    t_step = ev[0][0].elapsed_time(ev[-1][1]) * 1e-3 / args.steps
     t_kernel = statistics.mean(per)
     ref = recvs[0].view(torch.int16) if w.dtype == "bfloat16" else recvs[0]
     for t in recvs[1:]:
@@ -515,11 +607,14 @@ def run_oneshot(args, w):
             "alg_bytes_per_launch": alg_bytes,
             "kernel_ms": round(t_kernel * 1e3, 4),
         },
+        "stability": spread(per),
+        "parity": None,
         "kernel_sha": kernel_fingerprint("oneshot"),
     }
     if not args.no_cpu_baseline:
-        t_cpu, runs = cpu_baseline(w, xs, algo="oneshot")
+        t_cpu, runs, _, outs = cpu_baseline(w, xs, algo="oneshot")
         model, ncpu = cpu_info()
+        out["parity"] = parity_with(outs, [recvs], w.dtype)
         out["cpu_baseline"] = {
             "value": round(metrics.busbw_gbps(M, t_cpu, N), 4),
             "unit": "GB/s",
@@ -530,6 +625,9 @@ def run_oneshot(args, w):
                       f"{ncpu} CPUs visible",
         }
     print(json.dumps(out), flush=True)
+    if out["parity"] is False:
+        print("bench.py: the GPU result differs from the oracle's", file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -157,14 +157,17 @@ def geometry(nranks, mask, proto, buff_size, chunk_steps, dtype, counts):
 def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
               in_place=False, slots=8, sched=0, seed=0, drop_recv_head=False,
               direct=False, log_calls=False, op="sum", ll_wrap8=False, direct_read=False,
-              scalars=None):
+              scalars=None, threads=None):
     """Run the simulator.
 
     ``inputs`` is a list over works of arrays shaped [N, count] holding the raw
     elements (int32, float32, or uint16 bit patterns for bfloat16).
     ``ring_order`` is one ring, or a list of rings (channel id c runs ring
     c mod len(rings)).  ``op="premulsum"`` needs ``scalars``, an array
-    [works, N] of payload-type elements (rank r's scalar for work w).  Returns
+    [works, N] of payload-type elements (rank r's scalar for work w).
+    ``threads``: run the channels in parallel on that many threads (0 = one
+    per hardware thread), each channel with the round-robin schedule; the
+    outputs are those of any interleaving.  Returns
     (rc, outputs, stats, calls): outputs is a list over works of [N, count]
     arrays in the same representation.
     """
@@ -195,6 +198,9 @@ def allreduce(inputs, ring_order, mask, proto, buff_size, chunk_steps, dtype, *,
     if log_calls:
         cap = 1 << 20
         log = (Call * cap)()
+    if threads is not None:
+        assert not log_calls, "the channel-parallel mode keeps no call log"
+        sched, seed = 2, int(threads)
     options = (1 if drop_recv_head else 0) | (2 if direct else 0) | (4 if ll_wrap8 else 0) | \
         (16 if direct_read else 0) | (RED[op] << 8)
     flat = [r for ring in rings for r in ring]

@@ -15,7 +15,7 @@ SRC = os.path.join(HERE, "ring_sim.cpp")
 def build(verbose: bool = False) -> str:
     cmd = [
         "g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-fno-fast-math",
-        "-ffp-contract=off", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC,
+        "-ffp-contract=off", "-pthread", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC,
     ]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -17,6 +17,7 @@
 #include <cmath>
 #include <cstring>
 #include <random>
+#include <thread>
 #include <vector>
 
 namespace {
@@ -393,7 +394,10 @@ struct Sim {
   /* One unit = one slice (Simple) or one step (LL, LL128) of a primitive call:
    * wait -> reduce/copy -> publish [C23 "Primitive API 是模板组合", "Simple 的
    * Credit 与 Step", "发布顺序与 Fence"].  Returns false when a wait fails. */
-  bool try_unit(Agent& ag) {
+  bool try_unit(Agent& ag) { return try_unit(ag, stats); }
+  // `st`: where this unit's counts go (each thread of the channel-parallel
+  // mode has its own, merged at the end)
+  bool try_unit(Agent& ag, orc_stats* st) {
     const Unit& u = ag.prog[ag.pc];
     const bool recv = u.op != ORC_OP_SEND;
     const bool send = u.op != ORC_OP_RECV;
@@ -479,22 +483,22 @@ struct Sim {
       ag.send_step += adv;
       if (proto == ORC_PROTO_SIMPLE) sc.tail = ag.send_step;
     }
-    if (stats) {
-      stats->units_run++;
+    if (st) {
+      st->units_run++;
       if (u.first_of_call) {
-        if (send) stats->send_ops[ag.rank]++;
-        if (recv) stats->recv_ops[ag.rank]++;
+        if (send) st->send_ops[ag.rank]++;
+        if (recv) st->recv_ops[ag.rank]++;
       }
       if (send) {
-        stats->payload_sent[ag.rank] += u.nelem * es;
+        st->payload_sent[ag.rank] += u.nelem * es;
         if (proto == ORC_PROTO_SIMPLE) {
-          if (!direct_send && !skip_send) stats->wire_sent[ag.rank] += u.nelem * es;  // FIFO bytes
+          if (!direct_send && !skip_send) st->wire_sent[ag.rank] += u.nelem * es;  // FIFO bytes
         }
-        else if (proto == ORC_PROTO_LL) stats->wire_sent[ag.rank] += lines_for(u.nelem) * 16;
-        else stats->wire_sent[ag.rank] += lines_for(u.nelem) * 128;
+        else if (proto == ORC_PROTO_LL) st->wire_sent[ag.rank] += lines_for(u.nelem) * 16;
+        else st->wire_sent[ag.rank] += lines_for(u.nelem) * 128;
       }
-      if (u.first_of_call && log && stats->calls_recorded < log_cap) {
-        orc_call& c = log[stats->calls_recorded++];
+      if (u.first_of_call && log && st->calls_recorded < log_cap) {
+        orc_call& c = log[st->calls_recorded++];
         c.rank = ag.rank;
         c.channel_id = channel_ids[ag.n];
         c.work = u.work;
@@ -719,7 +723,73 @@ int orc_allreduce_premul(int nranks, int nrings, const int* ring_orders, uint64_
         return;
       }
   };
-  if (sched == 0) {
+  if (sched == 2) {
+    // Channel-parallel: channels share no connector, no agent and no output
+    // element, so each thread runs whole channels (n = t, t + T, ...) with
+    // the round-robin schedule below restricted to that channel's agents,
+    // counting into its own statistics.  The results are those of any other
+    // interleaving.
+    if (call_log) return ORC_INVALID;
+    const int hw = (int)std::thread::hardware_concurrency();
+    int T = seed ? (int)seed : (hw > 0 ? hw : 1);
+    if (T > sim.C) T = sim.C;
+    std::vector<orc_stats> tstats((size_t)T);
+    std::vector<int> rcode((size_t)T, ORC_OK);
+    std::vector<int> stuck((size_t)T, -1);  // an agent index of a deadlocked channel
+    auto run_channels = [&](int t) {
+      orc_stats* st = stats ? &tstats[(size_t)t] : nullptr;
+      if (st) std::memset(st, 0, sizeof(*st));
+      for (int n = t; n < sim.C; n += T) {
+        while (true) {
+          bool progress = false, all_done = true;
+          for (int r = 0; r < nranks; ++r) {
+            Agent& ag = agents[(size_t)r * sim.C + n];
+            while (ag.pc < ag.prog.size() && sim.try_unit(ag, st)) {
+              ++ag.pc;
+              progress = true;
+            }
+            if (ag.pc < ag.prog.size()) all_done = false;
+          }
+          if (all_done) break;
+          if (!progress) {
+            rcode[(size_t)t] = ORC_DEADLOCK;
+            for (int r = 0; r < nranks; ++r)
+              if (agents[(size_t)r * sim.C + n].pc < agents[(size_t)r * sim.C + n].prog.size()) {
+                stuck[(size_t)t] = r * sim.C + n;
+                break;
+              }
+            return;
+          }
+        }
+      }
+    };
+    std::vector<std::thread> pool;
+    for (int t = 1; t < T; ++t) pool.emplace_back(run_channels, t);
+    run_channels(0);
+    for (std::thread& th : pool) th.join();
+    if (stats) {
+      for (const orc_stats& ts : tstats) {
+        stats->units_run += ts.units_run;
+        for (int r = 0; r < 64; ++r) {
+          stats->send_ops[r] += ts.send_ops[r];
+          stats->recv_ops[r] += ts.recv_ops[r];
+          stats->payload_sent[r] += ts.payload_sent[r];
+          stats->wire_sent[r] += ts.wire_sent[r];
+        }
+      }
+    }
+    for (int t = 0; t < T; ++t)
+      if (rcode[(size_t)t] != ORC_OK) {
+        if (stats && stuck[(size_t)t] >= 0) {
+          const Agent& ag = agents[(size_t)stuck[(size_t)t]];
+          stats->deadlock_rank = ag.rank;
+          stats->deadlock_channel = sim.channel_ids[ag.n];
+          stats->deadlock_send_step = (int64_t)ag.send_step;
+          stats->deadlock_recv_step = (int64_t)ag.recv_step;
+        }
+        return rcode[(size_t)t];
+      }
+  } else if (sched == 0) {
     // Deterministic: visit agents round robin; each runs until it blocks.
     while (true) {
       bool progress = false, all_done = true;

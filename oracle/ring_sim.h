@@ -122,6 +122,11 @@ typedef struct {
  *   slots               : FIFO slots per connector (NCCL_STEPS, normally 8)
  *   sched               : 0 = round robin, each agent runs until it blocks
  *                          1 = seeded random choice of agent, one unit at a time
+ *                          2 = channel-parallel: channels share no connector or
+ *                              output element, so `seed` threads (0 = the
+ *                              hardware's count, at most one per channel) run
+ *                              whole channels, each with the round-robin
+ *                              schedule; call_log must be NULL
  *   options             : ORC_OPT_* bits
  *   call_log            : optional, records every primitive call (may be NULL)
  */

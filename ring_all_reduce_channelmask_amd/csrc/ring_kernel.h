@@ -299,7 +299,7 @@ __device__ __forceinline__ bool should_stop(Ctx& cx, uint64_t t0) {
 // Spin until *p >= want (relaxed reads; the caller issues any acquire fence).
 // `cache` keeps the last value read [C23 "Simple 的 Credit 与 Step": the wait
 // loop reloads connStepCache only while it is short of the desired step].
-__device__ __forceinline__ bool wait_cached(const uint64_t* p, uint64_t want, uint64_t& cache, Ctx& cx) {
+__device__ bool wait_cached(const uint64_t* p, uint64_t want, uint64_t& cache, Ctx& cx) {
   if (cache >= want) return true;
   cache = load_relaxed(p);
   if (cache >= want) return true;
@@ -500,7 +500,7 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
 // of the last wave) [C23 "Primitive API 是模板组合", "Simple 的线程角色",
 // "发布顺序与 Fence", "Slice Size"].  Empty slices still wait and post.
 template <class Ty, int OP>
-__device__ __forceinline__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
+__device__ void simple_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
                             typename Ty::S* next_dst, const typename Ty::S* prev_src, bool raw,
                             int64_t nelem, int chunk) {
   using S = typename Ty::S;
@@ -656,7 +656,7 @@ __device__ __forceinline__ void store_bytes8(uint8_t* p, uint64_t v, int64_t val
 }
 
 template <class Ty, int OP>
-__device__ __forceinline__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
+__device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
                         int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
@@ -812,7 +812,7 @@ __device__ __forceinline__ void store_bytes16(uint8_t* p, v4u v, int64_t valid, 
 }
 
 template <class Ty, int OP>
-__device__ __forceinline__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
+__device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst, int64_t nelem,
                            int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
@@ -1190,7 +1190,7 @@ struct Plan {
   const uint32_t* scalars;
 };
 
-__device__ __forceinline__ void load_batch(Shmem& sh, const Plan& a, uint32_t b, int lid) {
+__device__ void load_batch(Shmem& sh, const Plan& a, uint32_t b, int lid) {
   const DevBatch hdr = a.batches[b];
   const uint64_t bits = hdr.offset_bitset;
   if (lid == 0) {
