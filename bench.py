@@ -230,6 +230,11 @@ def main():
                     help="Simple direct variants: bit 0 write, bit 1 read")
     ap.add_argument("--deal-works", type=int, default=None, choices=[0, 1],
                     help="1: the lanes of a channel take its works in turn")
+    ap.add_argument("--strict-scope", type=int, default=None, choices=[0, 1],
+                    help="1: publish at agent scope with the release even to a receiver on the "
+                         "same XCD")
+    ap.add_argument("--waves-by-size", type=int, default=None, choices=[0, 1],
+                    help="1: each work runs on the waves its per-call data fills")
     ap.add_argument("--graph", action="store_true",
                     help="time the K steps as one captured HIP graph (kernel durations still "
                          "come from K eagerly launched steps)")
@@ -290,6 +295,10 @@ def main():
         tune["direct"] = args.direct
     if args.deal_works is not None:
         tune["deal_works"] = args.deal_works
+    if args.strict_scope is not None:
+        tune["strict_scope"] = args.strict_scope
+    if args.waves_by_size is not None:
+        tune["waves_by_size"] = args.waves_by_size
     torch.cuda.set_device(0)
     xs = workloads.inputs_for(w)
     N = w.nranks
@@ -451,6 +460,8 @@ def main():
             if tune.get("launch_mode", 0) == 1 else "cooperative",
             "misalign_elems": args.misalign,
             "direct": int(tune.get("direct", 0)),
+            "strict_scope": int(tune.get("strict_scope", 0)),
+            "waves_by_size": int(tune.get("waves_by_size", 0)),
         },
         "algbw_GBps": round(algbw, 3),
         "busbw_GBps": round(busbw, 3),

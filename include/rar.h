@@ -147,6 +147,29 @@ typedef struct {
                             the latency of its dependent steps, not by
                             bytes: dealing the works divides the steps each
                             workgroup runs in sequence.  Timing only    */
+  int strict_scope;      /* 0: to a receiver found on this XCD (placement 0),
+                            Simple tails, LL lines and LL128 flags are
+                            workgroup-scope stores into the L2 both sides
+                            share, which relies on this GPU's L1 being
+                            write-through to that L2 rather than on the
+                            formal memory model.  1: every publication takes
+                            the agent-scope path whatever the placement: a
+                            release (L2 write-back) before Simple tails and
+                            LL128 flags, agent-scope atomic stores for LL
+                            lines and flags [C23 "发布顺序与 Fence": the
+                            release before publishing].  The fallback should
+                            the same-L2 behaviour change; same results,
+                            slower                                       */
+  int waves_by_size;     /* 0: every work of a launch runs on waves_per_lane
+                            waves.  1: a work runs on as many waves as its
+                            per-call data fills with full passes (Simple
+                            4 KiB, LL 2 KiB, LL128 1,920 payload bytes per
+                            wave and pass), at least 1 and at most
+                            waves_per_lane, so the small pieces of a fused
+                            group use fewer waves and RunWorkBatch fences
+                            each change of the active wave count with a
+                            barrier [C23 "RunWorkBatch 与 Fused Work"].
+                            Timing only                                  */
 } rar_tuning_t;
 
 #define RAR_DEBUG_DROP_RECV_HEAD 1
@@ -371,6 +394,8 @@ typedef struct {
   uint32_t wait_ticks;   /* until the workgroup passed its wait             */
   uint32_t data_ticks;   /* moving data until the workgroup's last barrier  */
   uint64_t recv_step;    /* receive step at the start of the unit (low bits)*/
+  int32_t waves;         /* waves that moved the unit's data (its work's)   */
+  int32_t pad;
 } rar_trace_rec_t;
 rar_result_t rar_comm_read_trace(rar_comm_t comm, rar_trace_rec_t* out, size_t cap,
                                  size_t* written);

@@ -79,7 +79,7 @@ class Comm:
 
     def __init__(self, nranks, ring_order, mask, proto="SIMPLE", buff_size=0, chunk_steps=0,
                  lanes=0, waves=0, timeout_us=0, debug_flags=0, launch_mode=0, placement=0,
-                 slices_per_chunk=0, direct=0, deal_works=0):
+                 slices_per_chunk=0, direct=0, deal_works=0, strict_scope=0, waves_by_size=0):
         lib = _lib.load()
         rings = [list(r) for r in ring_order] if len(ring_order) and \
             isinstance(ring_order[0], (list, tuple)) else [list(ring_order)]
@@ -93,7 +93,7 @@ class Comm:
         flat = [r for ring in rings for r in ring]
         order = (ctypes.c_int * len(flat))(*flat)
         tune = _lib.Tuning(lanes, waves, timeout_us, debug_flags, launch_mode, placement,
-                           slices_per_chunk, direct, deal_works)
+                           slices_per_chunk, direct, deal_works, strict_scope, waves_by_size)
         h = ctypes.c_void_p()
         _lib.check(lib.rar_comm_create_rings(ctypes.byref(h), nranks, len(rings), order, mask,
                                              _lib.PROTO[proto], buff_size, chunk_steps,

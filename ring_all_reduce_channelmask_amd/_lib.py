@@ -22,7 +22,8 @@ class Tuning(ctypes.Structure):
                 ("spin_timeout_us", ctypes.c_int), ("debug_flags", ctypes.c_int),
                 ("launch_mode", ctypes.c_int), ("placement", ctypes.c_int),
                 ("slices_per_chunk", ctypes.c_int), ("direct", ctypes.c_int),
-                ("deal_works", ctypes.c_int)]
+                ("deal_works", ctypes.c_int), ("strict_scope", ctypes.c_int),
+                ("waves_by_size", ctypes.c_int)]
 
 
 class OneshotTuning(ctypes.Structure):
@@ -35,7 +36,7 @@ class TraceRec(ctypes.Structure):
                 ("lane", ctypes.c_int32), ("op", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("nelem", ctypes.c_uint32), ("t_begin", ctypes.c_uint64),
                 ("wait_ticks", ctypes.c_uint32), ("data_ticks", ctypes.c_uint32),
-                ("recv_step", ctypes.c_uint64)]
+                ("recv_step", ctypes.c_uint64), ("waves", ctypes.c_int32), ("pad", ctypes.c_int32)]
 
 
 class Piece(ctypes.Structure):

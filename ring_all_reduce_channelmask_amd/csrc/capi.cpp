@@ -92,6 +92,7 @@ struct rar_comm {
   std::vector<uint32_t> wgmap;
   int launch_mode = 0;
   int debug_flags = 0;
+  rar::WaveSizing sizing;  // per-work wave counts (waves_by_size)
   rar::TraceRec* d_trace = nullptr;
   uint64_t* d_placement = nullptr;
   uint32_t* d_wg_peer = nullptr;
@@ -173,14 +174,17 @@ rar_result_t check_rank_buffers(int nranks, const void* const* sendbufs, void* c
 
 
 PlanBlock build_plan_block(const std::vector<QueuedCall>& calls, int nranks, uint64_t mask, int proto,
-                           size_t buff, int chunk_steps, int n_channels, int n_waves) {
+                           size_t buff, int chunk_steps, int n_channels, int n_waves,
+                           const WaveSizing& sizing) {
   PlanBlock out;
   const int64_t es = elem_size(calls.front().dtype);
   std::vector<size_t> counts;
   for (const QueuedCall& q : calls) counts.push_back(q.count);
   const std::vector<Piece> pieces = split_channels(mask, proto, buff, chunk_steps, es, counts);
   if (pieces.empty()) return out;  // nothing to move
-  const BatchPlan plan = encode_batches(pieces, n_channels, n_waves);
+  WaveSizing sz = sizing;
+  sz.es = es;  // the launch's payload type
+  const BatchPlan plan = encode_batches(pieces, n_channels, n_waves, sz);
   auto align_to = [](size_t v, size_t a) { return (v + a - 1) / a * a; };
   const size_t off_batches = 0;
   const size_t off_works = align_to(off_batches + plan.batches.size() * sizeof(DevBatch), 64);
@@ -278,7 +282,7 @@ rar_result_t launch(rar_comm* c, const std::vector<QueuedCall>& calls, hipStream
   plan_key(calls, &key);
   if (key != c->plan_key) {
     c->plan_cached = rar::build_plan_block(calls, c->nranks, c->mask, c->proto, c->buff, c->chunk_steps, c->C,
-                                           c->W);
+                                           c->W, c->sizing);
     c->plan_key.swap(key);
   }
   const rar::PlanBlock& pb = c->plan_cached;
@@ -437,7 +441,7 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
   for (int k = 0; k < nrings; ++k)
     if (!rar::build_ring(nranks, ring_orders + (size_t)k * nranks, &rings[k], &err))
       return fail(RAR_INVALID_ARGUMENT, "ring " + std::to_string(k) + ": " + err);
-  rar_tuning_t tune{0, 0, 0, 0, 0, 0, 0, 0, 0};
+  rar_tuning_t tune{};
   if (tuning) tune = *tuning;
   if (tune.lanes_per_channel < 0 || tune.lanes_per_channel > rar::kMaxLanes)
     return fail(RAR_INVALID_ARGUMENT, "lanes_per_channel must be in [0, 16]");
@@ -459,6 +463,10 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
     return fail(RAR_UNSUPPORTED, "the direct variant exists for the Simple protocol only");
   if (tune.deal_works != 0 && tune.deal_works != 1)
     return fail(RAR_INVALID_ARGUMENT, "deal_works must be 0 or 1");
+  if (tune.strict_scope != 0 && tune.strict_scope != 1)
+    return fail(RAR_INVALID_ARGUMENT, "strict_scope must be 0 or 1");
+  if (tune.waves_by_size != 0 && tune.waves_by_size != 1)
+    return fail(RAR_INVALID_ARGUMENT, "waves_by_size must be 0 or 1");
 
   int dev = 0;
   RAR_HIP(hipGetDevice(&dev));
@@ -486,6 +494,10 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
   c->wgmap = wg;
   c->launch_mode = tune.launch_mode;
   c->debug_flags = tune.debug_flags;
+  c->sizing.on = tune.waves_by_size != 0;
+  c->sizing.nranks = nranks;
+  c->sizing.proto = proto;
+  c->sizing.split_lanes = tune.deal_works ? 1 : c->P;
 
   // every workgroup must be resident at once: the ranks wait on each other
   for (int k = 0; k < 3 * rar::kNumRed; ++k) {
@@ -589,6 +601,7 @@ rar_result_t rar_comm_create_rings(rar_comm_t* out, int nranks, int nrings, cons
   hc.hot.slices_per_chunk = spc;
   hc.hot.direct = tune.direct;
   hc.hot.deal_works = tune.deal_works;
+  hc.hot.strict_scope = tune.strict_scope;
   hc.hot.step_per_slice = (int)proto == rar::kSimple ? chunk_steps / spc : 1;
   hc.hot.channel_mask = channel_mask;
   hc.hot.fifo = c->d_fifo;
@@ -872,6 +885,8 @@ rar_result_t rar_comm_read_trace(rar_comm_t c, rar_trace_rec_t* out, size_t cap,
       o.wait_ticks = buf[i].wait_ticks;
       o.data_ticks = buf[i].data_ticks;
       o.recv_step = buf[i].recv_step;
+      o.waves = (int32_t)buf[i].waves;
+      o.pad = 0;
     }
   }
   *written = k;

@@ -47,7 +47,8 @@ struct PlanBlock {
   uint32_t off_batches = 0, off_works = 0, off_ptrs = 0, off_scalars = 0, off_first = 0;
 };
 PlanBlock build_plan_block(const std::vector<QueuedCall>& calls, int nranks, uint64_t mask, int proto,
-                           size_t buff, int chunk_steps, int n_channels, int n_waves);
+                           size_t buff, int chunk_steps, int n_channels, int n_waves,
+                           const WaveSizing& sizing = WaveSizing());
 
 // The arguments shared by ring_allreduce and ring_allreduce_noalloc, checked
 // on the host in the same order by both: on success the channel mask, the

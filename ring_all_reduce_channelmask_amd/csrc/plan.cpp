@@ -146,7 +146,20 @@ std::vector<Piece> split_channels(uint64_t mask, int proto, size_t buff_size, in
   return pieces;
 }
 
-BatchPlan encode_batches(const std::vector<Piece>& pieces, int n_channels, int n_waves) {
+int work_waves(const Piece& p, int n_waves, const WaveSizing& sz) {
+  if (!sz.on) return n_waves;
+  // the chunk of the piece's first call: the protocol maximum, or the tail
+  // loop's re-chunked size when the piece is shorter than one loop
+  const int64_t vec = 16 / sz.es;
+  const int64_t loop = (int64_t)sz.nranks * p.chunk_count;
+  const int64_t cc = p.channel_count < loop ? align_up(div_up(p.channel_count, sz.nranks), vec) : p.chunk_count;
+  const int64_t bytes = div_up(cc * sz.es, sz.split_lanes);
+  const int64_t pass = sz.proto == kSimple ? 4096 : sz.proto == kLL ? 2048 : 1920;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(n_waves, div_up(bytes, pass)));
+}
+
+BatchPlan encode_batches(const std::vector<Piece>& pieces, int n_channels, int n_waves,
+                         const WaveSizing& sizing) {
   BatchPlan plan;
   plan.batches.push_back(DevBatch{0, 0, 0});  // sentinel: next_jump 0 means "no next"
   plan.first_batch.assign(kMaxChannels, 0);
@@ -170,7 +183,7 @@ BatchPlan encode_batches(const std::vector<Piece>& pieces, int n_channels, int n
         w.channel_count = p.channel_count;
         w.chunk_count = p.chunk_count;
         w.buf_index = (uint32_t)p.work;
-        w.n_waves = (uint16_t)n_waves;
+        w.n_waves = (uint16_t)work_waves(p, n_waves, sizing);
         plan.works.push_back(w);
       }
       const uint32_t idx = (uint32_t)plan.batches.size();

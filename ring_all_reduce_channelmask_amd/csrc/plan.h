@@ -58,8 +58,23 @@ struct BatchPlan {
 };
 
 // Pack each channel's pieces, in order, into batches of at most kBatchWorks
-// works (1024 bytes), chained by next_jump.
-BatchPlan encode_batches(const std::vector<Piece>& pieces, int n_channels, int n_waves);
+// works (1024 bytes), chained by next_jump.  Every work runs on n_waves
+// waves, or, with `sizing`, on the waves its per-call data fills (see
+// work_waves).
+struct WaveSizing {
+  bool on = false;
+  int nranks = 0;
+  int proto = 0;
+  int64_t es = 4;
+  int split_lanes = 1;  // workgroups that split one call (1 when works are dealt)
+};
+BatchPlan encode_batches(const std::vector<Piece>& pieces, int n_channels, int n_waves,
+                         const WaveSizing& sizing = WaveSizing());
+
+// Waves for a piece: the bytes one workgroup moves per call of the piece
+// (its first call's chunk, split over the workgroups of the channel) over
+// the bytes a wave moves per pass, rounded up, within [1, n_waves].
+int work_waves(const Piece& p, int n_waves, const WaveSizing& sizing);
 
 
 // Workgroup map: the N ranks of one (channel, lane) pipeline are placed on

@@ -78,7 +78,7 @@ struct alignas(16) TraceRec {
   uint32_t recv_step;   // low bits of the receive step at the unit
   uint16_t op, chunk;
   uint32_t nelem;       // elements of the unit (all lanes together)
-  uint32_t pad;
+  uint32_t waves;       // waves that moved data for the unit's work
 };
 static_assert(sizeof(TraceRec) == 32, "trace record layout");
 
@@ -119,6 +119,9 @@ struct alignas(16) DevCommHot {
   const uint32_t* wg_peer;     // [grid] -> workgroup that receives from this one
   uint32_t ll_flag_mask;       // LL flag period - 1 (0xFFFFFFFF, or 0xFF in the wrap test mode)
   int32_t deal_works;          // 1: work k of a channel runs whole on lane k mod n_lanes
+  int32_t strict_scope;        // 1: publish at agent scope with the release even to a
+                               // receiver on this XCD (the placement check is ignored)
+  int32_t pad_hot[3];
 };
 static_assert(sizeof(DevCommHot) % 16 == 0, "hot fields are copied in 16-byte packs");
 

@@ -273,7 +273,7 @@ __device__ __forceinline__ void trace_unit(Ctx& cx, int op, int chunk, int64_t n
     r.op = (uint16_t)op;
     r.chunk = (uint16_t)chunk;
     r.nelem = (uint32_t)nelem;
-    r.pad = 0;
+    r.waves = (uint32_t)(cx.workers / kWaveSize);
     cx.trace[cx.trace_n++] = r;
   }
 }
@@ -1319,7 +1319,8 @@ ring_allreduce_kernel(KernelArgs args) {
       }
     }
     if (ok) {
-      sh.local_send = (v & 0xFFu) == my_xcc;
+      // strict scope: every publication takes the agent-scope path
+      sh.local_send = (v & 0xFFu) == my_xcc && !comm->hot.strict_scope;
     } else {
       // the receiving workgroup never arrived (or another waiter gave up):
       // raise the communicator's abort word, as every bounded wait does
