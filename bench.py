@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 # (which fits the device at once) is resident without the cooperative-launch
 # guarantee, and consecutive launches are ~20 us closer together.
 TUNING = {
-    "simple_64m": dict(lanes=5, waves=8, launch_mode=1),
+    "simple_64m": dict(lanes=10, waves=4, launch_mode=1),
     "ll128_64m": dict(lanes=16, waves=4, launch_mode=1),
     "bf16_n8": dict(lanes=2, waves=8, launch_mode=1),
     "int32_n8": dict(lanes=2, waves=8, launch_mode=1),
@@ -208,6 +208,134 @@ def spread(per):
             "kernel_mean_ms": round(m * 1e3, 4), "kernel_cv": round(cv, 4), "runs": len(per)}
 
 
+class RingRun:
+    """One ring workload set up for timing: device inputs and outputs, the
+    communicator, and arguments marshalled once, so that the timed loops call
+    the C entry point directly and the events bracket launches, not Python's
+    checks."""
+
+    def __init__(self, w, tune, misalign=0):
+        import numpy as np
+        import torch
+
+        import ring_all_reduce_channelmask_amd as rar
+        from ring_all_reduce_channelmask_amd import _lib as comm_lib
+        from ring_all_reduce_channelmask_amd import workloads
+
+        self.w, self.cl = w, comm_lib
+        self.xs = workloads.inputs_for(w)
+        N = w.nranks
+
+        def dev(a):
+            if w.dtype == "bfloat16":
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+            return torch.from_numpy(a).cuda()
+
+        self.sends = [[place(dev(x[r]), misalign) for r in range(N)] for x in self.xs]
+        self.recvs = [[place(torch.empty_like(t), misalign) for t in s] for s in self.sends]
+        self.comm = rar.Comm(N, list(w.ring_order), w.mask, proto=w.proto, buff_size=w.buff_size,
+                             chunk_steps=w.chunk_steps if w.proto == "SIMPLE" else 0, **tune)
+        self.lib = comm_lib.load()
+        self.sarr = (ctypes.c_void_p * N)(*[t.data_ptr() for t in self.sends[0]])
+        self.rarr = (ctypes.c_void_p * N)(*[t.data_ptr() for t in self.recvs[0]])
+        self.hstream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.dcode = comm_lib.DTYPE[w.dtype]
+        self.grouped = len(self.xs) > 1
+
+    def step(self, a=None, b=None):
+        # A group is queued on the host and launched by group_end; the events
+        # bracket the launch only, so host-side queueing is not timed as GPU work.
+        cl, lib, hs = self.cl, self.lib, self.hstream
+        if not self.grouped:
+            if a is not None:
+                a.record(hs)
+            cl.check(lib.rar_allreduce(self.comm.handle, self.sarr, self.rarr, self.w.counts[0],
+                                       self.dcode, cl.SUM, hs))
+        else:
+            cl.check(lib.rar_group_start(self.comm.handle))
+            for s, r in zip(self.sends, self.recvs):
+                self.comm.allreduce(s, r)
+            if a is not None:
+                a.record(hs)
+            cl.check(lib.rar_group_end(self.comm.handle, hs))
+        if b is not None:
+            b.record(hs)
+
+    def warm(self, n):
+        import torch
+        for _ in range(n):
+            self.step()
+        torch.cuda.synchronize()
+
+    def timed(self, steps):
+        """The timed region: (seconds per step, wall seconds).  K launches back
+        to back between one pair of events, so the step includes the gaps
+        between launches and no per-launch event.  A fused group is queued on
+        the host call by call and launched by group_end: its step is that
+        launch, bracketed by its own events (the queueing is host work)."""
+        import torch
+        if not self.grouped:
+            e0, e1 = HipEvent(), HipEvent()
+            t0 = time.perf_counter()
+            e0.record(self.hstream)
+            for _ in range(steps):
+                self.step()
+            e1.record(self.hstream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e-3 / steps, time.perf_counter() - t0
+        ev = [(HipEvent(), HipEvent()) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for a, b in ev:
+            self.step(a, b)
+        torch.cuda.synchronize()
+        return statistics.mean([a.elapsed_time(b) * 1e-3 for a, b in ev]), time.perf_counter() - t0
+
+    def kernel_pass(self, steps):
+        """K more launches, each between its own pair of timing-only events on
+        the launch stream: the kernel's duration per launch (seconds).  For a
+        group, a sleep kernel keeps the device busy while the host queues the
+        group, so the events see the launch alone."""
+        import torch
+        ev = [(HipEvent(), HipEvent()) for _ in range(steps)]
+        for a, b in ev:
+            if self.grouped and hasattr(torch.cuda, "_sleep"):
+                torch.cuda._sleep(1 << 21)  # about 1 ms of device clock cycles
+            self.step(a, b)
+        torch.cuda.synchronize()
+        if self.comm.async_error() != 0:
+            raise RuntimeError("the wait watchdog fired during the timed region")
+        return [a.elapsed_time(b) * 1e-3 for a, b in ev]
+
+
+def sweep(args):
+    """Every ring workload in its benchmark shape, visited in forward and then
+    reverse order [C12 "正确性与稳定性": replicates in forward and reverse
+    configuration order, each group's CV at most 5 %].  One JSON line per
+    workload: the step and kernel figures of both visits and whether every
+    visit's kernel CV stays within 5 %."""
+    import torch
+
+    from ring_all_reduce_channelmask_amd import workloads
+    torch.cuda.set_device(0)
+    keys = [k for k in workloads.WORKLOADS]
+    runs = {k: RingRun(workloads.WORKLOADS[k], dict(TUNING.get(k, {}))) for k in keys}
+    visits = {k: [] for k in keys}
+    for order in (keys, list(reversed(keys))):
+        for k in order:
+            r = runs[k]
+            r.warm(args.warmup)
+            t_step, _ = r.timed(args.steps)
+            per = r.kernel_pass(args.steps)
+            visits[k].append({"step_ms": round(t_step * 1e3, 4), **spread(per)})
+    for k in keys:
+        v = visits[k]
+        print(json.dumps({"workload": k, "forward": v[0], "reverse": v[1],
+                          "cv_within_5pct": all(x["kernel_cv"] <= 0.05 for x in v),
+                          "reverse_vs_forward_kernel": round(v[1]["kernel_median_ms"] /
+                                                             v[0]["kernel_median_ms"], 4)}),
+              flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +367,9 @@ def main():
                     help="time the K steps as one captured HIP graph (kernel durations still "
                          "come from K eagerly launched steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="every ring workload, forward then reverse order, one JSON line each "
+                         "(step, kernel median and CV per visit); not the benchmark line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the AllReduce, time a plain device copy of MIB MiB "
                          "(used to calibrate the HBM byte counters)")
@@ -276,6 +407,9 @@ def main():
                           "GBps_read_plus_write": round(2 * n * 4 / t / 1e9, 1)}), flush=True)
         return
 
+    if args.sweep:
+        sweep(args)
+        return
     w = workloads.WORKLOADS[args.workload]
     if args.algo == "oneshot":
         run_oneshot(args, w)
@@ -300,88 +434,13 @@ def main():
     if args.waves_by_size is not None:
         tune["waves_by_size"] = args.waves_by_size
     torch.cuda.set_device(0)
-    xs = workloads.inputs_for(w)
-    N = w.nranks
-
-    def dev(a):
-        if w.dtype == "bfloat16":
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(a).cuda()
-
-    sends = [[place(dev(x[r]), args.misalign) for r in range(N)] for x in xs]
-    recvs = [[place(torch.empty_like(t), args.misalign) for t in s] for s in sends]
-    comm = rar.Comm(N, list(w.ring_order), w.mask, proto=w.proto, buff_size=w.buff_size,
-                    chunk_steps=w.chunk_steps if w.proto == "SIMPLE" else 0, **tune)
+    run = RingRun(w, tune, args.misalign)
+    xs, N, comm, sends, recvs = run.xs, w.nranks, run.comm, run.sends, run.recvs
     shape = comm.shape()
-
-    stream = torch.cuda.current_stream()  # the stream every launch goes to
-    lib = comm_lib.load()
-    # Arguments are marshalled once; the timed loop calls the C entry point
-    # directly, so the events bracket the launch and not Python's checks.
-    sarr = (ctypes.c_void_p * N)(*[t.data_ptr() for t in sends[0]])
-    rarr = (ctypes.c_void_p * N)(*[t.data_ptr() for t in recvs[0]])
-    hstream = ctypes.c_void_p(stream.cuda_stream)
-    dcode = comm_lib.DTYPE[w.dtype]
-
-    def step(a=None, b=None):
-        # A group is queued on the host and launched by group_end; the events
-        # bracket the launch only, so host-side queueing is not timed as GPU work.
-        if len(xs) == 1:
-            if a is not None:
-                a.record(hstream)
-            comm_lib.check(lib.rar_allreduce(comm.handle, sarr, rarr, w.counts[0], dcode,
-                                             comm_lib.SUM, hstream))
-        else:
-            comm_lib.check(comm_lib.load().rar_group_start(comm.handle))
-            for s, r in zip(sends, recvs):
-                comm.allreduce(s, r)
-            if a is not None:
-                a.record(hstream)
-            comm_lib.check(comm_lib.load().rar_group_end(comm.handle, hstream))
-        if b is not None:
-            b.record(hstream)
-
-    grouped = len(xs) > 1
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    if not grouped:
-        # The timed region: K launches back to back between one pair of
-        # events, so the step includes the gaps between launches and no
-        # per-launch event.
-        e0, e1 = HipEvent(), HipEvent()
-        t0 = time.perf_counter()
-        e0.record(hstream)
-        for _ in range(args.steps):
-            step()
-        e1.record(hstream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        t_step = e0.elapsed_time(e1) * 1e-3 / args.steps
-    else:
-        # A fused group is queued on the host call by call and launched by
-        # group_end: the step is that launch, bracketed by its own events
-        # (the queueing before it is host work, not timed).
-        ev = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
-        t0 = time.perf_counter()
-        for a, b in ev:
-            step(a, b)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        t_step = statistics.mean([a.elapsed_time(b) * 1e-3 for a, b in ev])
-    # The kernel pass, right after: K more launches, each between its own
-    # pair of timing-only events on the launch stream, give the kernel's
-    # duration per launch.  For a group, a sleep kernel keeps the device busy
-    # while the host queues the group, so the events see the launch alone.
-    ev = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
-    for a, b in ev:
-        if grouped and hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(1 << 21)  # about 1 ms of device clock cycles
-        step(a, b)
-    torch.cuda.synchronize()
-    if comm.async_error() != 0:
-        raise RuntimeError("the wait watchdog fired during the timed region")
-    per = [a.elapsed_time(b) * 1e-3 for a, b in ev]            # seconds, one launch each
+    lib, sarr, rarr, dcode = run.lib, run.sarr, run.rarr, run.dcode
+    run.warm(args.warmup)
+    t_step, wall = run.timed(args.steps)
+    per = run.kernel_pass(args.steps)
     t_kernel = statistics.mean(per)
     if args.graph:
         # the same K steps captured into one HIP graph and replayed: the
