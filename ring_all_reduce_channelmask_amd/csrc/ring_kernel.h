@@ -771,21 +771,11 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
 #define RAR_LL128_UNROLL 2
 #endif
 constexpr int kLl128Unroll = RAR_LL128_UNROLL;  // groups of 8 lines in flight per wave
-// How many iterations of a wave's whole-group loop its flags trail the data
-// (0, 1 or 2); timing only.
-#ifndef RAR_LL128_FLAG_LAG
-#define RAR_LL128_FLAG_LAG 0
-#endif
 
-// Wait until at most K of this wave's vector memory operations are
-// outstanding.  The counter retires them in the order they were issued, so
-// every operation issued before the last K has completed.  The asm is also
-// a compiler barrier: no memory access moves across it.
-template <int K>
-__device__ __forceinline__ void wait_vmem_below() {
-  static_assert(K >= 0 && K <= 63, "vmcnt holds 6 bits");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory");
-}
+// Wait until every vector memory operation this wave has issued has
+// completed (stores: reached L2).  The asm is also a compiler barrier: no
+// memory access moves across it.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Orders this wave's LDS accesses around a hand-off between its lanes.  The
 // fences cover LDS only ("local"): a fence over all address spaces would also
@@ -870,6 +860,9 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
     __syncthreads();
     if (cx.sh->abort) ok = false;
   }
+  // every lane of a wave read the same words: a wave-uniform answer, so
+  // the loops below compile to scalar branches
+  ok = __builtin_amdgcn_readfirstlane(ok ? 1 : 0) != 0;
   if (active && ok) {
     if (ok) {
       // A wave moves groups of 8 lines: 960 payload bytes, 1 KiB of FIFO.
@@ -898,8 +891,9 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
           const int64_t j = g + (int64_t)u * stride + sub;
           in[u] = zero;
           if (O::kRecv) {
+            // lane 7's upper half is the line's flag word: process() drops
+            // it (a zeroing here would wait for the load)
             in[u] = *G(reinterpret_cast<const v4u*>(rl + 16 * j + 2 * k));
-            if (k == 7) in[u].z = in[u].w = 0;  // the flag word is not payload
           }
         }
         // lanes 60..63 hold no user bytes of a group: they repeat lane 0's
@@ -989,86 +983,65 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
         }
       };
       // Whole groups run software-pipelined: the next iteration's loads are
-      // issued before this iteration's stores, so waiting for them never
-      // waits for those stores too (the vector memory counter retires in
-      // order).  The partial groups at the end of a share follow unpipelined.
-      // Two register sets take turns (no copies between them, which would
-      // wait for the loads); the last whole iteration is peeled (nothing to
-      // prefetch), and no load sits under a branch, so the waits stay exact.
+      // issued before this iteration's stores, so they are in flight while
+      // this iteration computes and stores.  Two register sets take turns
+      // (no copies between them, which would wait for the loads); the last
+      // whole iteration is peeled (nothing to prefetch).  The partial groups
+      // at the end of a share follow unpipelined.
       const std::integral_constant<bool, true> kW{};
       const std::integral_constant<bool, false> kP{};
       const int64_t gstep = (int64_t)U * stride;
       // Flags to a receiver on this XCD go out while the step is still
-      // being written, kLag iterations behind the data (iteration i = the
-      // U groups at first + i * gstep).  Whole-group iterations issue, in
-      // program order, L(i+1) (kLoads loads) and then S(i) (kStores
-      // stores).  The wait before a flag counts only operations that
-      // program order puts after that iteration's stores and that no
-      // compiler reordering can remove: with lag 2, at the start of
-      // iteration i at least L(i), S(i-1) (and L(i+1) unless i is the last)
-      // follow S(i-2), so at most kStores + kLoads outstanding retires it;
-      // with lag 1, L(i+1) follows S(i-1), or nothing does in the last
-      // iteration; with lag 0 the wait is for everything.  The vector memory
-      // counter retires operations in issue order, and spills or anything
-      // else the compiler interleaves only add operations.  A flag then
-      // lands in L2 after its line's data, and soon enough to merge with
-      // the line while it is still there (a flag stored after the whole
-      // step found most half-lines written back already, and they went to
-      // memory twice).  Other flags, and every flag to a receiver on
+      // being written: after an iteration's data stores, the wave waits for
+      // every vector memory operation it has outstanding (those stores and
+      // the next iteration's loads) and then stores that iteration's flags.
+      // A flag thus lands in L2 after its line's data, and soon enough to
+      // merge with the line while it is still there (a flag stored after
+      // the whole step found most half-lines written back already, and they
+      // went to memory twice).  Other flags, and every flag to a receiver on
       // another XCD, follow the drain at the end of the step.
-      constexpr int kLag = RAR_LL128_FLAG_LAG;
-      constexpr int kLoads = U * ((O::kRecv ? 1 : 0) + (O::kSrc ? 1 : 0));
-      constexpr int kStores = U * ((O::kSend ? 1 : 0) + (O::kDst ? 1 : 0));
-      // outstanding operations allowed at the start of an iteration, when
-      // the next iteration's loads were issued (kMid) or not (kLast)
-      constexpr int kMid = kLag == 2 ? kStores + kLoads : kLag == 1 ? kLoads : 0;
-      constexpr int kLast = kLag == 2 ? kStores + kLoads : 0;
       const bool early = O::kSend && __builtin_amdgcn_readfirstlane(cx.local_send ? 1 : 0) != 0;
-      int64_t pub = first;  // first group of the oldest iteration whose flags are not out
-      // flags of iteration `pub` once the iteration starting at g is kLag
-      // ahead of it
-      auto publish = [&](auto kWait, int64_t g) {
-        if (!early || g < pub + kLag * gstep) return;
-        wait_vmem_below<decltype(kWait)::value>();
+      // pub and g0 pass through readfirstlane when they advance: they are
+      // the same on every lane, but they merge right after the per-lane
+      // flag stores, and without it the compiler keeps them per lane and
+      // runs the loop on lane masks (measured: 3 % slower at 64 MiB)
+      int64_t pub = first;  // first group whose flags are not out
+      // flags of the iteration at g, once its data stores have retired
+      auto publish = [&](int64_t g) {
+        if (!early) return;
+        wait_vmem();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t j = pub + (int64_t)u * stride + sub;
+          const int64_t j = g + (int64_t)u * stride + sub;
           if (k == 7) store_relaxed_xcd(sl + 16 * j + 15, sflag);
         }
-        pub += gstep;
+        pub = uni64(g + gstep);
       };
-      const std::integral_constant<int, kMid> kWaitMid{};
-      const std::integral_constant<int, kLast> kWaitLast{};
-      const std::integral_constant<int, 0> kWaitAll{};
       int64_t g0 = first;
       if (g0 < hi && whole(g0)) {
         v4u inA[U], xA[U], inB[U], xB[U];
         load_whole(g0, inA, xA);
         for (;;) {
           if (!(g0 + gstep < hi && whole(g0 + gstep))) {
-            if constexpr (kLag > 0) publish(kWaitLast, g0);
             process(kW, g0, inA, xA);
-            if constexpr (kLag == 0) publish(kWaitAll, g0 + gstep);
-            g0 += gstep;
+            publish(g0);
+            g0 = uni64(g0 + gstep);
             break;
           }
           load_whole(g0 + gstep, inB, xB);
-          if constexpr (kLag > 0) publish(kWaitMid, g0);
           process(kW, g0, inA, xA);
-          if constexpr (kLag == 0) publish(kWaitAll, g0 + gstep);
-          g0 += gstep;
+          publish(g0);
+          g0 = uni64(g0 + gstep);
           if (!(g0 + gstep < hi && whole(g0 + gstep))) {
-            if constexpr (kLag > 0) publish(kWaitLast, g0);
             process(kW, g0, inB, xB);
-            if constexpr (kLag == 0) publish(kWaitAll, g0 + gstep);
-            g0 += gstep;
+            publish(g0);
+            g0 = uni64(g0 + gstep);
             break;
           }
           load_whole(g0 + gstep, inA, xA);
-          if constexpr (kLag > 0) publish(kWaitMid, g0);
           process(kW, g0, inB, xB);
-          if constexpr (kLag == 0) publish(kWaitAll, g0 + gstep);
-          g0 += gstep;
+          publish(g0);
+          g0 = uni64(g0 + gstep);
         }
       }
       for (; g0 < hi; g0 += gstep) {
