@@ -13,6 +13,7 @@ fraction of MI355X peak HBM bandwidth, and the CPU oracle timed on this host.
 """
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -351,6 +352,9 @@ def main():
                     help="place every user buffer ELEMS elements past a 16-byte boundary")
     ap.add_argument("--lanes", type=int, default=None)
     ap.add_argument("--waves", type=int, default=None)
+    ap.add_argument("--buff-size", type=int, default=None, metavar="BYTES",
+                    help="FIFO bytes per connection (0 = the protocol default), as in the "
+                         "pages' buffer sweep")
     ap.add_argument("--launch-mode", type=int, default=None, choices=[0, 1])
     ap.add_argument("--slices", type=int, default=None, choices=[1, 2, 4])
     ap.add_argument("--placement", type=int, default=None, choices=[0, 1])
@@ -411,6 +415,8 @@ def main():
         sweep(args)
         return
     w = workloads.WORKLOADS[args.workload]
+    if args.buff_size is not None:
+        w = dataclasses.replace(w, buff_size=args.buff_size)
     if args.algo == "oneshot":
         run_oneshot(args, w)
         return
