@@ -404,11 +404,40 @@ rar_result_t rar_comm_read_trace(rar_comm_t comm, rar_trace_rec_t* out, size_t c
  * per lane W, workgroups in the grid G (including idle padding). */
 rar_result_t rar_comm_shape(rar_comm_t comm, int* nchannels, int* lanes, int* waves, int* grid);
 
+/* The communicator's rings as GRAPH lines, each followed by that channel's
+ * geometry [C12 "Graph 如何变成完整 ring": the ring a channel runs is
+ * recomputed from the connector graph; "GRAPH 重建：N=2 / N=3 / N=4": one
+ * line per channel].  For every active channel, in channel id order:
+ *   "Channel cc/CC : r0 r1 ... r(N-1)\n"   as rar_graph_text, then
+ *   "  lanes P, waves W, FIFO B B per connection, S B per lane and step,
+ *    XCD per lane: x ...\n"
+ * where x is the XCD of the lane's workgroups, or x0/x1/... (rank order)
+ * when its ranks run on different XCDs.  Text and sizes as rar_graph_text.
+ * RAR_INVALID_ARGUMENT: comm NULL, or buf too small (only *len set). */
+rar_result_t rar_comm_graph_text(rar_comm_t comm, char* buf, size_t cap, size_t* len);
+
 /* ---- host planner, exposed for testing (no device needed) ------------------ */
 
 /* Ring index, prev and next of every user rank, as rar_comm_create computes
  * them.  Errors: RAR_INVALID_ARGUMENT if ring_order is not a permutation. */
 rar_result_t rar_ring_info(int nranks, const int* ring_order, int* index, int* prev, int* next);
+
+/* GRAPH lines of a ring layout, without a communicator [C12 "Graph 如何变成完整
+ * ring": each ring is rebuilt from the connector graph by walking next from
+ * rank 0 N times, which must return to rank 0 having met every rank once;
+ * C12 "GRAPH 重建：N=2 / N=3 / N=4" for the lines].  One line per set bit c
+ * of channel_mask, in increasing c:
+ *   "Channel cc/CC : r0 r1 ... r(N-1)\n"
+ * with cc = c and CC = the highest set bit + 1 (two digits each), and the
+ * ring channel c runs (ring c mod nrings of ring_orders, nrings rows of
+ * nranks ints, as rar_comm_create_rings) listed from rank 0 along next.
+ * The text goes to buf with a terminating NUL; *len (may be NULL) receives
+ * its length without the NUL.  buf NULL with cap 0 only reports the length.
+ * RAR_INVALID_ARGUMENT: nranks outside [2, 64], nrings outside [1, 64],
+ * NULL ring_orders, an empty mask, a ring that is not a permutation of the
+ * ranks (its walk would not loop back), or a buf too small (only *len set). */
+rar_result_t rar_graph_text(int nranks, int nrings, const int* ring_orders, uint64_t channel_mask,
+                            char* buf, size_t cap, size_t* len);
 
 typedef struct {
   int32_t channel;    /* dense channel index n                        */

@@ -16,7 +16,7 @@ import ctypes
 from . import _lib
 from ._lib import RarError  # noqa: F401
 
-__all__ = ["Comm", "ring_allreduce", "ring_allreduce_noalloc", "oneshot_allreduce", "ring_info", "plan_pieces", "RarError"]
+__all__ = ["Comm", "ring_allreduce", "ring_allreduce_noalloc", "oneshot_allreduce", "ring_info", "graph_text", "plan_pieces", "RarError"]
 
 
 def _dtype_name(t):
@@ -142,6 +142,10 @@ class Comm:
                                               ctypes.byref(w), ctypes.byref(g)))
         return dict(channels=c.value, lanes=p.value, waves=w.value, grid=g.value)
 
+    def graph(self):
+        """The rings as GRAPH lines, each followed by its channel's geometry."""
+        return _text(lambda buf, cap, n: _lib.load().rar_comm_graph_text(self._h, buf, cap, n))
+
     def query_state(self):
         s = self.shape()
         cap = self.nranks * s["channels"] * s["lanes"] * 2
@@ -223,6 +227,26 @@ def ring_info(ring_order):
     idx, prv, nxt = (ctypes.c_int * n)(), (ctypes.c_int * n)(), (ctypes.c_int * n)()
     _lib.check(_lib.load().rar_ring_info(n, (ctypes.c_int * n)(*ring_order), idx, prv, nxt))
     return list(idx), list(prv), list(nxt)
+
+
+def _text(call):
+    """A text result: ask for its length, then fetch it."""
+    n = ctypes.c_size_t()
+    _lib.check(call(None, 0, ctypes.byref(n)))
+    buf = ctypes.create_string_buffer(n.value + 1)
+    _lib.check(call(buf, n.value + 1, ctypes.byref(n)))
+    return buf.value.decode()
+
+
+def graph_text(nranks, rings, mask):
+    """GRAPH lines of a ring layout: one "Channel cc/CC : r0 r1 ..." line per
+    set bit of mask; `rings` is one ring order or a list of them."""
+    rings = [list(r) for r in rings] if len(rings) and isinstance(rings[0], (list, tuple)) \
+        else [list(rings)]
+    flat = [r for ring in rings for r in ring]
+    arr = (ctypes.c_int * len(flat))(*flat)
+    return _text(lambda buf, cap, n: _lib.load().rar_graph_text(nranks, len(rings), arr, mask, buf,
+                                                                cap, n))
 
 
 def plan_pieces(nranks, mask, proto, buff_size, chunk_steps, dtype, counts):

@@ -86,9 +86,13 @@ SIGNATURES = [
     ("rar_comm_query_state", _c.c_int, [_c.c_void_p, _c.POINTER(_c.c_int64), _c.c_size_t,
                                         _c.POINTER(_c.c_size_t)]),
     ("rar_comm_shape", _c.c_int, [_c.c_void_p, _ip, _ip, _ip, _ip]),
+    ("rar_comm_graph_text", _c.c_int, [_c.c_void_p, _c.c_char_p, _c.c_size_t,
+                                       _c.POINTER(_c.c_size_t)]),
     ("rar_comm_read_trace", _c.c_int, [_c.c_void_p, _c.POINTER(TraceRec), _c.c_size_t,
                                        _c.POINTER(_c.c_size_t)]),
     ("rar_ring_info", _c.c_int, [_c.c_int, _ip, _ip, _ip, _ip]),
+    ("rar_graph_text", _c.c_int, [_c.c_int, _c.c_int, _ip, _c.c_uint64, _c.c_char_p, _c.c_size_t,
+                                  _c.POINTER(_c.c_size_t)]),
     ("rar_plan_pieces", _c.c_int, [_c.c_int, _c.c_uint64, _c.c_int, _c.c_size_t, _c.c_int,
                                    _c.c_int, _c.c_int, _c.POINTER(_c.c_size_t),
                                    _c.POINTER(Piece), _c.c_int, _ip, _c.POINTER(_c.c_int64)]),

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstddef>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -55,6 +56,18 @@ using rar::check_dtype;
 using rar::check_op;
 using rar::check_rank_buffers;
 rar_result_t fail(rar_result_t r, const std::string& msg) { return rar::set_error(r, msg); }
+
+// Copy a text result out: *len (if given) gets its length without the NUL;
+// with buf NULL and cap 0 the call only reports the length.
+rar_result_t put_text(const std::string& text, char* buf, size_t cap, size_t* len) {
+  if (len) *len = text.size();
+  if (!buf && cap == 0) return RAR_SUCCESS;
+  if (!buf || cap < text.size() + 1)
+    return fail(RAR_INVALID_ARGUMENT, "text buffer holds " + std::to_string(cap) + " bytes, " +
+                                          std::to_string(text.size() + 1) + " needed");
+  std::memcpy(buf, text.c_str(), text.size() + 1);
+  return RAR_SUCCESS;
+}
 
 #define RAR_HIP(expr)                                                                      \
   do {                                                                                     \
@@ -891,6 +904,54 @@ rar_result_t rar_comm_read_trace(rar_comm_t c, rar_trace_rec_t* out, size_t cap,
   }
   *written = k;
   return RAR_SUCCESS;
+}
+
+rar_result_t rar_graph_text(int nranks, int nrings, const int* ring_orders, uint64_t channel_mask,
+                            char* buf, size_t cap, size_t* len) {
+  g_last_error.clear();
+  std::vector<std::string> lines;
+  std::string err;
+  if (!rar::graph_lines(nranks, nrings, ring_orders, channel_mask, &lines, &err))
+    return fail(RAR_INVALID_ARGUMENT, err);
+  std::string text;
+  for (const std::string& l : lines) text += l + "\n";
+  return put_text(text, buf, cap, len);
+}
+
+rar_result_t rar_comm_graph_text(rar_comm_t c, char* buf, size_t cap, size_t* len) {
+  g_last_error.clear();
+  if (!c) return fail(RAR_INVALID_ARGUMENT, "comm is NULL");
+  std::vector<std::string> lines;
+  std::string err;
+  if (!rar::graph_lines(c->nranks, c->nrings, c->order.data(), c->mask, &lines, &err))
+    return fail(RAR_INTERNAL_ERROR, err);
+  // XCD of every (channel, lane, rank) workgroup: block g of the grid runs on
+  // XCD g mod 8 (the dispatcher deals workgroups to the XCDs in turn)
+  std::vector<int> xcd((size_t)c->C * c->P * c->nranks, -1);
+  for (size_t g = 0; g < c->wgmap.size(); ++g) {
+    const uint32_t m = c->wgmap[g];
+    if (m == rar::kIdleWg) continue;
+    const int r = (int)(m & 0xFF), n = (int)((m >> 8) & 0xFF), lane = (int)(m >> 16);
+    xcd[((size_t)n * c->P + lane) * c->nranks + r] = (int)(g % 8);
+  }
+  const int64_t lane_step = rar::lane_step_bytes(c->proto, c->buff, c->sizing.split_lanes);
+  std::string text;
+  for (int n = 0; n < (int)lines.size(); ++n) {
+    text += lines[n] + "\n";
+    char head[160];
+    snprintf(head, sizeof head, "  lanes %d, waves %d, FIFO %zu B per connection, %lld B per lane and step, XCD per lane:",
+             c->P, c->W, c->buff, (long long)lane_step);
+    text += head;
+    for (int lane = 0; lane < c->P; ++lane) {
+      const int* x = &xcd[((size_t)n * c->P + lane) * c->nranks];
+      const bool one = std::all_of(x, x + c->nranks, [&](int v) { return v == x[0]; });
+      text += " " + std::to_string(x[0]);
+      if (!one)
+        for (int r = 1; r < c->nranks; ++r) text += "/" + std::to_string(x[r]);
+    }
+    text += "\n";
+  }
+  return put_text(text, buf, cap, len);
 }
 
 rar_result_t rar_comm_shape(rar_comm_t c, int* nchannels, int* lanes, int* waves, int* grid) {

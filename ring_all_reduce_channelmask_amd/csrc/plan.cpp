@@ -2,6 +2,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <cstdio>
 
 namespace rar {
 namespace {
@@ -219,6 +220,41 @@ std::vector<uint32_t> make_wg_map(int nranks, int n_channels, int n_lanes, bool 
   for (int x = 0; x < kXcds; ++x)
     for (size_t k = 0; k < per_xcd[x].size(); ++k) map[k * kXcds + x] = per_xcd[x][k];
   return map;
+}
+
+bool graph_lines(int nranks, int nrings, const int* orders, uint64_t mask,
+                 std::vector<std::string>* lines, std::string* err) {
+  if (nrings < 1 || nrings > kMaxChannels) {
+    *err = "nrings must be in [1, 64]";
+    return false;
+  }
+  if (!orders) {
+    *err = "ring_orders is NULL";
+    return false;
+  }
+  if (mask == 0) {
+    *err = "channel mask selects no channel";
+    return false;
+  }
+  std::vector<RingInfo> rings(nrings);
+  for (int k = 0; k < nrings; ++k)
+    if (!build_ring(nranks, orders + (size_t)k * nranks, &rings[k], err)) return false;
+  const int space = 64 - __builtin_clzll(mask);
+  lines->clear();
+  for (int c = 0; c < 64; ++c) {
+    if (!((mask >> c) & 1)) continue;
+    const RingInfo& ring = rings[c % nrings];
+    char head[32];
+    snprintf(head, sizeof head, "Channel %02d/%02d :", c, space);
+    std::string line = head;
+    int cur = 0;
+    for (int i = 0; i < nranks; ++i) {
+      line += " " + std::to_string(cur);
+      cur = ring.next[cur];
+    }
+    lines->push_back(line);
+  }
+  return true;
 }
 
 int64_t lane_step_bytes(int proto, size_t buff_size, int lanes) {

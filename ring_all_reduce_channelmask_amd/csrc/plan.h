@@ -25,6 +25,15 @@ struct RingInfo {
 // message) unless every rank appears exactly once and the walk loops back.
 bool build_ring(int nranks, const int* ring_order, RingInfo* out, std::string* err);
 
+// GRAPH lines of a ring layout [NCCL 专家课程 12, "Graph 如何变成完整 ring" (a
+// channel's ring is recomputed from the connector graph) and "GRAPH 重建：N=2 /
+// N=3 / N=4" (the lines)]: one line "Channel cc/CC : r0 r1 ..." per set bit c
+// of mask, in increasing c, CC = highest set bit + 1; channel c runs ring
+// c mod nrings of `orders` (nranks ints each), printed from rank 0 along next.
+// Returns false (with a message) for a bad nranks, nrings, mask or ring.
+bool graph_lines(int nranks, int nrings, const int* orders, uint64_t mask,
+                 std::vector<std::string>* lines, std::string* err);
+
 int64_t elem_size(int dtype);
 
 // Largest chunk in elements [NCCL 专家课程 23, "Buffer 到 Chunk 的实测公式";

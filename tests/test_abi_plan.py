@@ -309,3 +309,62 @@ def test_group_context_discards_on_error(monkeypatch):
         pass
     assert calls == ["start", "end"]
     c._h = None
+
+
+# ---- GRAPH lines (rar_graph_text) ----------------------------------------
+
+def _graph_lines(nranks, rings, mask):
+    return rar.graph_text(nranks, rings, mask).splitlines()
+
+
+@pytest.mark.parametrize("key,n", [("n2", 2), ("n3", 3), ("n4", 4)])
+def test_graph_text_reproduces_the_pages_channel_rings(key, n):
+    """Course 12 "GRAPH 重建": with the pages' base rings duplicated over 12
+    channels, channel c runs base ring c mod len(base); each line lists that
+    ring from rank 0."""
+    with open(os.path.join(ROOT, "tests", "golden", "graph_rings.json")) as f:
+        g = json.load(f)[key]
+    base, nch = g["base"], g["channels"]
+    lines = _graph_lines(n, base, (1 << nch) - 1)
+    assert len(lines) == nch
+    for c, line in enumerate(lines):
+        want = base[c % len(base)]
+        assert line == f"Channel {c:02d}/{nch:02d} : " + " ".join(map(str, want))
+
+
+def test_graph_text_the_pages_single_line():
+    """Course 12 "Graph 如何变成完整 ring" prints the ring 0-2-3-1 of channel 2
+    of 12 as "Channel 02/12 : 0 2 3 1"; any rotation of the ring order walks
+    the same connector graph, so it prints the same line."""
+    for order in ([0, 2, 3, 1], [2, 3, 1, 0], [3, 1, 0, 2], [1, 0, 2, 3]):
+        assert _graph_lines(4, order, (1 << 12) - 1)[2] == "Channel 02/12 : 0 2 3 1"
+    # N=2, one channel: a single line with the one ring
+    assert _graph_lines(2, [1, 0], 1) == ["Channel 00/01 : 0 1"]
+
+
+def test_graph_text_sparse_mask_and_reversed_ring():
+    lines = _graph_lines(4, [0, 1, 2, 3], (1 << 63) | (1 << 9) | 1)
+    assert lines == ["Channel 00/64 : 0 1 2 3", "Channel 09/64 : 0 1 2 3", "Channel 63/64 : 0 1 2 3"]
+    # the reversed ring walks next the other way round
+    assert _graph_lines(4, [3, 2, 1, 0], 1) == ["Channel 00/01 : 0 3 2 1"]
+
+
+def test_graph_text_errors_and_sizes():
+    lib = _lib.load()
+    ring = (ctypes.c_int * 4)(0, 2, 3, 1)
+    n = ctypes.c_size_t(0)
+    assert lib.rar_graph_text(4, 1, ring, 0xFFF, None, 0, ctypes.byref(n)) == 0
+    assert n.value == 12 * len("Channel 00/12 : 0 2 3 1\n")
+    small = ctypes.create_string_buffer(10)
+    m = ctypes.c_size_t(0)
+    assert lib.rar_graph_text(4, 1, ring, 0xFFF, small, 10, ctypes.byref(m)) == 1
+    assert m.value == n.value and b"needed" in lib.rar_get_last_error()
+    bad = (ctypes.c_int * 4)(0, 2, 2, 1)
+    assert lib.rar_graph_text(4, 1, bad, 1, None, 0, None) == 1
+    assert lib.rar_graph_text(4, 1, ring, 0, None, 0, None) == 1
+    assert lib.rar_graph_text(4, 0, ring, 1, None, 0, None) == 1
+    assert lib.rar_graph_text(1, 1, ring, 1, None, 0, None) == 1
+    assert lib.rar_graph_text(4, 1, None, 1, None, 0, None) == 1
+    # a base ring that is not a permutation fails even if no channel uses it
+    two = (ctypes.c_int * 8)(0, 1, 2, 3, 0, 0, 1, 2)
+    assert lib.rar_graph_text(4, 2, two, 1, None, 0, None) == 1

@@ -165,3 +165,27 @@ def test_cached_plan_follows_pointer_count_and_operator_changes(proto):
                 assert_bits_equal(to_host(r[q], dtype), wv, f"group {k} rank {q}")
     assert comm.async_error() == 0
     comm.close()
+
+
+@pytest.mark.parametrize("placement", [0, 1])
+def test_comm_graph_text_lists_rings_and_lane_xcds(placement):
+    """The communicator's GRAPH lines are the rings rar_graph_text prints for
+    its layout, and each geometry line names the XCD of every lane's
+    workgroups: pipeline q = n * lanes + lane on XCD q mod 8 (placement 0,
+    one XCD per pipeline), rank r of it on XCD (q + r) mod 8 (placement 1)."""
+    import ring_all_reduce_channelmask_amd as rar
+    rings = [[0, 1, 2, 3], [0, 2, 3, 1]]
+    mask = 0b1011
+    c = _comm(nranks=4, ring_order=rings, mask=mask, proto="SIMPLE", lanes=3, waves=2,
+              placement=placement, launch_mode=1)
+    lines = c.graph().splitlines()
+    assert lines[0::2] == rar.graph_text(4, rings, mask).splitlines()
+    for n, g in enumerate(lines[1::2]):
+        head, xcds = g.split("XCD per lane:")
+        assert head.startswith("  lanes 3, waves 2, FIFO ")
+        got = xcds.split()
+        assert len(got) == 3
+        for lane, x in enumerate(got):
+            q = n * 3 + lane
+            want = str(q % 8) if placement == 0 else "/".join(str((q + r) % 8) for r in range(4))
+            assert x == want, (n, lane, x, want)
