@@ -767,10 +767,19 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
 // (at workgroup scope to a receiver on this XCD).  Receiver: wave 0 polls the
 // flag word of every line of the workgroup's share, voting until none is
 // missing, issues one acquire, and a barrier lets every wave load its lines.
+// Groups of 8 lines in flight per wave: 4 for 4-byte payloads, 3 for bf16,
+// whose operators need more registers (measured at 64 MiB against 2 groups:
+// fp32 -2 %, int32 -2 %, bf16 -2 %; bf16 with 4 spills more and is slower).
 #ifndef RAR_LL128_UNROLL
-#define RAR_LL128_UNROLL 2
+#define RAR_LL128_UNROLL 4
 #endif
-constexpr int kLl128Unroll = RAR_LL128_UNROLL;  // groups of 8 lines in flight per wave
+#ifndef RAR_LL128_UNROLL_BF16
+#define RAR_LL128_UNROLL_BF16 3
+#endif
+template <class S>
+constexpr int ll128_unroll() {
+  return sizeof(S) == 2 ? RAR_LL128_UNROLL_BF16 : RAR_LL128_UNROLL;
+}
 
 // Wait until every vector memory operation this wave has issued has
 // completed (stores: reached L2).  The asm is also a compiler barrier: no
@@ -806,7 +815,7 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
                            int chunk) {
   using S = typename Ty::S;
   using O = OpTraits<OP>;
-  constexpr int U = kLl128Unroll;
+  constexpr int U = ll128_unroll<S>();
   // the share's bounds and the wave index are the same on every lane of a
   // wave: held in scalar registers, the loops below branch per wave rather
   // than through lane masks
@@ -1186,12 +1195,14 @@ __device__ void load_batch(Shmem& sh, const Plan& a, uint32_t b, int lid) {
 // ---------------------------------------------------------------- entry
 // LL128 workgroups are small (4 waves in the measured shape) and the protocol
 // wants many of them: capping its registers at three waves per SIMD lets three
-// such workgroups share a CU (bf16 then spills a few hundred bytes per lane).
+// such workgroups share a CU (fp32 and int32, with 4 groups of lines in flight,
+// then spill 17 registers per lane; still faster than 2 groups unspilled).
 template <class Ty, int PROTO>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PROTO == kLL128 ? 3 : 1)))
 ring_allreduce_kernel(KernelArgs args) {
   __shared__ Shmem sh;
-  __shared__ __attribute__((aligned(16))) uint8_t stage[PROTO == kLL128 ? kMaxWaves * kLl128Unroll * 1024 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t
+      stage[PROTO == kLL128 ? kMaxWaves * ll128_unroll<typename Ty::S>() * 1024 : 16];
   const DevComm* comm = args.comm;
   // Startup is a chain of dependent loads, so the independent ones go out
   // together: the workgroup map and the channel mask here, the ring position,
