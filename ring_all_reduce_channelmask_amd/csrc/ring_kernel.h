@@ -764,9 +764,9 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
 // 16 bytes per lane; lane 7 of each line holds word 14 and the flag word.
 // Sender: every wave stores the data words of its lines, drains (plus an L2
 // write-back when the receiver is on another XCD), then stores the flag words
-// (at workgroup scope to a receiver on this XCD).  Receiver: wave 0 polls the
-// flag word of every line of the workgroup's share, voting until none is
-// missing, issues one acquire, and a barrier lets every wave load its lines.
+// (at workgroup scope to a receiver on this XCD).  Receiver: each wave waits
+// for one flag per group of lines it is about to read (the flags follow all
+// of those lines' data) and reads the lines with agent-coherent loads.
 // Groups of 8 lines in flight per wave: 4 for 4-byte payloads, 3 for bf16,
 // whose operators need more registers (measured at 64 MiB against 2 groups:
 // fp32 -2 %, int32 -2 %, bf16 -2 %; bf16 with 4 spills more and is slower).
@@ -776,6 +776,10 @@ __device__ void ll_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* dst,
 #ifndef RAR_LL128_UNROLL_BF16
 #define RAR_LL128_UNROLL_BF16 3
 #endif
+// Word 3 of a raw buffer resource on gfx9 (untyped access), and the cache
+// policy bit of an agent-coherent load (sc1).
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kCpolSc1 = 16;
 template <class S>
 constexpr int ll128_unroll() {
   return sizeof(S) == 2 ? RAR_LL128_UNROLL_BF16 : RAR_LL128_UNROLL;
@@ -844,31 +848,12 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
   uint64_t* sl = reinterpret_cast<uint64_t*>(cx.send_fifo + (cx.send_step % kSteps) * cx.lane_step_bytes) - 16 * lo;
   const uint8_t* sb = reinterpret_cast<const uint8_t*>(src);
   uint8_t* db = reinterpret_cast<uint8_t*>(dst);
-  // Receive: wave 0 polls the flags of every line of this lane's share and
-  // then issues one agent-scope acquire; the barrier hands that ordering to
-  // the other waves, which load data only after it.  One L1 invalidation per
-  // workgroup and step, not one per wave.  Flags to different lines need not
-  // arrive in order, so every line is checked; between rounds the wave
-  // sleeps, leaving the memory system to the data.
-  if (O::kRecv) {
-    if (wave == 0 && lo < hi) {
-      const uint64_t tp = __builtin_amdgcn_s_memrealtime();
-      for (uint32_t it = 1;; ++it) {
-        bool pending = false;
-        for (int64_t j = lo + lid; j < hi; j += 64) pending |= load_relaxed(rl + 16 * j + 15) != rflag;
-        if (!__any(pending)) break;
-        __builtin_amdgcn_s_sleep(1);
-        if ((it & 15u) == 0 && should_stop(cx, tp)) {
-          ok = false;
-          break;
-        }
-      }
-      if (ok) acquire_fence();
-      else cx.sh->abort = 1;
-    }
-    __syncthreads();
-    if (cx.sh->abort) ok = false;
-  }
+  // The receive slot as a buffer resource: its FIFO words are read with
+  // agent-coherent (sc1) loads, like the flag words, so they read the L2 the
+  // sender wrote and need no L1 invalidation first.
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      cx.recv_fifo + (cx.recv_step % kSteps) * cx.lane_step_bytes, 0, (int)cx.lane_step_bytes,
+      kRawBufferWord3);
   // every lane of a wave read the same words: a wave-uniform answer, so
   // the loops below compile to scalar branches
   ok = __builtin_amdgcn_readfirstlane(ok ? 1 : 0) != 0;
@@ -894,6 +879,10 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
         const int64_t last_end = g + (int64_t)(U - 1) * stride + 8;
         return last_end <= hi && 120 * last_end <= nbytes;
       };
+      // this lane's 16 bytes of line j of the receive slot
+      auto fifo_load = [&](int64_t j) -> v4u {
+        return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)(128 * (j - lo) + 16 * k), 0, kCpolSc1);
+      };
       auto load_whole = [&](int64_t g, v4u* in, v4u* x) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -902,7 +891,7 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
           if (O::kRecv) {
             // lane 7's upper half is the line's flag word: process() drops
             // it (a zeroing here would wait for the load)
-            in[u] = *G(reinterpret_cast<const v4u*>(rl + 16 * j + 2 * k));
+            in[u] = fifo_load(j);
           }
         }
         // lanes 60..63 hold no user bytes of a group: they repeat lane 0's
@@ -922,7 +911,7 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
           in[u] = zero;
           x[u] = zero;
           if (O::kRecv && j < hi) {
-            in[u] = *G(reinterpret_cast<const v4u*>(rl + 16 * j + 2 * k));
+            in[u] = fifo_load(j);
             if (k == 7) in[u].z = in[u].w = 0;
           }
           if (O::kSrc && ulane) {
@@ -1026,10 +1015,46 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
         }
         pub = uni64(g + gstep);
       };
+      // Receive group by group: before a wave loads the lines of an
+      // iteration it waits for the flag of the iteration's first line.  The
+      // sender stores an iteration's flags only after all of that
+      // iteration's data stores have completed (the rest of the step's
+      // flags after the step's drain), so one flag stands for every line of
+      // the iteration.  The next iteration's flag is loaded one iteration
+      // ahead: a sender that is ahead costs no extra round trip.  Measured
+      // against wave 0 polling every flag of the step before any wave reads
+      // (then one acquire and a barrier): 276 -> 245 us at 64 MiB, the
+      // receivers no longer wait for whole steps of their senders.
+      constexpr bool kGroupRecv = O::kRecv;
+      auto wait_line = [&](int64_t j) -> bool {
+        if constexpr (!kGroupRecv) return true;
+        const uint64_t tp = __builtin_amdgcn_s_memrealtime();
+        for (uint32_t it = 1;; ++it) {
+          if (uni64(load_relaxed(rl + 16 * j + 15)) == rflag) break;
+          __builtin_amdgcn_s_sleep(1);
+          if ((it & 15u) == 0 && __builtin_amdgcn_readfirstlane(should_stop(cx, tp) ? 1 : 0) != 0)
+            return false;
+        }
+        asm volatile("" ::: "memory");  // the lines' loads stay after the flag
+        return true;
+      };
+      auto ready = [&](int64_t j, uint64_t seen) -> bool {
+        if constexpr (!kGroupRecv) return true;
+        if (uni64(seen) == rflag) {
+          asm volatile("" ::: "memory");
+          return true;
+        }
+        return wait_line(j);
+      };
+      auto peek = [&](int64_t j) -> uint64_t {
+        if constexpr (!kGroupRecv) return 0;
+        return j < hi ? load_relaxed(rl + 16 * j + 15) : 0;
+      };
       int64_t g0 = first;
-      if (g0 < hi && whole(g0)) {
+      if (g0 < hi && whole(g0) && (ok = wait_line(g0))) {
         v4u inA[U], xA[U], inB[U], xB[U];
         load_whole(g0, inA, xA);
+        uint64_t seen = peek(g0 + gstep);
         for (;;) {
           if (!(g0 + gstep < hi && whole(g0 + gstep))) {
             process(kW, g0, inA, xA);
@@ -1037,7 +1062,9 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
             g0 = uni64(g0 + gstep);
             break;
           }
+          if (!(ok = ready(g0 + gstep, seen))) break;
           load_whole(g0 + gstep, inB, xB);
+          seen = peek(g0 + 2 * gstep);
           process(kW, g0, inA, xA);
           publish(g0);
           g0 = uni64(g0 + gstep);
@@ -1047,18 +1074,21 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
             g0 = uni64(g0 + gstep);
             break;
           }
+          if (!(ok = ready(g0 + gstep, seen))) break;
           load_whole(g0 + gstep, inA, xA);
+          seen = peek(g0 + 2 * gstep);
           process(kW, g0, inB, xB);
           publish(g0);
           g0 = uni64(g0 + gstep);
         }
       }
-      for (; g0 < hi; g0 += gstep) {
+      for (; ok && g0 < hi; g0 = uni64(g0 + gstep)) {
+        if (!(ok = wait_line(g0))) break;
         v4u in[U], x[U];
         load_part(g0, in, x);
         process(kP, g0, in, x);
       }
-      if (O::kSend) {
+      if (O::kSend && ok) {
         // data words before flag words: drained into this L2, and written
         // back when the receiver runs on another XCD
         drain_vmem();
