@@ -639,3 +639,30 @@ def test_ll128_benchmark_shape_every_dtype_and_operator(dtype, op):
     for i in range(len(xs)):
         for r in range(4):
             assert_bits_equal(got[i][r], want[i], f"{dtype} {op} work {i} rank {r}")
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+@pytest.mark.parametrize("waves", [1, 3, 8])
+@pytest.mark.parametrize("extra", [0, 1, 13])
+def test_ll128_iteration_boundaries(dtype, waves, extra):
+    """LL128 receivers wait for one flag per wave iteration (U groups of 8
+    lines: U = 4 for 4-byte payloads, 3 for bf16) and then read that
+    iteration's lines.  A lane's step holds two whole iterations of every
+    wave plus `extra` lines (none, one, or a partial group), over one and two
+    lanes, and the runRing tail loop cuts a smaller chunk; every result bit
+    matches the simulator."""
+    U = 3 if dtype == "bfloat16" else 4
+    es = 2 if dtype == "bfloat16" else 4
+    lines = 2 * 8 * waves * U + extra
+    for lanes in (1, 2):
+        # a lane's slot is a whole number of 256-byte units: size the buffer
+        # so that each lane's step holds `lines` lines
+        lane_step = 256 * -(-lines * 128 // 256)
+        buff = 8 * lanes * lane_step
+        chunk_bytes = lanes * lines * 120
+        count = (4 * chunk_bytes + 4 * chunk_bytes // 2) // es + 7
+        x = _rand(dtype, (4, count), 100 + waves + extra + lanes)
+        comm = _comm(nranks=4, ring_order=[0, 2, 3, 1], mask=0x1, proto="LL128", buff_size=buff,
+                     lanes=lanes, waves=waves)
+        _check_vs_sim(comm, [x], dtype, buff, 4)
+        comm.close()
