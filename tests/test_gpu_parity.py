@@ -615,7 +615,8 @@ def test_more_than_2g_elements(proto):
 def test_ll128_benchmark_shape_every_dtype_and_operator(dtype, op):
     """LL128 in the launch shape the benchmark uses (16 lanes x 4 waves over
     12 channels: 768 workgroups, three per CU, possible because the LL128
-    kernels keep to three waves' registers per SIMD; the bf16 ones spill),
+    kernels keep to three waves' registers per SIMD; fp32 and int32 spill a
+    few registers),
     for every payload type and the operators with the heaviest kernels, on
     a ragged 3-collective group, bit for bit against the closed form."""
     rng = np.random.default_rng([["int32", "float32", "bfloat16"].index(dtype),
