@@ -258,9 +258,11 @@ bool graph_lines(int nranks, int nrings, const int* orders, uint64_t mask,
 }
 
 int64_t lane_step_bytes(int proto, size_t buff_size, int lanes) {
-  // LL128 lanes take an even number of 128-byte lines
-  const int64_t unit = proto == kLL128 ? 256 : 16;
-  const int64_t step_units = (int64_t)buff_size / kSteps / unit;
+  // LL128 lanes take an even number of 128-byte lines; Simple lanes take
+  // whole 128-byte cache lines of every slice, so a lane's slot steps are
+  // cache-line multiples too
+  const int64_t unit = proto == kLL128 ? 256 : proto == kSimple ? 128 : 16;
+  const int64_t step_units = div_up((int64_t)buff_size / kSteps, unit);
   return unit * div_up(step_units, lanes);
 }
 
