@@ -36,7 +36,7 @@ TUNING = {
     "ll128_64m": dict(lanes=16, waves=4, launch_mode=1),
     "bf16_n8": dict(lanes=2, waves=8, launch_mode=1),
     "int32_n8": dict(lanes=2, waves=8, launch_mode=1),
-    "ll_512k": dict(lanes=16, waves=2, launch_mode=1),
+    "ll_512k": dict(lanes=16, waves=4, launch_mode=1),
     "ll_64m": dict(lanes=8, waves=4, launch_mode=1),
     "fused_ll": dict(lanes=16, waves=4, launch_mode=1, deal_works=1),
     "simple_4k": dict(lanes=1, waves=2, launch_mode=1, slices_per_chunk=1),
