@@ -861,251 +861,249 @@ __device__ void ll128_call(Ctx& cx, const typename Ty::S* src, typename Ty::S* d
   // the loops below compile to scalar branches
   ok = __builtin_amdgcn_readfirstlane(ok ? 1 : 0) != 0;
   if (active && ok) {
-    if (ok) {
-      // A wave moves groups of 8 lines: 960 payload bytes, 1 KiB of FIFO.
-      // User data goes through an LDS tile [C23 "LL128：15/16 Payload" stages
-      // user data through shared memory]: 60 lanes load or store 16
-      // contiguous user bytes each, and the tile is read or written in
-      // line layout (lane (line, segment), 16 bytes, 8 in the last segment).
-      // Every lane then stores its 16 FIFO bytes with one instruction; the
-      // flag word gets a placeholder 0 that never matches a flag, and the
-      // real flag follows after the drain below.
-      constexpr bool kNu = RAR_NT_USER != 0;
-      uint8_t* stage = cx.stage + (int64_t)wave * U * 1024;
-      const int64_t ub = 16 * (int64_t)lid;  // this lane's 16 bytes of a group, user layout
-      const bool ulane = lid < 60;
-      const v4u zero = {0, 0, 0, 0};
-      // The FIFO words (in) and user bytes (x) of U groups of 8 lines, group u
-      // starting at line g + u * stride.  whole(g): all U groups are full
-      // lines inside the step and the chunk.
-      auto whole = [&](int64_t g) {
-        const int64_t last_end = g + (int64_t)(U - 1) * stride + 8;
-        return last_end <= hi && 120 * last_end <= nbytes;
-      };
-      // this lane's 16 bytes of line j of the receive slot
-      auto fifo_load = [&](int64_t j) -> v4u {
-        return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)(128 * (j - lo) + 16 * k), 0, kCpolSc1);
-      };
-      auto load_whole = [&](int64_t g, v4u* in, v4u* x) {
+    // A wave moves groups of 8 lines: 960 payload bytes, 1 KiB of FIFO.
+    // User data goes through an LDS tile [C23 "LL128：15/16 Payload" stages
+    // user data through shared memory]: 60 lanes load or store 16
+    // contiguous user bytes each, and the tile is read or written in
+    // line layout (lane (line, segment), 16 bytes, 8 in the last segment).
+    // Every lane then stores its 16 FIFO bytes with one instruction; the
+    // flag word gets a placeholder 0 that never matches a flag, and the
+    // real flag follows after the drain below.
+    constexpr bool kNu = RAR_NT_USER != 0;
+    uint8_t* stage = cx.stage + (int64_t)wave * U * 1024;
+    const int64_t ub = 16 * (int64_t)lid;  // this lane's 16 bytes of a group, user layout
+    const bool ulane = lid < 60;
+    const v4u zero = {0, 0, 0, 0};
+    // The FIFO words (in) and user bytes (x) of U groups of 8 lines, group u
+    // starting at line g + u * stride.  whole(g): all U groups are full
+    // lines inside the step and the chunk.
+    auto whole = [&](int64_t g) {
+      const int64_t last_end = g + (int64_t)(U - 1) * stride + 8;
+      return last_end <= hi && 120 * last_end <= nbytes;
+    };
+    // this lane's 16 bytes of line j of the receive slot
+    auto fifo_load = [&](int64_t j) -> v4u {
+      return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)(128 * (j - lo) + 16 * k), 0, kCpolSc1);
+    };
+    auto load_whole = [&](int64_t g, v4u* in, v4u* x) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t j = g + (int64_t)u * stride + sub;
-          in[u] = zero;
-          if (O::kRecv) {
-            // lane 7's upper half is the line's flag word: process() drops
-            // it (a zeroing here would wait for the load)
-            in[u] = fifo_load(j);
-          }
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = g + (int64_t)u * stride + sub;
+        in[u] = zero;
+        if (O::kRecv) {
+          // lane 7's upper half is the line's flag word: process() drops
+          // it (a zeroing here would wait for the load)
+          in[u] = fifo_load(j);
         }
-        // lanes 60..63 hold no user bytes of a group: they repeat lane 0's
-        // load (in bounds) so that no load needs a branch around it
+      }
+      // lanes 60..63 hold no user bytes of a group: they repeat lane 0's
+      // load (in bounds) so that no load needs a branch around it
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        x[u] = O::kSrc ? ldv<kNu, true>(sb + 120 * (g + (int64_t)u * stride) + (ulane ? ub : 0), 0) : zero;
+    };
+    auto load_part = [&](int64_t g, v4u* in, v4u* x) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t gs = g + (int64_t)u * stride;  // first line of group u
+        const int64_t ge = gs + 8 < hi ? gs + 8 : hi;
+        const int64_t gend = 120 * ge < nbytes ? 120 * ge : nbytes;
+        const int64_t gvalid = gs < hi ? gend - 120 * gs : 0;  // payload bytes of the group
+        const int64_t j = gs + sub;
+        in[u] = zero;
+        x[u] = zero;
+        if (O::kRecv && j < hi) {
+          in[u] = fifo_load(j);
+          if (k == 7) in[u].z = in[u].w = 0;
+        }
+        if (O::kSrc && ulane) {
+          if (ub + 16 <= gvalid) x[u] = ldv<kNu, true>(sb + 120 * gs + ub, 0);
+          else if (ub < gvalid) x[u] = load_bytes16<S>(sb + 120 * gs + ub, gvalid - ub, 16);
+        }
+      }
+    };
+    // Reduce and store the U groups at g whose loads are in `in` and `x`;
+    // kWhole: every group is whole (known at compile time: no bounds
+    // checks around the stores).
+    auto process = [&](auto kWhole, int64_t g, const v4u* in, const v4u* x) {
+      v4u own[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) own[u] = zero;
+      if (O::kSrc) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          x[u] = O::kSrc ? ldv<kNu, true>(sb + 120 * (g + (int64_t)u * stride) + (ulane ? ub : 0), 0) : zero;
-      };
-      auto load_part = [&](int64_t g, v4u* in, v4u* x) {
+          if (ulane) *reinterpret_cast<v4u*>(stage + u * 1024 + ub) = x[u];
+        wave_sync();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t gs = g + (int64_t)u * stride;  // first line of group u
+          const uint8_t* q = stage + u * 1024 + 120 * sub + 16 * k;
+          const uint64_t w0 = *reinterpret_cast<const uint64_t*>(q);
+          const uint64_t w1 = k < 7 ? *reinterpret_cast<const uint64_t*>(q + 8) : 0;
+          own[u].x = (uint32_t)w0;
+          own[u].y = (uint32_t)(w0 >> 32);
+          own[u].z = (uint32_t)w1;
+          own[u].w = (uint32_t)(w1 >> 32);
+          if constexpr (Ty::kPre) own[u] = pre16<Ty>(own[u], cx.s_own);
+        }
+        wave_sync();  // the tile is read before it is written again
+      }
+      v4u v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        v[u] = (O::kRecv && O::kSrc) ? red16<Ty>(in[u], own[u]) : (O::kRecv ? in[u] : own[u]);
+        if constexpr (OP == kOpRecvReduceCopySend && Ty::kPost) v[u] = post16<Ty>(v[u], cx.nranks);
+        if (k == 7) v[u].z = v[u].w = 0;  // flag placeholder
+        const int64_t j = g + (int64_t)u * stride + sub;
+        if (O::kSend && (kWhole || j < hi)) *G(reinterpret_cast<v4u*>(sl + 16 * j + 2 * k)) = v[u];
+      }
+      if (O::kDst) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          uint8_t* q = stage + u * 1024 + 120 * sub + 16 * k;
+          *reinterpret_cast<uint64_t*>(q) = (uint64_t)v[u].x | ((uint64_t)v[u].y << 32);
+          if (k < 7) *reinterpret_cast<uint64_t*>(q + 8) = (uint64_t)v[u].z | ((uint64_t)v[u].w << 32);
+        }
+        wave_sync();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (!ulane) continue;
+          const int64_t gs = g + (int64_t)u * stride;
+          const v4u y = *reinterpret_cast<const v4u*>(stage + u * 1024 + ub);
+          if (kWhole) {
+            stv<kNu, true>(db + 120 * gs + ub, 0, y);
+            continue;
+          }
           const int64_t ge = gs + 8 < hi ? gs + 8 : hi;
           const int64_t gend = 120 * ge < nbytes ? 120 * ge : nbytes;
-          const int64_t gvalid = gs < hi ? gend - 120 * gs : 0;  // payload bytes of the group
-          const int64_t j = gs + sub;
-          in[u] = zero;
-          x[u] = zero;
-          if (O::kRecv && j < hi) {
-            in[u] = fifo_load(j);
-            if (k == 7) in[u].z = in[u].w = 0;
-          }
-          if (O::kSrc && ulane) {
-            if (ub + 16 <= gvalid) x[u] = ldv<kNu, true>(sb + 120 * gs + ub, 0);
-            else if (ub < gvalid) x[u] = load_bytes16<S>(sb + 120 * gs + ub, gvalid - ub, 16);
-          }
+          const int64_t gvalid = gs < hi ? gend - 120 * gs : 0;
+          if (ub + 16 <= gvalid) stv<kNu, true>(db + 120 * gs + ub, 0, y);
+          else if (ub < gvalid) store_bytes16<S>(db + 120 * gs + ub, y, gvalid - ub, 16);
         }
-      };
-      // Reduce and store the U groups at g whose loads are in `in` and `x`;
-      // kWhole: every group is whole (known at compile time: no bounds
-      // checks around the stores).
-      auto process = [&](auto kWhole, int64_t g, const v4u* in, const v4u* x) {
-        v4u own[U];
+        wave_sync();
+      }
+    };
+    // Whole groups run software-pipelined: the next iteration's loads are
+    // issued before this iteration's stores, so they are in flight while
+    // this iteration computes and stores.  Two register sets take turns
+    // (no copies between them, which would wait for the loads); the last
+    // whole iteration is peeled (nothing to prefetch).  The partial groups
+    // at the end of a share follow unpipelined.
+    const std::integral_constant<bool, true> kW{};
+    const std::integral_constant<bool, false> kP{};
+    const int64_t gstep = (int64_t)U * stride;
+    // Flags to a receiver on this XCD go out while the step is still
+    // being written: after an iteration's data stores, the wave waits for
+    // every vector memory operation it has outstanding (those stores and
+    // the next iteration's loads) and then stores that iteration's flags.
+    // A flag thus lands in L2 after its line's data, and soon enough to
+    // merge with the line while it is still there (a flag stored after
+    // the whole step found most half-lines written back already, and they
+    // went to memory twice).  Other flags, and every flag to a receiver on
+    // another XCD, follow the drain at the end of the step.
+    const bool early = O::kSend && __builtin_amdgcn_readfirstlane(cx.local_send ? 1 : 0) != 0;
+    // pub and g0 pass through readfirstlane when they advance: they are
+    // the same on every lane, but they merge right after the per-lane
+    // flag stores, and without it the compiler keeps them per lane and
+    // runs the loop on lane masks (measured: 3 % slower at 64 MiB)
+    int64_t pub = first;  // first group whose flags are not out
+    // flags of the iteration at g, once its data stores have retired
+    auto publish = [&](int64_t g) {
+      if (!early) return;
+      wait_vmem();
 #pragma unroll
-        for (int u = 0; u < U; ++u) own[u] = zero;
-        if (O::kSrc) {
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-            if (ulane) *reinterpret_cast<v4u*>(stage + u * 1024 + ub) = x[u];
-          wave_sync();
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const uint8_t* q = stage + u * 1024 + 120 * sub + 16 * k;
-            const uint64_t w0 = *reinterpret_cast<const uint64_t*>(q);
-            const uint64_t w1 = k < 7 ? *reinterpret_cast<const uint64_t*>(q + 8) : 0;
-            own[u].x = (uint32_t)w0;
-            own[u].y = (uint32_t)(w0 >> 32);
-            own[u].z = (uint32_t)w1;
-            own[u].w = (uint32_t)(w1 >> 32);
-            if constexpr (Ty::kPre) own[u] = pre16<Ty>(own[u], cx.s_own);
-          }
-          wave_sync();  // the tile is read before it is written again
-        }
-        v4u v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          v[u] = (O::kRecv && O::kSrc) ? red16<Ty>(in[u], own[u]) : (O::kRecv ? in[u] : own[u]);
-          if constexpr (OP == kOpRecvReduceCopySend && Ty::kPost) v[u] = post16<Ty>(v[u], cx.nranks);
-          if (k == 7) v[u].z = v[u].w = 0;  // flag placeholder
-          const int64_t j = g + (int64_t)u * stride + sub;
-          if (O::kSend && (kWhole || j < hi)) *G(reinterpret_cast<v4u*>(sl + 16 * j + 2 * k)) = v[u];
-        }
-        if (O::kDst) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            uint8_t* q = stage + u * 1024 + 120 * sub + 16 * k;
-            *reinterpret_cast<uint64_t*>(q) = (uint64_t)v[u].x | ((uint64_t)v[u].y << 32);
-            if (k < 7) *reinterpret_cast<uint64_t*>(q + 8) = (uint64_t)v[u].z | ((uint64_t)v[u].w << 32);
-          }
-          wave_sync();
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            if (!ulane) continue;
-            const int64_t gs = g + (int64_t)u * stride;
-            const v4u y = *reinterpret_cast<const v4u*>(stage + u * 1024 + ub);
-            if (kWhole) {
-              stv<kNu, true>(db + 120 * gs + ub, 0, y);
-              continue;
-            }
-            const int64_t ge = gs + 8 < hi ? gs + 8 : hi;
-            const int64_t gend = 120 * ge < nbytes ? 120 * ge : nbytes;
-            const int64_t gvalid = gs < hi ? gend - 120 * gs : 0;
-            if (ub + 16 <= gvalid) stv<kNu, true>(db + 120 * gs + ub, 0, y);
-            else if (ub < gvalid) store_bytes16<S>(db + 120 * gs + ub, y, gvalid - ub, 16);
-          }
-          wave_sync();
-        }
-      };
-      // Whole groups run software-pipelined: the next iteration's loads are
-      // issued before this iteration's stores, so they are in flight while
-      // this iteration computes and stores.  Two register sets take turns
-      // (no copies between them, which would wait for the loads); the last
-      // whole iteration is peeled (nothing to prefetch).  The partial groups
-      // at the end of a share follow unpipelined.
-      const std::integral_constant<bool, true> kW{};
-      const std::integral_constant<bool, false> kP{};
-      const int64_t gstep = (int64_t)U * stride;
-      // Flags to a receiver on this XCD go out while the step is still
-      // being written: after an iteration's data stores, the wave waits for
-      // every vector memory operation it has outstanding (those stores and
-      // the next iteration's loads) and then stores that iteration's flags.
-      // A flag thus lands in L2 after its line's data, and soon enough to
-      // merge with the line while it is still there (a flag stored after
-      // the whole step found most half-lines written back already, and they
-      // went to memory twice).  Other flags, and every flag to a receiver on
-      // another XCD, follow the drain at the end of the step.
-      const bool early = O::kSend && __builtin_amdgcn_readfirstlane(cx.local_send ? 1 : 0) != 0;
-      // pub and g0 pass through readfirstlane when they advance: they are
-      // the same on every lane, but they merge right after the per-lane
-      // flag stores, and without it the compiler keeps them per lane and
-      // runs the loop on lane masks (measured: 3 % slower at 64 MiB)
-      int64_t pub = first;  // first group whose flags are not out
-      // flags of the iteration at g, once its data stores have retired
-      auto publish = [&](int64_t g) {
-        if (!early) return;
-        wait_vmem();
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t j = g + (int64_t)u * stride + sub;
-          if (k == 7) store_relaxed_xcd(sl + 16 * j + 15, sflag);
-        }
-        pub = uni64(g + gstep);
-      };
-      // Receive group by group: before a wave loads the lines of an
-      // iteration it waits for the flag of the iteration's first line.  The
-      // sender stores an iteration's flags only after all of that
-      // iteration's data stores have completed (the rest of the step's
-      // flags after the step's drain), so one flag stands for every line of
-      // the iteration.  The next iteration's flag is loaded one iteration
-      // ahead: a sender that is ahead costs no extra round trip.  Measured
-      // against wave 0 polling every flag of the step before any wave reads
-      // (then one acquire and a barrier): 276 -> 245 us at 64 MiB, the
-      // receivers no longer wait for whole steps of their senders.
-      constexpr bool kGroupRecv = O::kRecv;
-      auto wait_line = [&](int64_t j) -> bool {
-        if constexpr (!kGroupRecv) return true;
-        const uint64_t tp = __builtin_amdgcn_s_memrealtime();
-        for (uint32_t it = 1;; ++it) {
-          if (uni64(load_relaxed(rl + 16 * j + 15)) == rflag) break;
-          __builtin_amdgcn_s_sleep(1);
-          if ((it & 15u) == 0 && __builtin_amdgcn_readfirstlane(should_stop(cx, tp) ? 1 : 0) != 0)
-            return false;
-        }
-        asm volatile("" ::: "memory");  // the lines' loads stay after the flag
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = g + (int64_t)u * stride + sub;
+        if (k == 7) store_relaxed_xcd(sl + 16 * j + 15, sflag);
+      }
+      pub = uni64(g + gstep);
+    };
+    // Receive group by group: before a wave loads the lines of an
+    // iteration it waits for the flag of the iteration's first line.  The
+    // sender stores an iteration's flags only after all of that
+    // iteration's data stores have completed (the rest of the step's
+    // flags after the step's drain), so one flag stands for every line of
+    // the iteration.  The next iteration's flag is loaded one iteration
+    // ahead: a sender that is ahead costs no extra round trip.  Measured
+    // against wave 0 polling every flag of the step before any wave reads
+    // (then one acquire and a barrier): 276 -> 245 us at 64 MiB, the
+    // receivers no longer wait for whole steps of their senders.
+    constexpr bool kGroupRecv = O::kRecv;
+    auto wait_line = [&](int64_t j) -> bool {
+      if constexpr (!kGroupRecv) return true;
+      const uint64_t tp = __builtin_amdgcn_s_memrealtime();
+      for (uint32_t it = 1;; ++it) {
+        if (uni64(load_relaxed(rl + 16 * j + 15)) == rflag) break;
+        __builtin_amdgcn_s_sleep(1);
+        if ((it & 15u) == 0 && __builtin_amdgcn_readfirstlane(should_stop(cx, tp) ? 1 : 0) != 0)
+          return false;
+      }
+      asm volatile("" ::: "memory");  // the lines' loads stay after the flag
+      return true;
+    };
+    auto ready = [&](int64_t j, uint64_t seen) -> bool {
+      if constexpr (!kGroupRecv) return true;
+      if (uni64(seen) == rflag) {
+        asm volatile("" ::: "memory");
         return true;
-      };
-      auto ready = [&](int64_t j, uint64_t seen) -> bool {
-        if constexpr (!kGroupRecv) return true;
-        if (uni64(seen) == rflag) {
-          asm volatile("" ::: "memory");
-          return true;
-        }
-        return wait_line(j);
-      };
-      auto peek = [&](int64_t j) -> uint64_t {
-        if constexpr (!kGroupRecv) return 0;
-        return j < hi ? load_relaxed(rl + 16 * j + 15) : 0;
-      };
-      int64_t g0 = first;
-      if (g0 < hi && whole(g0) && (ok = wait_line(g0))) {
-        v4u inA[U], xA[U], inB[U], xB[U];
-        load_whole(g0, inA, xA);
-        uint64_t seen = peek(g0 + gstep);
-        for (;;) {
-          if (!(g0 + gstep < hi && whole(g0 + gstep))) {
-            process(kW, g0, inA, xA);
-            publish(g0);
-            g0 = uni64(g0 + gstep);
-            break;
-          }
-          if (!(ok = ready(g0 + gstep, seen))) break;
-          load_whole(g0 + gstep, inB, xB);
-          seen = peek(g0 + 2 * gstep);
+      }
+      return wait_line(j);
+    };
+    auto peek = [&](int64_t j) -> uint64_t {
+      if constexpr (!kGroupRecv) return 0;
+      return j < hi ? load_relaxed(rl + 16 * j + 15) : 0;
+    };
+    int64_t g0 = first;
+    if (g0 < hi && whole(g0) && (ok = wait_line(g0))) {
+      v4u inA[U], xA[U], inB[U], xB[U];
+      load_whole(g0, inA, xA);
+      uint64_t seen = peek(g0 + gstep);
+      for (;;) {
+        if (!(g0 + gstep < hi && whole(g0 + gstep))) {
           process(kW, g0, inA, xA);
           publish(g0);
           g0 = uni64(g0 + gstep);
-          if (!(g0 + gstep < hi && whole(g0 + gstep))) {
-            process(kW, g0, inB, xB);
-            publish(g0);
-            g0 = uni64(g0 + gstep);
-            break;
-          }
-          if (!(ok = ready(g0 + gstep, seen))) break;
-          load_whole(g0 + gstep, inA, xA);
-          seen = peek(g0 + 2 * gstep);
+          break;
+        }
+        if (!(ok = ready(g0 + gstep, seen))) break;
+        load_whole(g0 + gstep, inB, xB);
+        seen = peek(g0 + 2 * gstep);
+        process(kW, g0, inA, xA);
+        publish(g0);
+        g0 = uni64(g0 + gstep);
+        if (!(g0 + gstep < hi && whole(g0 + gstep))) {
           process(kW, g0, inB, xB);
           publish(g0);
           g0 = uni64(g0 + gstep);
+          break;
         }
+        if (!(ok = ready(g0 + gstep, seen))) break;
+        load_whole(g0 + gstep, inA, xA);
+        seen = peek(g0 + 2 * gstep);
+        process(kW, g0, inB, xB);
+        publish(g0);
+        g0 = uni64(g0 + gstep);
       }
-      for (; ok && g0 < hi; g0 = uni64(g0 + gstep)) {
-        if (!(ok = wait_line(g0))) break;
-        v4u in[U], x[U];
-        load_part(g0, in, x);
-        process(kP, g0, in, x);
-      }
-      if (O::kSend && ok) {
-        // data words before flag words: drained into this L2, and written
-        // back when the receiver runs on another XCD
-        drain_vmem();
-        if (!cx.local_send) release_fence();
-        for (int64_t g = pub; g < hi; g += stride) {
-          const int64_t j = g + sub;
-          // to a receiver on this XCD the flag goes out at workgroup scope: it
-          // merges into the line in L2 instead of being written through as
-          // a partial line (measured: 472 -> 332 us at 64 MiB, partial
-          // memory-side writes from 24 % to 6 %)
-          if (j < hi && k == 7) {
-            if (cx.local_send) store_relaxed_xcd(sl + 16 * j + 15, sflag);
-            else store_relaxed(sl + 16 * j + 15, sflag);
-          }
+    }
+    for (; ok && g0 < hi; g0 = uni64(g0 + gstep)) {
+      if (!(ok = wait_line(g0))) break;
+      v4u in[U], x[U];
+      load_part(g0, in, x);
+      process(kP, g0, in, x);
+    }
+    if (O::kSend && ok) {
+      // data words before flag words: drained into this L2, and written
+      // back when the receiver runs on another XCD
+      drain_vmem();
+      if (!cx.local_send) release_fence();
+      for (int64_t g = pub; g < hi; g += stride) {
+        const int64_t j = g + sub;
+        // to a receiver on this XCD the flag goes out at workgroup scope: it
+        // merges into the line in L2 instead of being written through as
+        // a partial line (measured: 472 -> 332 us at 64 MiB, partial
+        // memory-side writes from 24 % to 6 %)
+        if (j < hi && k == 7) {
+          if (cx.local_send) store_relaxed_xcd(sl + 16 * j + 15, sflag);
+          else store_relaxed(sl + 16 * j + 15, sflag);
         }
       }
     }
@@ -1229,7 +1227,10 @@ __device__ void load_batch(Shmem& sh, const Plan& a, uint32_t b, int lid) {
 // LL128 workgroups are small (4 waves in the measured shape) and the protocol
 // wants many of them: capping its registers at three waves per SIMD lets three
 // such workgroups share a CU (fp32 and int32, with 4 groups of lines in flight,
-// then spill 17 registers per lane; still faster than 2 groups unspilled).
+// then spill 4 registers per lane, 12 for avg and PreMulSum; bf16 with 3
+// groups spills none).  Measured at 64 MiB: this beats a two-waves-per-SIMD
+// cap with 6 or 8 groups in flight and fewer workgroups (254-288 us against
+// 246 us).
 template <class Ty, int PROTO>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PROTO == kLL128 ? 3 : 1)))
 ring_allreduce_kernel(KernelArgs args) {
