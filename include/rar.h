@@ -303,6 +303,23 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
                             const int* ring_order, rar_proto_t proto, int nchannels,
                             size_t buff_size, int chunk_steps, void* stream);
 
+/* Destroy every communicator that ring_allreduce has cached, on every
+ * device: the clean-up step that ends the pages' communicator life cycle,
+ * after the collectives that used it are done [C2 "4 User Buffer
+ * Registration", the ncclCommDestroy step].  Each one's last launch is waited
+ * for (hipEventSynchronize on the event ring_allreduce records after it)
+ * before its FIFOs, counters and plan memory are freed; the next
+ * ring_allreduce of that shape builds a fresh communicator.  Use it to give
+ * the device memory back (a 64 MiB Simple shape at 12 channels holds 192 MiB
+ * of FIFOs), or after ring_allreduce returned RAR_ABORTED: a communicator
+ * whose launch hit the wait watchdog refuses every later call until it is
+ * destroyed.  Must not run while another thread is inside ring_allreduce,
+ * nor while a HIP graph that captured a ring_allreduce launch may still be
+ * replayed (the replay would use freed memory).  With nothing cached it
+ * touches no device.  RAR_HIP_ERROR if a wait or a free fails (the
+ * communicators not yet freed stay cached). */
+rar_result_t ring_allreduce_cache_release(void);
+
 /* For callers that cannot allocate device memory (code that runs under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * ring_allreduce with the same arguments and the same results, bit for bit,

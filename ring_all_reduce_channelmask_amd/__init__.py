@@ -189,6 +189,13 @@ def ring_allreduce(sends, recvs, ring_order, proto="SIMPLE", nchannels=1, buff_s
                                   buff_size, chunk_steps, _stream_handle(stream)))
 
 
+def ring_allreduce_cache_release():
+    """Destroy the communicators ring_allreduce has cached (after their last
+    launches): frees their device memory, and clears one that a watchdog
+    abort left refusing calls."""
+    _lib.check(_lib.load().ring_allreduce_cache_release())
+
+
 def ring_allreduce_noalloc(sends, recvs, ring_order, proto="SIMPLE", nchannels=1, buff_size=0,
                            chunk_steps=0, stream=None, op="sum"):
     """ring_allreduce with its device state in the library's static array:

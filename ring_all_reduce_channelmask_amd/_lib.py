@@ -74,6 +74,7 @@ SIGNATURES = [
     ("rar_comm_destroy", _c.c_int, [_c.c_void_p]),
     ("ring_allreduce", _c.c_int, [_vpp, _vpp, _c.c_int, _c.c_size_t, _c.c_int, _c.c_int, _ip,
                                   _c.c_int, _c.c_int, _c.c_size_t, _c.c_int, _c.c_void_p]),
+    ("ring_allreduce_cache_release", _c.c_int, []),
     ("ring_allreduce_noalloc", _c.c_int, [_vpp, _vpp, _c.c_int, _c.c_size_t, _c.c_int, _c.c_int,
                                           _ip, _c.c_int, _c.c_int, _c.c_size_t, _c.c_int,
                                           _c.c_void_p]),

@@ -785,6 +785,34 @@ rar_result_t ring_allreduce(const void* const* sendbufs, void* const* recvbufs, 
   return RAR_SUCCESS;
 }
 
+rar_result_t ring_allreduce_cache_release(void) {
+  g_last_error.clear();
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  if (g_cache.empty()) return RAR_SUCCESS;  // nothing cached: no device call
+  int cur = 0;
+  RAR_HIP(hipGetDevice(&cur));
+  rar_result_t res = RAR_SUCCESS;
+  while (!g_cache.empty()) {
+    auto it = g_cache.begin();
+    rar_comm* c = it->second;
+    // wait for its last launch and free it with its own device current
+    hipError_t e = hipSetDevice(c->device);
+    if (e == hipSuccess && c->has_last) {
+      std::lock_guard<std::mutex> call_lk(c->call_mu);
+      e = hipEventSynchronize(c->last_done);
+    }
+    if (e != hipSuccess) {
+      res = fail(RAR_HIP_ERROR, std::string("waiting for a cached communicator's last launch failed: ") +
+                                    hipGetErrorString(e));
+      break;
+    }
+    g_cache.erase(it);
+    release(c);
+  }
+  (void)hipSetDevice(cur);
+  return res;
+}
+
 static rar_result_t oneshot_impl(const void* const* sendbufs, void* const* recvbufs, int nranks,
                                  size_t count, rar_dtype_t dtype, int op, const void* scalars,
                                  const rar_oneshot_tuning_t* tuning, void* stream) {

@@ -38,6 +38,13 @@ def test_error_strings():
         assert lib.rar_get_error_string(code)
 
 
+def test_cache_release_with_nothing_cached_touches_no_device():
+    # no communicator is cached in this process: the call returns at once,
+    # making no HIP call (on a host without a GPU any HIP call would fail)
+    assert _lib.load().ring_allreduce_cache_release() == _lib.SUCCESS
+    rar.ring_allreduce_cache_release()
+
+
 def test_ring_info_matches_pages_and_oracle():
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "ring_tables.json")))
     for key in ("0-1-2-3", "0-2-3-1"):

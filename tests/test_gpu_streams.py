@@ -77,3 +77,28 @@ def test_same_shape_from_two_threads():
         for i in range(reps):
             for r in range(4):
                 assert_bits_equal(to_host(outs[k][i][r], "float32"), want, f"thread {k} call {i} rank {r}")
+
+
+def test_cache_release_waits_for_the_launch_and_next_call_rebuilds():
+    """ring_allreduce_cache_release right after a launch, with no
+    synchronize in between: it waits for that launch before freeing the
+    communicator, and the next call of the shape builds a fresh one whose
+    output has the same bits."""
+    import torch
+    import ring_all_reduce_channelmask_amd as rar
+    order, C, n = [0, 2, 3, 1], 4, 300007
+    for proto in ("SIMPLE", "LL128"):
+        x = _rand((4, n), 90)
+        sends = [to_device(r, "float32") for r in x]
+        outs = [[torch.empty_like(t) for t in sends] for _ in range(3)]
+        torch.cuda.synchronize()
+        rar.ring_allreduce_cache_release()  # whatever earlier tests cached
+        for i in range(3):
+            rar.ring_allreduce(sends, outs[i], order, proto=proto, nchannels=C)
+            rar.ring_allreduce_cache_release()
+        rar.ring_allreduce_cache_release()  # nothing left: a no-op
+        torch.cuda.synchronize()
+        want = cf.allreduce([x], order, (1 << C) - 1, proto, BUFF[proto], 4, "float32")[0]
+        for i in range(3):
+            for r in range(4):
+                assert_bits_equal(to_host(outs[i][r], "float32"), want, f"{proto} call {i} rank {r}")
