@@ -324,14 +324,22 @@ __device__ __forceinline__ bool wait_credit(Ctx& cx, uint64_t n) {
 }
 
 // ---------------------------------------------------------------- Simple
-// Loads in flight per thread and per source in reduceCopy, and whether the
-// user buffers (each read once, written once) and the FIFO slots are accessed
-// with the non-temporal hint, so that streaming user data does not push the
-// FIFO slots (re-read moments later on the same XCD) out of L2.  Measured on
-// MI355X at 64 MiB x 4 ranks: user-buffer hint on, FIFO hint off, 4 vectors in
-// flight is the fastest of the combinations tried.  Performance only.
+// Loads in flight per thread and per source in reduceCopy (16-byte vectors;
+// bf16, whose per-element widening needs more registers, keeps fewer), and
+// whether the user buffers (each read once, written once) and the FIFO slots
+// are accessed with the non-temporal hint, so that streaming user data does
+// not push the FIFO slots (re-read moments later on the same XCD) out of L2.
+// Measured on MI355X at 64 MiB x 4 ranks: user-buffer hint on, FIFO hint off.
+// Vectors in flight, fp32 64 MiB x 4 ranks: 4 -> 212.0 us, 8 -> 207.5, 12 ->
+// 213.0 (a larger remainder after the last whole block), 16 -> 205.0; int32
+// 128 MiB x 8 ranks: 835.5 / 833.3 / 839.5 / 831.7 us; bf16 64 MiB x 8 ranks:
+// 8 is 1 % and 6 is 9 % slower than 4.  16 keeps 2 waves per SIMD, as 4 did
+// (218-222 registers).  Performance only.
 #ifndef RAR_UNROLL
-#define RAR_UNROLL 4
+#define RAR_UNROLL 16
+#endif
+#ifndef RAR_UNROLL_BF16
+#define RAR_UNROLL_BF16 4
 #endif
 #ifndef RAR_NT_USER
 #define RAR_NT_USER 1
@@ -416,7 +424,7 @@ __device__ __forceinline__ void stv(void* base, int64_t i, v4u v) {
   }
 }
 
-// reduceCopy over n elements with 16-byte vectors, RAR_UNROLL in flight per
+// reduceCopy over n elements with 16-byte vectors, kUnroll in flight per
 // thread and source; consecutive threads touch consecutive 16-byte vectors.
 // The call that combines a partial with the own input and writes the output
 // is the owner's final step, which also applies the post-op (divisor n_post).
@@ -435,7 +443,7 @@ __device__ __forceinline__ void reduce_copy(const typename Ty::S* fin, const typ
   constexpr bool kPreOwn = kSrc && Ty::kPre;
   constexpr bool kPreIn = kRecv && kRawIn && Ty::kPre;
   constexpr int kVec = 16 / sizeof(S);
-  constexpr int kUnroll = RAR_UNROLL;
+  constexpr int kUnroll = sizeof(S) == 2 ? RAR_UNROLL_BF16 : RAR_UNROLL;
   constexpr bool kNu = RAR_NT_USER != 0;
   constexpr bool kNi = kUserIn ? RAR_NT_DIRECT != 0 : RAR_NT_FIFO != 0;
   constexpr bool kNo = kUserOut ? RAR_NT_DIRECT != 0 : RAR_NT_FIFO != 0;
