@@ -155,7 +155,13 @@ int work_waves(const Piece& p, int n_waves, const WaveSizing& sz) {
   const int64_t loop = (int64_t)sz.nranks * p.chunk_count;
   const int64_t cc = p.channel_count < loop ? align_up(div_up(p.channel_count, sz.nranks), vec) : p.chunk_count;
   const int64_t bytes = div_up(cc * sz.es, sz.split_lanes);
-  const int64_t pass = sz.proto == kSimple ? 4096 : sz.proto == kLL ? 2048 : 1920;
+  // bytes one wave moves per pass: Simple 64 lanes x 16 bytes x the vectors
+  // reduceCopy keeps in flight (16 for 4-byte payloads, 4 for bf16); LL 64
+  // lanes x 4 lines x 8 payload bytes; LL128 groups of 8 lines x 120 bytes,
+  // 4 groups per pass for 4-byte payloads and 3 for bf16
+  const int64_t simple_pass = sz.es == 2 ? 4096 : 16384;
+  const int64_t ll128_pass = 960 * (sz.es == 2 ? 3 : 4);
+  const int64_t pass = sz.proto == kSimple ? simple_pass : sz.proto == kLL ? 2048 : ll128_pass;
   return (int)std::max<int64_t>(1, std::min<int64_t>(n_waves, div_up(bytes, pass)));
 }
 

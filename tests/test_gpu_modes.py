@@ -81,7 +81,7 @@ def test_mixed_wave_counts_in_one_batch(proto, deal):
     import ring_all_reduce_channelmask_amd as rar
     from ring_all_reduce_channelmask_amd import _lib
     # buffers whose chunks fill all 8 waves for the large works
-    buff = {"SIMPLE": 64 << 10, "LL": 256 << 10, "LL128": 8 * 2048 * 8}[proto]
+    buff = {"SIMPLE": 256 << 10, "LL": 256 << 10, "LL128": 8 * 2048 * 8}[proto]
     mask, order, dtype = 0b1011, [0, 2, 3, 1], "float32"
     comm = rar.Comm(4, order, mask, proto=proto, buff_size=buff, lanes=2, waves=8,
                     waves_by_size=1, deal_works=deal, debug_flags=_lib.DEBUG_TRACE)
